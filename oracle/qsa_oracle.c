@@ -1,0 +1,351 @@
+/*
+ * qsa_oracle.c -- plain, slow, single-threaded CPU oracle for the QSA
+ * sparse-attention decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * bench's CPU-baseline leg may load this library.  It shares no code,
+ * header, table or helper with the HIP path and never calls into it.
+ *
+ * What it computes (intel/llm-scaler PR #651, "vLLM: integrate FP16 packed
+ * QSA extension", sections "Summary" and "Exact contracts"):
+ *
+ *   selection, per query row r
+ *     req  = token_to_req[r], L = seq_lens[req], qp = query_pos[r]
+ *     V    = max(0, min(floor((qp+1)/4), floor(L/4)))       visible blocks
+ *            (vllm qsa_cache.py page, _build_qsa_metadata_kernel and its
+ *             torch fallback: the visible-block rule)
+ *     T    = max(0, min(qp+1, L) - 4V)                       tail tokens
+ *     key of block b = kcache[bt[req][b / 128]][b % 128][0][:]
+ *            (qsa_cache.py page, compressed_qsa_slot_mapping: the
+ *             compressed position b lives in logical page b / 128 at slot
+ *             b % 128)
+ *     score s_b = sum over the 4 indexer heads h of ReLU(q[r][h] . key_b)
+ *     order all V blocks by score descending, ties by ascending block
+ *     index; keep the first n = min(512, V)
+ *     out[r][4i+j] = 4*b_i + j (i < n, j < 4), then the tail tokens
+ *     4V .. 4V+T-1, then -1 up to width 2051.
+ *
+ *   attention, per row r and query head h in {0,1,2}
+ *     J = positions j of indices[r] with indices[r][j] >= 0 (a multiset:
+ *         a repeated index is a separate member)
+ *     l_j = scale * sum_d q[r][h][d] * K[idx_j][d]      (K = kv[t][0:256])
+ *     o[r][h][:] = sum_j softmax(l)_j * V[idx_j][:]      (V = kv[t][256:512])
+ *     an empty J gives o = 0.
+ *
+ * Precision: fp16 inputs are widened to double with a conversion written
+ * from the IEEE 754 binary16 definition; every dot product and softmax is
+ * evaluated in double.  A selection score is rounded once to binary32 at
+ * the end, so that both sides of a comparison decide ties in binary32.
+ *
+ * Sorting uses the C library's qsort as the one library primitive.
+ *
+ * Compile-time switch QSA_ORACLE_MUTANT (default 0) plants a single known
+ * mistake; it exists only so that the pin tests can show they would catch
+ * that mistake.  The oracle the tests trust is built without it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef QSA_ORACLE_MUTANT
+#define QSA_ORACLE_MUTANT 0
+#endif
+
+/* Fixed contract of the pages ("Exact contracts", selection): 2048 tokens
+ * from 512 blocks of 4, plus up to three tail tokens. */
+#define OR_TOKEN_TOPK 2048
+#define OR_RATIO 4
+#define OR_TOPK_BLOCKS (OR_TOKEN_TOPK / OR_RATIO)
+#define OR_WIDTH 2051
+#define OR_PAGE_SLOTS 128
+#define OR_SEL_HEADS 4
+#define OR_SEL_DIM 128
+#define OR_ATT_HEADS 3
+#define OR_ATT_DIM 256
+#define OR_KV_ROW 512
+
+enum {
+  OR_OK = 0,
+  OR_ERR_REQ = -1,      /* token_to_req outside [0, N) */
+  OR_ERR_TABLE = -2,    /* a visible block lies beyond the block table */
+  OR_ERR_PAGE = -3,     /* a needed page id outside [0, P) */
+  OR_ERR_INDEX = -4,    /* an attention index outside [-1, NT) */
+  OR_ERR_NOMEM = -5,
+  OR_ERR_ARG = -6
+};
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent 0 encodes subnormals (fraction * 2^-24); exponent 31
+ * encodes infinities and NaNs. */
+double qsa_oracle_half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 31;
+  int frac = h & 1023;
+  double v;
+  if (expo == 0) {
+    v = ldexp((double)frac, -24);
+  } else if (expo == 31) {
+    v = frac ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + frac), expo - 25);
+  }
+  return sign ? -v : v;
+}
+
+/* Visible blocks and tail length of one query row. */
+void qsa_oracle_row_extent(int64_t seq_len, int64_t query_pos, int64_t* visible,
+                           int64_t* tail) {
+  int64_t upto = query_pos + 1; /* tokens up to and including the query */
+#if QSA_ORACLE_MUTANT == 8
+  upto = query_pos; /* planted: off by one in the visible-block rule */
+#endif
+  int64_t a = upto >= 0 ? upto / OR_RATIO : -1;
+  int64_t b = seq_len >= 0 ? seq_len / OR_RATIO : -1;
+  int64_t v = a < b ? a : b;
+  if (v < 0) v = 0;
+  int64_t end = upto < seq_len ? upto : seq_len;
+  int64_t t = end - OR_RATIO * v;
+  if (t < 0) t = 0;
+#if QSA_ORACLE_MUTANT == 4
+  t = 0; /* planted: tail omitted */
+#endif
+  *visible = v;
+  *tail = t;
+}
+
+typedef struct {
+  float score;
+  int64_t block;
+} scored_block;
+
+/* Score descending; equal scores by ascending block index. */
+static int by_score_then_index(const void* pa, const void* pb) {
+  const scored_block* a = (const scored_block*)pa;
+  const scored_block* b = (const scored_block*)pb;
+#if QSA_ORACLE_MUTANT == 10
+  if (a->score < b->score) return -1; /* planted: ascending score */
+  if (a->score > b->score) return 1;
+#else
+  if (a->score > b->score) return -1;
+  if (a->score < b->score) return 1;
+#endif
+#if QSA_ORACLE_MUTANT == 1
+  if (a->block > b->block) return -1; /* planted: ties by descending index */
+  if (a->block < b->block) return 1;
+#else
+  if (a->block < b->block) return -1;
+  if (a->block > b->block) return 1;
+#endif
+  return 0;
+}
+
+/* Score of one compressed key against the row's four indexer heads. */
+static float block_score(const uint16_t* q_row, const uint16_t* key) {
+  double total = 0.0;
+  int heads = OR_SEL_HEADS;
+#if QSA_ORACLE_MUTANT == 5
+  heads = 3; /* planted: one head dropped */
+#endif
+  for (int h = 0; h < heads; ++h) {
+    double dot = 0.0;
+    for (int d = 0; d < OR_SEL_DIM; ++d) {
+      dot += qsa_oracle_half_to_double(q_row[h * OR_SEL_DIM + d]) *
+             qsa_oracle_half_to_double(key[d]);
+    }
+#if QSA_ORACLE_MUTANT == 2
+    total += dot; /* planted: ReLU dropped */
+#else
+    total += dot > 0.0 ? dot : 0.0;
+#endif
+  }
+  return (float)total;
+}
+
+/* Address of compressed key b of a request.  Returns NULL when the block
+ * table or the page id cannot serve it. */
+static const uint16_t* key_address(const uint16_t* kcache, int64_t num_pages,
+                                   const int32_t* table_row, int64_t table_width,
+                                   int64_t b, int* err) {
+  int64_t logical_page = b / OR_PAGE_SLOTS;
+  int64_t slot = b % OR_PAGE_SLOTS;
+#if QSA_ORACLE_MUTANT == 3
+  logical_page = b % OR_PAGE_SLOTS; /* planted: page and slot transposed */
+  slot = b / OR_PAGE_SLOTS;
+  if (logical_page >= table_width) logical_page = table_width - 1;
+#endif
+  if (logical_page >= table_width) {
+    *err = OR_ERR_TABLE;
+    return NULL;
+  }
+  int64_t page = table_row[logical_page];
+  if (page < 0 || page >= num_pages) {
+    *err = OR_ERR_PAGE;
+    return NULL;
+  }
+  return kcache + (page * OR_PAGE_SLOTS + slot) * OR_SEL_DIM;
+}
+
+/*
+ * Scores of every visible block of one row, in block order.  scores must
+ * hold max_blocks floats; *visible receives V.  Returns OR_OK or an error.
+ */
+int qsa_oracle_row_scores(int64_t r, int64_t num_pages, int64_t num_reqs,
+                          int64_t table_width, const uint16_t* q,
+                          const uint16_t* kcache, const int32_t* block_table,
+                          const int32_t* token_to_req, const int32_t* seq_lens,
+                          const int64_t* query_pos, float* scores,
+                          int64_t max_blocks, int64_t* visible) {
+  int64_t req = token_to_req[r];
+  if (req < 0 || req >= num_reqs) return OR_ERR_REQ;
+  int64_t v, t;
+  qsa_oracle_row_extent(seq_lens[req], query_pos[r], &v, &t);
+  *visible = v;
+  if (v > max_blocks) return OR_ERR_ARG;
+  const uint16_t* q_row = q + r * OR_SEL_HEADS * OR_SEL_DIM;
+  const int32_t* table_row = block_table + req * table_width;
+  for (int64_t b = 0; b < v; ++b) {
+    int err = OR_OK;
+    const uint16_t* key = key_address(kcache, num_pages, table_row, table_width, b, &err);
+    if (!key) return err;
+    scores[b] = block_score(q_row, key);
+  }
+  return OR_OK;
+}
+
+/*
+ * Selection for rows [0, R).  Shapes: q [R,4,128] fp16 bits,
+ * kcache [P,128,1,128] fp16 bits, block_table [N,W] int32,
+ * token_to_req [R] int32, seq_lens [N] int32, query_pos [R] int64,
+ * out [R,2051] int32 (written).  Returns OR_OK or the first error.
+ */
+int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
+                      int64_t table_width, const uint16_t* q, const uint16_t* kcache,
+                      const int32_t* block_table, const int32_t* token_to_req,
+                      const int32_t* seq_lens, const int64_t* query_pos,
+                      int32_t* out) {
+  for (int64_t r = 0; r < R; ++r) {
+    int32_t* out_row = out + r * OR_WIDTH;
+    for (int i = 0; i < OR_WIDTH; ++i) out_row[i] = -1;
+    int64_t req = token_to_req[r];
+    if (req < 0 || req >= num_reqs) return OR_ERR_REQ;
+    int64_t v, t;
+    qsa_oracle_row_extent(seq_lens[req], query_pos[r], &v, &t);
+    scored_block* all = NULL;
+    if (v > 0) {
+      all = (scored_block*)malloc((size_t)v * sizeof(scored_block));
+      if (!all) return OR_ERR_NOMEM;
+    }
+    const uint16_t* q_row = q + r * OR_SEL_HEADS * OR_SEL_DIM;
+    const int32_t* table_row = block_table + req * table_width;
+    for (int64_t b = 0; b < v; ++b) {
+      int err = OR_OK;
+      const uint16_t* key = key_address(kcache, num_pages, table_row, table_width, b, &err);
+      if (!key) {
+        free(all);
+        return err;
+      }
+      all[b].score = block_score(q_row, key);
+      all[b].block = b;
+    }
+    if (v > 1) qsort(all, (size_t)v, sizeof(scored_block), by_score_then_index);
+    int64_t n = v < OR_TOPK_BLOCKS ? v : OR_TOPK_BLOCKS;
+    for (int64_t i = 0; i < n; ++i) {
+      for (int j = 0; j < OR_RATIO; ++j) {
+        out_row[OR_RATIO * i + j] = (int32_t)(OR_RATIO * all[i].block + j);
+      }
+    }
+    for (int64_t k = 0; k < t; ++k) {
+      out_row[OR_RATIO * n + k] = (int32_t)(OR_RATIO * v + k);
+    }
+    free(all);
+  }
+  return OR_OK;
+}
+
+/*
+ * Sparse attention for rows [0, R).  q [R,3,256] fp16 bits, kv [NT,512]
+ * fp16 bits (token t: K = kv[t][0:256], V = kv[t][256:512]),
+ * indices [R,2051] int32, out [R,3,256] double (written).
+ */
+int qsa_oracle_sparse_attn(int64_t R, int64_t num_tokens, const uint16_t* q,
+                           const uint16_t* kv, const int32_t* indices, double scale,
+                           double* out) {
+  double* logit = (double*)malloc(OR_WIDTH * sizeof(double));
+  double* kq = (double*)malloc(OR_ATT_DIM * sizeof(double));
+  if (!logit || !kq) {
+    free(logit);
+    free(kq);
+    return OR_ERR_NOMEM;
+  }
+  int rc = OR_OK;
+  for (int64_t r = 0; r < R && rc == OR_OK; ++r) {
+    const int32_t* idx = indices + r * OR_WIDTH;
+    for (int j = 0; j < OR_WIDTH; ++j) {
+      if (idx[j] < -1 || idx[j] >= num_tokens) rc = OR_ERR_INDEX;
+    }
+    if (rc != OR_OK) break;
+    for (int h = 0; h < OR_ATT_HEADS; ++h) {
+      const uint16_t* qh = q + (r * OR_ATT_HEADS + h) * OR_ATT_DIM;
+      double* o = out + (r * OR_ATT_HEADS + h) * OR_ATT_DIM;
+      for (int d = 0; d < OR_ATT_DIM; ++d) {
+        kq[d] = qsa_oracle_half_to_double(qh[d]);
+        o[d] = 0.0;
+      }
+      /* logits of the members of J, and their maximum */
+      int members = 0;
+      double m = -INFINITY;
+      for (int j = 0; j < OR_WIDTH; ++j) {
+        int64_t t = idx[j];
+#if QSA_ORACLE_MUTANT == 9
+        if (t < 0) t = 0; /* planted: a hole read as token 0 */
+#endif
+        if (t < 0) continue;
+#if QSA_ORACLE_MUTANT == 7
+        int seen = 0; /* planted: a repeated index counted once */
+        for (int j2 = 0; j2 < j; ++j2) seen |= (idx[j2] == idx[j]);
+        if (seen) {
+          logit[j] = -INFINITY;
+          continue;
+        }
+#endif
+        const uint16_t* krow = kv + t * OR_KV_ROW;
+        double dot = 0.0;
+        for (int d = 0; d < OR_ATT_DIM; ++d) {
+          dot += kq[d] * qsa_oracle_half_to_double(krow[d]);
+        }
+#if QSA_ORACLE_MUTANT == 6
+        logit[j] = dot; /* planted: softmax scale dropped */
+        (void)scale;
+#else
+        logit[j] = scale * dot;
+#endif
+        if (logit[j] > m) m = logit[j];
+        ++members;
+      }
+      if (members == 0) continue; /* empty J: output stays zero */
+      /* softmax weights relative to the maximum, then the weighted V sum */
+      double z = 0.0;
+      for (int j = 0; j < OR_WIDTH; ++j) {
+        int64_t t = idx[j];
+#if QSA_ORACLE_MUTANT == 9
+        if (t < 0) t = 0;
+#endif
+        if (t < 0 || logit[j] == -INFINITY) continue;
+        double w = exp(logit[j] - m);
+        z += w;
+        const uint16_t* vrow = kv + t * OR_KV_ROW + OR_ATT_DIM;
+        for (int e = 0; e < OR_ATT_DIM; ++e) {
+          o[e] += w * qsa_oracle_half_to_double(vrow[e]);
+        }
+      }
+      for (int e = 0; e < OR_ATT_DIM; ++e) o[e] /= z;
+    }
+  }
+  free(logit);
+  free(kq);
+  return rc;
+}
+
+/* Which mistake this build carries (0 = none). */
+int qsa_oracle_mutant(void) { return QSA_ORACLE_MUTANT; }

@@ -1,0 +1,302 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with:
+
+* the worked examples printed on the pages (``golden/pages_worked_examples.txt``),
+* an independent brute force on small integer-valued inputs (exact int64
+  scores, visible blocks counted token by token, selection by counting how
+  many blocks outrank each block -- no sort),
+* numpy's float64 gather and library sort on N(0,1) inputs,
+* closed-form special cases of selection and of attention,
+* torch's float64 softmax on gathered rows,
+* numpy's binary16 decoder, for every bit pattern.
+
+The same functions run against the trusted oracle (they must all pass) and
+against builds with one planted mistake (at least one must fail).
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+from paged_top_indexer_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "pages_worked_examples.txt")
+WIDTH, TOPK, RATIO = 2051, 512, 4
+
+
+def read_golden():
+    rows = []
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, L, qp, vis, valid = line.split()
+            rows.append((name, int(L), int(qp), int(vis), int(valid)))
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# independent brute force for selection
+
+def brute_visible(seq_len: int, query_pos: int) -> tuple[int, int]:
+    """Count, token by token, the tokens the query can see, the complete
+    groups of four among them and the leftover tail."""
+    seen = [t for t in range(max(0, seq_len)) if t <= query_pos]
+    blocks = [b for b in range(len(seen)) if 4 * b + 3 < len(seen)]
+    tail = [t for t in range(4 * len(blocks), len(seen))]
+    return len(blocks), len(tail)
+
+
+def brute_select_integer(q, kcache, bt, t2r, sl, qp) -> np.ndarray:
+    """Selection from exact integer scores and rank counting (inputs must be
+    integer-valued fp16)."""
+    R = q.shape[0]
+    out = np.full((R, WIDTH), -1, dtype=np.int32)
+    qi = q.astype(np.int64)
+    for r in range(R):
+        req = int(t2r[r])
+        V, T = brute_visible(int(sl[req]), int(qp[r]))
+        b = np.arange(V)
+        keys = kcache[bt[req, b // 128], b % 128, 0, :].astype(np.int64)  # [V,128]
+        dots = keys @ qi[r].T                                               # [V,4]
+        s = np.maximum(dots, 0).sum(axis=1)                                 # [V]
+        # rank = blocks with a larger score + earlier blocks with an equal score
+        better = (s[None, :] > s[:, None]) | ((s[None, :] == s[:, None]) & (b[None, :] < b[:, None]))
+        rank = better.sum(axis=1)
+        n = min(TOPK, V)
+        for blk in range(V):
+            if rank[blk] < n:
+                out[r, 4 * rank[blk]:4 * rank[blk] + 4] = 4 * blk + np.arange(4)
+        out[r, 4 * n:4 * n + T] = 4 * V + np.arange(T)
+    return out
+
+
+def integer_problem(seed: int, lengths, palette: int | None, q_range: int,
+                    num_pages: int = 96):
+    rng = np.random.default_rng(seed)
+    if palette:
+        pal = wl.int_f16(rng, -4, 4, (palette, 128))
+        kcache = pal[rng.integers(0, palette, size=(num_pages, 128))].reshape(num_pages, 128, 1, 128)
+    else:
+        kcache = wl.int_f16(rng, -4, 4, (num_pages, 128, 1, 128))
+    bt = wl.block_table_per_row(rng, lengths, num_pages)
+    q = wl.int_f16(rng, -q_range, q_range, (len(lengths), 4, 128))
+    t2r, sl, qp = wl.decode_rows(lengths)
+    return q, kcache, bt, t2r, sl, qp
+
+
+PIN_LENGTHS = [0, 1, 3, 4, 7, 512, 515, 516, 2044, 2047, 2048, 2049, 2052, 2055, 4099, 6001]
+
+
+def pin_select_brute_force_integer(orc):
+    """Bit-exact against the brute force, with and without massive ties."""
+    for seed, palette, qr in [(0, None, 4), (1, 8, 2), (2, 3, 1), (3, None, 1)]:
+        args = integer_problem(seed, PIN_LENGTHS, palette, qr)
+        got = orc.select(*args)
+        want = brute_select_integer(*args)
+        assert np.array_equal(got, want), f"brute force mismatch (seed {seed})"
+
+
+def pin_select_multirow_requests(orc):
+    """Several query rows per request (chunked-prefill style positions) and a
+    padded row with query position -1: V and T follow each row's position."""
+    rng = np.random.default_rng(11)
+    kcache = wl.int_f16(rng, -4, 4, (40, 128, 1, 128))
+    lengths = [3000, 700]
+    bt = wl.block_table_per_row(rng, lengths, 40)
+    t2r = np.array([0, 0, 0, 1, 1, 0], dtype=np.int32)
+    qp = np.array([2999, 2050, 13, 699, 515, -1], dtype=np.int64)
+    sl = np.array(lengths, dtype=np.int32)
+    q = wl.int_f16(rng, -3, 3, (6, 4, 128))
+    got = orc.select(q, kcache, bt, t2r, sl, qp)
+    want = brute_select_integer(q, kcache, bt, t2r, sl, qp)
+    assert np.array_equal(got, want)
+    assert np.all(got[5] == -1)
+
+
+def pin_select_worked_examples(orc):
+    """The pages' printed visible blocks and valid widths."""
+    for name, L, qp, vis, valid in read_golden():
+        V, T = orc.row_extent(L, qp)
+        assert V == vis, (name, V, vis)
+        rng = np.random.default_rng(5)
+        pages = wl.pages_needed(L)
+        kcache = wl.int_f16(rng, -4, 4, (pages + 3, 128, 1, 128))
+        bt = rng.permutation(pages + 3)[:pages].astype(np.int32).reshape(1, pages)
+        q = wl.int_f16(rng, -4, 4, (1, 4, 128))
+        out = orc.select(q, kcache, bt, np.array([0], np.int32), np.array([L], np.int32),
+                         np.array([qp], np.int64))
+        width = int((out[0] >= 0).sum())
+        assert width == valid, (name, width, valid)
+        assert np.all(out[0, width:] == -1)
+        # the tail is appended right after the expanded blocks
+        assert np.array_equal(out[0, width - T:width], 4 * V + np.arange(T))
+
+
+def pin_select_closed_forms(orc):
+    """Equal scores everywhere -> blocks in ascending order; one dominant
+    block -> first; zero query -> ascending; a key that only matches head 3
+    still scores."""
+    rng = np.random.default_rng(7)
+    L = 2600
+    pages = wl.pages_needed(L)
+    one = np.ones((pages, 128, 1, 128), np.float16)
+    bt = np.arange(pages, dtype=np.int32).reshape(1, pages)
+    t2r, sl, qp = wl.decode_rows([L])
+    V = L // 4
+    ascending = np.concatenate([np.arange(2048), 4 * V + np.arange(L % 4)])
+    for q in [wl.int_f16(rng, -4, 4, (1, 4, 128)), np.zeros((1, 4, 128), np.float16)]:
+        out = orc.select(q, one, bt, t2r, sl, qp)
+        assert np.array_equal(out[0, :ascending.size], ascending)
+    # a dominant block, visible only through head 3, at the last visible slot
+    kc = np.zeros((pages, 128, 1, 128), np.float16)
+    last = V - 1
+    kc[last // 128, last % 128, 0, 5] = 2.0
+    q = np.zeros((1, 4, 128), np.float16)
+    q[0, 3, 5] = 1.0
+    q[0, 0, 5] = -1.0  # head 0 sees it negatively: ReLU must drop that
+    out = orc.select(q, kc, bt, t2r, sl, qp)
+    assert np.array_equal(out[0, :4], 4 * last + np.arange(4))
+    assert np.array_equal(out[0, 4:8], np.arange(4))
+
+
+def pin_select_gather_and_sort_normal(orc):
+    """N(0,1) inputs: scores against a numpy float64 gather, selection
+    against numpy's lexsort of the float32-rounded scores."""
+    rng = np.random.default_rng(3)
+    lengths = [2900, 517, 64]
+    P = 64
+    kcache = wl.normal_f16(rng, (P, 128, 1, 128))
+    bt = wl.block_table_per_row(rng, lengths, P)
+    q = wl.normal_f16(rng, (3, 4, 128))
+    t2r, sl, qp = wl.decode_rows(lengths)
+    out = orc.select(q, kcache, bt, t2r, sl, qp)
+    for r, L in enumerate(lengths):
+        V = L // 4
+        b = np.arange(V)
+        keys = kcache[bt[r, b // 128], b % 128, 0, :].astype(np.float64)
+        s64 = np.maximum(keys @ q[r].astype(np.float64).T, 0.0).sum(axis=1)
+        s32 = s64.astype(np.float32)
+        got_scores = orc.row_scores(r, q, kcache, bt, t2r, sl, qp)
+        assert np.allclose(got_scores, s64, rtol=1e-6, atol=1e-6)
+        order = np.lexsort((b, -s32.astype(np.float64)))
+        n = min(TOPK, V)
+        want = (4 * order[:n, None] + np.arange(4)).reshape(-1)
+        assert np.array_equal(out[r, :4 * n], want)
+        assert np.array_equal(out[r, 4 * n:4 * n + L % 4], 4 * V + np.arange(L % 4))
+        assert np.all(out[r, 4 * n + L % 4:] == -1)
+
+
+# ---------------------------------------------------------------------------
+# attention
+
+def _exact_dot(a16, b16) -> float:
+    return float(np.dot(a16.astype(np.float64), b16.astype(np.float64)))
+
+
+def pin_attn_closed_forms(orc):
+    rng = np.random.default_rng(9)
+    NT = 64
+    kv = wl.normal_f16(rng, (NT, 512))
+    q = wl.normal_f16(rng, (5, 3, 256))
+    idx = np.full((5, WIDTH), -1, np.int32)
+    idx[1, 700] = 17                       # one valid index
+    idx[2, ::7] = 23                        # one index repeated, holes between
+    idx[3, :] = 41                          # one index over the full width
+    idx[4, 0] = 0                           # token 0 present...
+    idx[4, 0] = -1                          # ...then removed: all holes again
+    out = orc.sparse_attn(q, kv, idx, 1.0 / 16)
+    V = kv[:, 256:].astype(np.float64)
+    assert np.all(out[0] == 0.0) and np.all(out[4] == 0.0)
+    for r, t in [(1, 17), (2, 23), (3, 41)]:
+        assert np.allclose(out[r], np.broadcast_to(V[t], (3, 256)), rtol=0, atol=1e-12)
+
+
+def pin_attn_equal_logits_mean(orc):
+    """Identical K rows -> every logit equal -> output = mean of V over the
+    multiset of valid positions (duplicates weighted by multiplicity)."""
+    rng = np.random.default_rng(10)
+    NT = 32
+    kv = wl.normal_f16(rng, (NT, 512))
+    kv[:, :256] = kv[0, :256]
+    q = wl.normal_f16(rng, (1, 3, 256))
+    idx = np.full((1, WIDTH), -1, np.int32)
+    members = [3, 3, 3, 9, 30, 30, 0]
+    idx[0, [5, 100, 2000, 7, 8, 2050, 1]] = members
+    out = orc.sparse_attn(q, kv, idx, 0.0625)
+    want = kv[members, 256:].astype(np.float64).mean(axis=0)
+    assert np.allclose(out[0], np.broadcast_to(want, (3, 256)), rtol=0, atol=1e-12)
+
+
+def pin_attn_two_token_logistic(orc):
+    """Tokens a (once) and b (twice): weight of b is 2e^{l_b}/(e^{l_a}+2e^{l_b})
+    with l = scale * q.k from exact integer dot products."""
+    rng = np.random.default_rng(12)
+    kv = np.zeros((8, 512), np.float16)
+    kv[:, :256] = wl.int_f16(rng, -2, 2, (8, 256))
+    kv[:, 256:] = wl.normal_f16(rng, (8, 256))
+    q = wl.int_f16(rng, -1, 1, (1, 3, 256))
+    idx = np.full((1, WIDTH), -1, np.int32)
+    idx[0, 10], idx[0, 11], idx[0, 1500] = 2, 5, 5
+    scale = 0.03125
+    out = orc.sparse_attn(q, kv, idx, scale)
+    for h in range(3):
+        la = scale * _exact_dot(q[0, h], kv[2, :256])
+        lb = scale * _exact_dot(q[0, h], kv[5, :256])
+        wb = 1.0 / (1.0 + 0.5 * np.exp(la - lb))
+        want = (1 - wb) * kv[2, 256:].astype(np.float64) + wb * kv[5, 256:].astype(np.float64)
+        assert np.allclose(out[0, h], want, rtol=0, atol=1e-12)
+
+
+def pin_attn_torch_float64(orc):
+    """Random rows with holes and duplicates against torch's float64 softmax
+    over the gathered rows."""
+    import torch
+    rng = np.random.default_rng(13)
+    NT = 1024
+    kv = wl.normal_f16(rng, (NT, 512))
+    q = wl.normal_f16(rng, (4, 3, 256))
+    idx = wl.random_index_rows(rng, 4, NT, valid=WIDTH, distinct=False)
+    idx = wl.inject_holes_and_duplicates(rng, idx, 0.1, 0.1)
+    idx[3, 100:] = -1
+    scale = 1.0 / 16
+    out = orc.sparse_attn(q, kv, idx, scale)
+    kvt = torch.from_numpy(kv.astype(np.float64))
+    for r in range(4):
+        sel = torch.from_numpy(idx[r][idx[r] >= 0].astype(np.int64))
+        K, Vr = kvt[sel, :256], kvt[sel, 256:]
+        qt = torch.from_numpy(q[r].astype(np.float64))
+        p = torch.softmax(qt @ K.T * scale, dim=-1)
+        want = (p @ Vr).numpy()
+        assert np.allclose(out[r], want, rtol=0, atol=1e-12)
+
+
+def pin_half_to_double(orc):
+    """Every binary16 bit pattern against numpy's decoder."""
+    bits = np.arange(65536, dtype=np.uint32)
+    want = bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    got = np.array([orc.half_to_double(int(b)) for b in bits[::1]])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+ALL_PINS = [
+    pin_half_to_double,
+    pin_select_worked_examples,
+    pin_select_brute_force_integer,
+    pin_select_multirow_requests,
+    pin_select_closed_forms,
+    pin_select_gather_and_sort_normal,
+    pin_attn_closed_forms,
+    pin_attn_equal_logits_mean,
+    pin_attn_two_token_logistic,
+    pin_attn_torch_float64,
+]

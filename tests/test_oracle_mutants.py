@@ -1,0 +1,39 @@
+"""Each planted mistake in the oracle must be caught by at least one pin.
+
+The oracle source carries ten compile-time mutants (a dropped term, a wrong
+sign, an off-by-one, a transposed operand, ...).  Building each one and
+running the pins shows that the pins constrain every step of the oracle.
+"""
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    1: "ties ordered by descending index",
+    2: "ReLU dropped",
+    3: "page and slot transposed",
+    4: "tail omitted",
+    5: "one indexer head dropped",
+    6: "softmax scale dropped",
+    7: "a repeated index counted once",
+    8: "visible-block rule off by one",
+    9: "a hole read as token 0",
+    10: "scores ordered ascending",
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS), ids=lambda m: MUTANTS[m].replace(" ", "_"))
+def test_mutant_is_caught(tmp_path, mutant):
+    path = oracle.build(str(tmp_path / f"liboracle_m{mutant}.so"), mutant=mutant)
+    orc = oracle.Oracle(path)
+    assert orc.mutant == mutant
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError) as e:
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin catches mutant {mutant} ({MUTANTS[mutant]})"
