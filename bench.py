@@ -1,0 +1,238 @@
+"""Decode-step throughput of the QSA select + sparse-attention path on one
+MI355X.
+
+Workload: the long-context decode batch -- R=128 query rows, each of a
+131072-token request (32768 compressed blocks), a 32768-page fp16 N(0,1)
+compressed-key cache (1 GiB) behind random permuted block tables, and
+full-width [128,2051] sparse attention over a 131072-token packed fp16 KV
+cache (128 MiB).  Inputs are seeded synthetic data, resident in HBM before
+timing starts.
+
+One step = qsa_select then qsa_sparse_attn on one stream (the same two
+launches qsa_decode_step makes), with HIP events recorded on that stream
+around each stage.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "select+sparse-attn decode rows/sec and achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+COUNTERS = os.path.join(ROOT, "profiles", "select_long_context_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
+                  for f in ("qsa_select.hip", "qsa_launch.h", "qsa_capi.cpp")]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def select_algorithmic_bytes(seq_lens, query_pos, token_to_req) -> int:
+    """Bytes the selection must move per launch: per row, 256 B per visible
+    compressed key, 4 B per block-table entry read, the 1 KiB query, 16 B of
+    row metadata and the 8204 B output row."""
+    total = 0
+    for r in range(len(token_to_req)):
+        L = int(seq_lens[token_to_req[r]])
+        qp = int(query_pos[r])
+        v = max(0, min((qp + 1) // 4, L // 4))
+        total += 256 * v + 4 * (-(-v // 128)) + 1024 + 16 + 8204
+    return total
+
+
+def attn_algorithmic_bytes(indices: np.ndarray) -> int:
+    """Per row: 1 KiB per distinct valid token (K and V halves), the 8204 B
+    index row, the 1.5 KiB query and the 1.5 KiB output."""
+    total = 0
+    for row in indices:
+        total += 1024 * len(np.unique(row[row >= 0])) + 8204 + 1536 + 1536
+    return total
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(launch_bytes: int):
+    """HBM bytes per select launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, scale: float, max_seconds: float = 20.0) -> dict:
+    """The CPU oracle (single-threaded C, unmodified) on the host cores: the
+    whole decode step of the first rows of the same workload, until all rows
+    are done or max_seconds of work have been spent."""
+    import oracle
+
+    orc = oracle.default()
+    inputs = w.select_inputs()
+    done = 0
+    t0 = time.perf_counter()
+    outs = []
+    while done < w.rows and time.perf_counter() - t0 < max_seconds:
+        r = np.array([done])
+        q, kc, bt, t2r, sl, qp = inputs
+        sel = orc.select(q[r], kc, bt, t2r[r], sl, qp[r])
+        att = orc.sparse_attn(w.q_attn[r], w.kv, sel, scale)
+        outs.append((sel, att))
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {w.rows} rows of the same workload, select + attention "
+                      f"per row, {dt:.1f} s single-threaded", "_outs": outs}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_top_indexer_amd as qsa
+    from paged_top_indexer_amd import workloads as wl
+
+    t0 = time.perf_counter()
+    w = wl.long_context(args.seed)
+    log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    sel_in = [d(a) for a in w.select_inputs()]
+    kvd = d(w.kv)
+    k, v = qsa.kv_views(kvd)
+    q_attn = d(w.q_attn)
+    R = w.rows
+    idx = torch.empty((R, 2051), dtype=torch.int32, device=dev)
+    out = torch.empty((R, 3, 256), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sel_ws = torch.zeros(max(1, qsa.select_workspace_bytes(R, w.block_table.shape[1])),
+                         dtype=torch.uint8, device=dev)
+    att_ws = torch.zeros(max(1, qsa.sparse_attn_workspace_bytes(R)), dtype=torch.uint8, device=dev)
+    scale = wl.SOFTMAX_SCALE
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        qsa.qsa_select(*sel_in, out=idx, workspace=sel_ws)
+        if ev is not None:
+            ev[1].record(stream)
+        qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    sel_ms = [e[0].elapsed_time(e[1]) for e in events]
+    att_ms = [e[1].elapsed_time(e[2]) for e in events]
+    gpu_ms = events[0][0].elapsed_time(events[-1][2])
+    ms_per_step = gpu_ms / args.steps
+    log(f"select {np.mean(sel_ms):.3f} ms (min {np.min(sel_ms):.3f}), attention "
+        f"{np.mean(att_ms):.3f} ms, step {ms_per_step:.3f} ms, wall {wall * 1e3 / args.steps:.3f} ms")
+
+    # the same step through the single decode-step entry point
+    t_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t_ev[0].record(stream)
+    ws_all = torch.zeros(max(1, qsa.decode_step_workspace_bytes(R, w.block_table.shape[1])),
+                         dtype=torch.uint8, device=dev)
+    for _ in range(args.steps):
+        qsa.qsa_decode_step(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
+    t_ev[1].record(stream)
+    torch.cuda.synchronize()
+    decode_step_ms = t_ev[0].elapsed_time(t_ev[1]) / args.steps
+
+    got_idx = idx.cpu().numpy()
+    got_out = out.cpu().numpy()
+    sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req)
+    att_bytes = attn_algorithmic_bytes(got_idx)
+    sel_avg_s = float(np.mean(sel_ms)) / 1e3
+    att_avg_s = float(np.mean(att_ms)) / 1e3
+    achieved = sel_bytes / sel_avg_s / 1e9
+    traffic = stored_traffic(sel_bytes)
+    rows_per_s = R / (ms_per_step / 1e3)
+    step_gbs = (sel_bytes + att_bytes) / (ms_per_step / 1e3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)",
+        "config": {"workload": w.name, "rows": R, "seq_len": 131072, "visible_blocks": 32768,
+                   "cache_pages": 32768, "kv_tokens": 131072, "top_blocks": 512,
+                   "index_width": 2051},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "qsa_select_kernel",
+                     "bytes_per_launch": sel_bytes, "avg_launch_ms": round(sel_avg_s * 1e3, 4)},
+        "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
+                   "attention_bytes": att_bytes,
+                   "attention_gbs": round(att_bytes / att_avg_s / 1e9, 1),
+                   "step_gbs": round(step_gbs, 1),
+                   "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "decode_step_entry_ms": round(decode_step_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(w, scale)
+        outs = base.pop("_outs")
+        # the timed configuration's output on the rows the oracle finished
+        same = sum(np.array_equal(s[0], got_idx[i]) for i, s in enumerate(outs))
+        errs = [float(np.max(np.abs(got_out[i].astype(np.float64) - a)))
+                for i, (s, a) in enumerate(outs) if np.array_equal(s[0], got_idx[i])]
+        result["cpu_baseline"] = base
+        result["parity"] = {"rows_checked": len(outs), "selection_identical": int(same),
+                            "attention_max_abs_err": max(errs) if errs else None}
+        log(f"oracle: {base['value']:.2f} rows/s; identical selections {same}/{len(outs)}")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

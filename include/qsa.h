@@ -1,0 +1,206 @@
+/*
+ * qsa.h -- C ABI of the MI355X (gfx950) QSA sparse-attention decode library.
+ *
+ * Two stages of one decode step, as the page "vLLM: integrate FP16 packed QSA
+ * extension" (intel/llm-scaler PR #651) defines them in its sections
+ * "Summary" and "Exact contracts":
+ *
+ *   qsa_select       paged top-512 block selection -> [R,2051] token indices
+ *   qsa_sparse_attn  fp16 attention over exactly those indices
+ *   qsa_decode_step  both, back to back on one stream, indices stay on device
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are passed as qsa_tensor descriptors: a DEVICE pointer to the
+ *   first element (any storage offset already applied), a dtype code, and
+ *   shape/strides in elements.  The descriptors themselves are host memory
+ *   read during the call only.  The library never keeps a pointer.
+ * - Every call is asynchronous on `stream` (a hipStream_t; NULL = the legacy
+ *   default stream of the current device).  The library never allocates,
+ *   never synchronises and never prints.  Pointers must belong to the
+ *   current HIP device.
+ * - Fail-closed: all arguments are validated on the host before anything is
+ *   launched ("fail-closed dtype/layout checks" and "fail-closed
+ *   dtype/output checks" in the page's "Validation" section).  On a
+ *   validation status (anything but QSA_OK and QSA_ERR_LAUNCH) nothing is
+ *   launched and no output or workspace byte is written; qsa_last_error()
+ *   then describes the first failed check.  QSA_ERR_LAUNCH means the HIP
+ *   runtime rejected a kernel launch (qsa_decode_step: the selection may
+ *   already be enqueued when the attention launch is rejected).
+ * - Outputs are caller-owned and must not overlap any input or the
+ *   workspace; inputs are never written ("caller-owned output; inputs remain
+ *   unchanged", "Exact contracts").
+ * - R = 0 rows is a valid no-op returning QSA_OK.
+ * - Device-side preconditions that cannot be checked without a sync:
+ *   token_to_req[r] in [0, N); the block-table entries of every visible
+ *   block in [0, P); every attention index is -1 or in [0, NT); fp16 inputs
+ *   finite.  The kernels stay memory-safe when these fail (a row with an
+ *   out-of-range request is treated as empty, a page id outside [0,P) as an
+ *   all-zero key, visible blocks beyond the block table's width are not
+ *   read, an index outside [-1, NT) as a hole) but the result is then
+ *   unspecified.
+ * - Workspaces: device memory of at least the queried size, 256-byte
+ *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every call that returns
+ *   QSA_OK leaves the workspace's counters at zero again once the call has
+ *   completed on the stream, so a workspace can be reused by consecutive
+ *   calls on one stream.  Calls that run concurrently (different streams)
+ *   must not share a workspace.
+ * - Thread safety: any host thread may call; qsa_last_error() is per thread.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_API __attribute__((visibility("default")))
+
+/* Fixed contract constants ("Exact contracts", selection: token_topk=2048,
+ * compress_ratio=4, output [R,2051]). */
+#define QSA_TOKEN_TOPK 2048
+#define QSA_COMPRESS_RATIO 4
+#define QSA_TOPK_BLOCKS 512  /* token_topk / compress_ratio */
+#define QSA_OUT_WIDTH 2051   /* 2048 selected tokens + at most 3 tail tokens */
+#define QSA_PAGE_SLOTS 128   /* compressed keys per cache page */
+#define QSA_SEL_HEADS 4
+#define QSA_SEL_DIM 128
+#define QSA_ATT_HEADS 3
+#define QSA_ATT_DIM 256
+#define QSA_KV_PAGE_TOKENS 512
+
+typedef enum {
+  QSA_DTYPE_F16 = 1,
+  QSA_DTYPE_I32 = 2,
+  QSA_DTYPE_I64 = 3
+} qsa_dtype;
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_NULL = 1,      /* a required pointer or descriptor is NULL */
+  QSA_ERR_DTYPE = 2,     /* wrong dtype code */
+  QSA_ERR_SHAPE = 3,     /* wrong rank or extent */
+  QSA_ERR_LAYOUT = 4,    /* wrong strides, V offset or alignment */
+  QSA_ERR_ALIAS = 5,     /* an output overlaps an input or the workspace */
+  QSA_ERR_WORKSPACE = 6, /* workspace missing, too small or misaligned */
+  QSA_ERR_ARG = 7,       /* a scalar argument out of range */
+  QSA_ERR_LAUNCH = 8     /* the HIP runtime rejected a launch */
+} qsa_status;
+
+typedef struct qsa_tensor {
+  void* data;        /* device address of element [0,...,0] */
+  int32_t dtype;     /* qsa_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];  /* extents; entries >= ndim ignored */
+  int64_t stride[4]; /* strides in elements; entries >= ndim ignored */
+} qsa_tensor;
+
+/* hipStream_t, passed opaquely so this header needs no HIP header. */
+typedef void* qsa_stream;
+
+/* Name of a status code (static string). */
+QSA_API const char* qsa_status_string(int status);
+
+/* Detail of the last non-OK status returned to the calling thread (static
+ * per-thread buffer; "" when there is none). */
+QSA_API const char* qsa_last_error(void);
+
+/* The fixed contract constants: 2048, 4, 2051, 512.  NULL outputs skipped. */
+QSA_API void qsa_constants(int32_t* token_topk, int32_t* compress_ratio,
+                           int32_t* out_width, int32_t* topk_blocks);
+
+/* Workspace bytes qsa_select needs for `rows` query rows and a block table
+ * of `table_width` columns.  0 when rows == 0. */
+QSA_API size_t qsa_select_workspace_bytes(int64_t rows, int64_t table_width);
+
+/* Workspace bytes qsa_sparse_attn needs for `rows` rows. */
+QSA_API size_t qsa_sparse_attn_workspace_bytes(int64_t rows);
+
+/* Workspace bytes qsa_decode_step needs (both stages, one buffer). */
+QSA_API size_t qsa_decode_step_workspace_bytes(int64_t rows, int64_t table_width);
+
+/*
+ * qsa_select -- fused paged top-512 selection ("Summary": reads paged
+ * compressed keys, computes four-head ReLU(Q*K) scores, performs streaming
+ * top-512 selection, expands blocks to 2,048 tokens, appends the tail and
+ * writes caller-owned [R,2051] int32 output; "Exact contracts", selection).
+ *
+ *   q            F16 [R,4,128] contiguous: 4 indexer heads per query row.
+ *   kcache       F16 [P,128,1,128] contiguous, P >= 1: compressed keys, 128
+ *                per page (vllm qsa_cache.py page: the compressed cache's
+ *                block table and slot mapping).
+ *   block_table  I32 [N,W], stride[1] == 1, stride[0] >= W: physical page
+ *                of logical page j of request n.  Only the first
+ *                ceil(V/128) entries of a row are read.
+ *   token_to_req I32 [R] (stride 1): request of each query row.
+ *   seq_lens     I32 [N] (stride 1): tokens of each request.
+ *   query_pos    I64 [R] (stride 1): logical position of each query row
+ *                (a decode row has L-1; -1 marks a padded row).
+ *   out          I32 [R,2051] contiguous, written.
+ *
+ * Per row r: V = max(0, min(floor((qp+1)/4), floor(L/4))) visible blocks
+ * (qsa_cache.py page, the visible-block rule of _build_qsa_metadata_kernel),
+ * T = max(0, min(qp+1, L) - 4V) tail tokens.  Block b's key is
+ * kcache[block_table[req][b/128]][b%128][0]; its score is the fp32 sum over
+ * the 4 heads of ReLU(q_h . key) with fp32 accumulation.  The first
+ * min(512, V) blocks in (score descending, block index ascending) order are
+ * written as tokens 4b..4b+3, then the T tail tokens 4V..4V+T-1, then -1.
+ */
+QSA_API int qsa_select(const qsa_tensor* q, const qsa_tensor* kcache,
+                       const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                       const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                       const qsa_tensor* out, void* workspace, size_t workspace_bytes,
+                       qsa_stream stream);
+
+/*
+ * qsa_sparse_attn -- fp16 sparse decode attention over logical indices with
+ * holes and duplicates ("Exact contracts", attention).
+ *
+ *   q        F16 [R,3,256] contiguous: 3 query heads sharing one K/V head.
+ *   k        F16 [NP,512,1,256], strides exactly [262144,512,256,1]: the K
+ *            half of a packed KV cache whose token rows are 512 elements,
+ *            K = row[0:256].
+ *   v        F16, same shape and strides as k, and v->data == k->data + 256
+ *            elements (the page's "V storage_offset=256").
+ *   indices  I32 [R,2051] contiguous: token t addresses flat row t of the
+ *            packed cache (page t/512, row t%512); -1 is a hole.
+ *   softmax_scale  finite, > 0 (logits are scale * q.k).
+ *   out      F16 [R,3,256] contiguous, written.
+ *
+ * out[r][h] = sum_j p_j V[idx_j] with p = softmax over the valid positions
+ * j of row r of scale * q[r][h].K[idx_j]; every position counts, so a
+ * repeated index weighs once per repetition; a row with no valid index
+ * yields zeros.  fp32 accumulation, fp16 round-to-nearest-even output.
+ */
+QSA_API int qsa_sparse_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_tensor* v,
+                            const qsa_tensor* indices, float softmax_scale,
+                            const qsa_tensor* out, void* workspace, size_t workspace_bytes,
+                            qsa_stream stream);
+
+/*
+ * qsa_decode_step -- qsa_select then qsa_sparse_attn on one stream, with the
+ * selection output fed to the attention without any host synchronisation
+ * ("Summary": no per-row .item()/CPU synchronisation).
+ *
+ * The selection arguments are as for qsa_select; q_attn, k, v,
+ * softmax_scale and out are as for qsa_sparse_attn with the same R.
+ * `indices` (I32 [R,2051] contiguous, caller-owned) receives the selection
+ * and is read back by the attention.  It is an output and must not overlap
+ * any input, `out` or the workspace.
+ */
+QSA_API int qsa_decode_step(const qsa_tensor* q_sel, const qsa_tensor* kcache,
+                            const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                            const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                            const qsa_tensor* q_attn, const qsa_tensor* k,
+                            const qsa_tensor* v, float softmax_scale,
+                            const qsa_tensor* indices, const qsa_tensor* out,
+                            void* workspace, size_t workspace_bytes, qsa_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

@@ -140,8 +140,16 @@ static int by_score_then_index(const void* pa, const void* pb) {
   return 0;
 }
 
-/* Score of one compressed key against the row's four indexer heads. */
-static float block_score(const uint16_t* q_row, const uint16_t* key) {
+/* The row's four query heads widened to double. */
+static void widen_query(const uint16_t* q_row, double* qd) {
+  for (int i = 0; i < OR_SEL_HEADS * OR_SEL_DIM; ++i) qd[i] = qsa_oracle_half_to_double(q_row[i]);
+}
+
+/* Score of one compressed key against the row's four indexer heads (qd:
+ * the row's query already widened to double, [4][128]). */
+static float block_score(const double* qd, const uint16_t* key) {
+  double kd[OR_SEL_DIM];
+  for (int d = 0; d < OR_SEL_DIM; ++d) kd[d] = qsa_oracle_half_to_double(key[d]);
   double total = 0.0;
   int heads = OR_SEL_HEADS;
 #if QSA_ORACLE_MUTANT == 5
@@ -150,8 +158,7 @@ static float block_score(const uint16_t* q_row, const uint16_t* key) {
   for (int h = 0; h < heads; ++h) {
     double dot = 0.0;
     for (int d = 0; d < OR_SEL_DIM; ++d) {
-      dot += qsa_oracle_half_to_double(q_row[h * OR_SEL_DIM + d]) *
-             qsa_oracle_half_to_double(key[d]);
+      dot += qd[h * OR_SEL_DIM + d] * kd[d];
     }
 #if QSA_ORACLE_MUTANT == 2
     total += dot; /* planted: ReLU dropped */
@@ -202,13 +209,14 @@ int qsa_oracle_row_scores(int64_t r, int64_t num_pages, int64_t num_reqs,
   qsa_oracle_row_extent(seq_lens[req], query_pos[r], &v, &t);
   *visible = v;
   if (v > max_blocks) return OR_ERR_ARG;
-  const uint16_t* q_row = q + r * OR_SEL_HEADS * OR_SEL_DIM;
+  double qd[OR_SEL_HEADS * OR_SEL_DIM];
+  widen_query(q + r * OR_SEL_HEADS * OR_SEL_DIM, qd);
   const int32_t* table_row = block_table + req * table_width;
   for (int64_t b = 0; b < v; ++b) {
     int err = OR_OK;
     const uint16_t* key = key_address(kcache, num_pages, table_row, table_width, b, &err);
     if (!key) return err;
-    scores[b] = block_score(q_row, key);
+    scores[b] = block_score(qd, key);
   }
   return OR_OK;
 }
@@ -236,7 +244,8 @@ int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
       all = (scored_block*)malloc((size_t)v * sizeof(scored_block));
       if (!all) return OR_ERR_NOMEM;
     }
-    const uint16_t* q_row = q + r * OR_SEL_HEADS * OR_SEL_DIM;
+    double qd[OR_SEL_HEADS * OR_SEL_DIM];
+    widen_query(q + r * OR_SEL_HEADS * OR_SEL_DIM, qd);
     const int32_t* table_row = block_table + req * table_width;
     for (int64_t b = 0; b < v; ++b) {
       int err = OR_OK;
@@ -245,7 +254,7 @@ int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
         free(all);
         return err;
       }
-      all[b].score = block_score(q_row, key);
+      all[b].score = block_score(qd, key);
       all[b].block = b;
     }
     if (v > 1) qsort(all, (size_t)v, sizeof(scored_block), by_score_then_index);

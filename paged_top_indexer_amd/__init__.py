@@ -1,3 +1,23 @@
 """MI355X-native QSA sparse-attention decode: paged top-512 block selection
 and sparse attention over the selected tokens, as hand-written HIP kernels
-for gfx950 behind a small C ABI (``include/qsa.h``)."""
+for gfx950 behind a small C ABI (``include/qsa.h``).
+
+The three entry points carry the C names; the library is loaded on first
+use and there is no fallback path.
+"""
+
+from ._binding import (  # noqa: F401
+    COMPRESS_RATIO,
+    OUT_WIDTH,
+    TOKEN_TOPK,
+    TOPK_BLOCKS,
+    constants,
+    decode_step_workspace_bytes,
+    kv_views,
+    library,
+    qsa_decode_step,
+    qsa_select,
+    qsa_sparse_attn,
+    select_workspace_bytes,
+    sparse_attn_workspace_bytes,
+)

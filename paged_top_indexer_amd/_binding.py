@@ -1,0 +1,216 @@
+"""ctypes binding of libqsa_amd.so (include/qsa.h).
+
+Argument marshalling only: torch tensors become qsa_tensor descriptors,
+the stream is torch's current HIP stream, and workspaces are zero-filled
+device buffers cached per (device, stream).  Every step of the path runs in
+the library's HIP kernels; there is no fallback -- if the library is missing
+or refuses the arguments, these functions raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libqsa_amd.so")
+
+F16, I32, I64 = 1, 2, 3
+TOKEN_TOPK, COMPRESS_RATIO, OUT_WIDTH, TOPK_BLOCKS = 2048, 4, 2051, 512
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_DTYPE", 3: "QSA_ERR_SHAPE",
+          4: "QSA_ERR_LAYOUT", 5: "QSA_ERR_ALIAS", 6: "QSA_ERR_WORKSPACE",
+          7: "QSA_ERR_ARG", 8: "QSA_ERR_LAUNCH"}
+
+
+class QsaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+def descriptor(data_ptr: int, dtype: int, shape, stride) -> QsaTensor:
+    t = QsaTensor()
+    t.data = ctypes.c_void_p(int(data_ptr))
+    t.dtype = int(dtype)
+    t.ndim = len(shape)
+    for i, (s, st) in enumerate(zip(shape, stride)):
+        t.shape[i] = int(s)
+        t.stride[i] = int(st)
+    return t
+
+
+_lib = None
+_lock = threading.Lock()
+
+_P = ctypes.POINTER(QsaTensor)
+
+
+def library() -> ctypes.CDLL:
+    """Load libqsa_amd.so (built by paged_top_indexer_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY):
+                raise RuntimeError(
+                    f"{LIBRARY} is missing: build it with `python -m paged_top_indexer_amd.build` "
+                    "(there is no fallback implementation)")
+            lib = ctypes.CDLL(LIBRARY)
+            sz, i64, vp, f32 = ctypes.c_size_t, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+            lib.qsa_status_string.argtypes = [ctypes.c_int]
+            lib.qsa_status_string.restype = ctypes.c_char_p
+            lib.qsa_last_error.argtypes = []
+            lib.qsa_last_error.restype = ctypes.c_char_p
+            lib.qsa_constants.argtypes = [ctypes.POINTER(ctypes.c_int32)] * 4
+            lib.qsa_constants.restype = None
+            lib.qsa_select_workspace_bytes.argtypes = [i64, i64]
+            lib.qsa_select_workspace_bytes.restype = sz
+            lib.qsa_sparse_attn_workspace_bytes.argtypes = [i64]
+            lib.qsa_sparse_attn_workspace_bytes.restype = sz
+            lib.qsa_decode_step_workspace_bytes.argtypes = [i64, i64]
+            lib.qsa_decode_step_workspace_bytes.restype = sz
+            lib.qsa_select.argtypes = [_P] * 7 + [vp, sz, vp]
+            lib.qsa_select.restype = ctypes.c_int
+            lib.qsa_sparse_attn.argtypes = [_P] * 4 + [f32, _P, vp, sz, vp]
+            lib.qsa_sparse_attn.restype = ctypes.c_int
+            lib.qsa_decode_step.argtypes = [_P] * 9 + [f32, _P, _P, vp, sz, vp]
+            lib.qsa_decode_step.restype = ctypes.c_int
+            _lib = lib
+        return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        detail = library().qsa_last_error().decode()
+        raise RuntimeError(f"{STATUS.get(status, status)}: {detail}")
+
+
+def constants() -> tuple[int, int, int, int]:
+    vals = [ctypes.c_int32() for _ in range(4)]
+    library().qsa_constants(*[ctypes.byref(v) for v in vals])
+    return tuple(v.value for v in vals)
+
+
+def select_workspace_bytes(rows: int, table_width: int) -> int:
+    return int(library().qsa_select_workspace_bytes(int(rows), int(table_width)))
+
+
+def sparse_attn_workspace_bytes(rows: int) -> int:
+    return int(library().qsa_sparse_attn_workspace_bytes(int(rows)))
+
+
+def decode_step_workspace_bytes(rows: int, table_width: int) -> int:
+    return int(library().qsa_decode_step_workspace_bytes(int(rows), int(table_width)))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float16: F16, torch.int32: I32, torch.int64: I64}
+    return codes.get(t.dtype, 0)
+
+
+def tensor_desc(t) -> QsaTensor:
+    """Descriptor of a torch tensor (the element pointer includes the storage
+    offset).  Unsupported dtypes get code 0, which the library rejects."""
+    return descriptor(t.data_ptr(), _dtype_code(t), tuple(t.shape), tuple(t.stride()))
+
+
+def kv_views(kv):
+    """K and V views of a packed [NP, 512, 512] fp16 cache: shape
+    [NP,512,1,256], strides [262144,512,256,1], V at storage offset +256."""
+    pages = kv.shape[0]
+    split = kv.view(pages, 512, 2, 256)
+    return split[:, :, 0:1, :], split[:, :, 1:2, :]
+
+
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device, stream_handle: int):
+    """A zero-filled device buffer of at least nbytes, cached per
+    (device, stream).  The library leaves its counters at zero after every
+    call, so consecutive calls on one stream may share it."""
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    key = (str(device), int(stream_handle))
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _ws_args(nbytes, device, stream_handle, ws):
+    if ws is None:
+        ws = workspace(nbytes, device, stream_handle)
+    if ws is None:
+        return None, 0
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def qsa_select(q, kcache, block_table, token_to_req, seq_lens, query_pos, out=None,
+               workspace=None, stream=None):
+    """Paged top-512 selection; returns out ([R,2051] int32)."""
+    torch = _torch()
+    lib = library()
+    R = q.shape[0]
+    if out is None:
+        out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
+    sh = _stream(stream, q.device)
+    need = select_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
+    ws, ws_bytes = _ws_args(need, q.device, sh, workspace)
+    descs = [tensor_desc(t) for t in (q, kcache, block_table, token_to_req, seq_lens, query_pos, out)]
+    check(lib.qsa_select(*[ctypes.byref(d) for d in descs], ws, ws_bytes, ctypes.c_void_p(sh)))
+    return out
+
+
+def qsa_sparse_attn(q, k, v, indices, softmax_scale: float, out=None, workspace=None, stream=None):
+    """Sparse attention over index rows; returns out ([R,3,256] fp16)."""
+    torch = _torch()
+    lib = library()
+    R = q.shape[0]
+    if out is None:
+        out = torch.empty((R, 3, 256), dtype=torch.float16, device=q.device)
+    sh = _stream(stream, q.device)
+    ws, ws_bytes = _ws_args(sparse_attn_workspace_bytes(R), q.device, sh, workspace)
+    descs = [tensor_desc(t) for t in (q, k, v, indices)]
+    od = tensor_desc(out)
+    check(lib.qsa_sparse_attn(*[ctypes.byref(d) for d in descs], ctypes.c_float(softmax_scale),
+                              ctypes.byref(od), ws, ws_bytes, ctypes.c_void_p(sh)))
+    return out
+
+
+def qsa_decode_step(q_sel, kcache, block_table, token_to_req, seq_lens, query_pos, q_attn, k, v,
+                    softmax_scale: float, indices=None, out=None, workspace=None, stream=None):
+    """Selection then attention on one stream; returns (indices, out)."""
+    torch = _torch()
+    lib = library()
+    R = q_sel.shape[0]
+    if indices is None:
+        indices = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q_sel.device)
+    if out is None:
+        out = torch.empty((R, 3, 256), dtype=torch.float16, device=q_sel.device)
+    sh = _stream(stream, q_sel.device)
+    need = decode_step_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
+    ws, ws_bytes = _ws_args(need, q_sel.device, sh, workspace)
+    first = [tensor_desc(t) for t in (q_sel, kcache, block_table, token_to_req, seq_lens,
+                                      query_pos, q_attn, k, v)]
+    idd, od = tensor_desc(indices), tensor_desc(out)
+    check(lib.qsa_decode_step(*[ctypes.byref(d) for d in first], ctypes.c_float(softmax_scale),
+                              ctypes.byref(idd), ctypes.byref(od), ws, ws_bytes,
+                              ctypes.c_void_p(sh)))
+    return indices, out

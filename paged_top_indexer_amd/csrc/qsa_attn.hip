@@ -1,0 +1,268 @@
+// qsa_attn.hip -- fp16 sparse decode attention over [R,2051] logical token
+// indices with holes and duplicates, for gfx950.
+//
+// Implements the attention contract of the page "vLLM: integrate FP16 packed
+// QSA extension" ("Exact contracts", attention): Q/output [R,3,256] fp16, a
+// packed K/V cache whose token rows hold K in elements 0..255 and V in
+// 256..511, index rows of 2051 int32 with -1 holes and repeated entries.
+// Every valid position is one softmax member (a repeated index weighs once
+// per repetition); a row without valid positions yields zeros.
+//
+// Design (MI355X / CDNA4): split-K over index positions.
+//  * Workgroup (row, split) = 4 waves; each wave walks tiles of 16 index
+//    positions.  Per tile, S^T = K_tile . Q^T runs on
+//    v_mfma_f32_16x16x32_f16 (A = 16 gathered K rows, lane l loading row
+//    l % 16 at bytes [64c + 16(l/16), +16) for c = 0..7; B = the 3 query
+//    heads, columns 3..15 zero).  Lane (h + 16g) then holds the logits of
+//    head h for positions 4g..4g+3.
+//  * Online softmax in base 2 (scale * log2 e folded into the logits), with
+//    running max and sum per head, fp32.
+//  * P.V on the vector ALU: lane l owns output dims 4l..4l+3 of all three
+//    heads; each gathered V row is one coalesced 512-byte wave load; the
+//    probabilities are broadcast from the MFMA lanes with v_readlane.
+//  * The 4 waves merge in LDS; each workgroup writes its unnormalised
+//    partial (max, sum, o[3][256]); a combine kernel merges the splits of a
+//    row and rounds to fp16.  With a single split the workgroup writes the
+//    final output itself.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "qsa_launch.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* kv;
+  const int32_t* indices;
+  uint16_t* out;
+  float* partial;  // [rows][splits][3][256]
+  float* stats;    // [rows][splits][3][2]
+  int64_t rows, num_tokens;
+  float scale_log2;
+  int splits;
+  int split_positions;
+};
+
+struct Smem {
+  float o[kWaves][kAttHeads][kAttDim];
+  float m[kWaves][kAttHeads];
+  float l[kWaves][kAttHeads];
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+__global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t r = blockIdx.x / p.splits;
+  const int split = blockIdx.x % p.splits;
+  if (r >= p.rows) return;
+
+  const int n = lane & 15;  // token row of A / head column of B
+  const int g = lane >> 4;
+
+  // Q^T as the B operand: lane holds head n (if < 3), dims 32c + 8g .. +8.
+  half8 qb[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    qb[c] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (n < kAttHeads) {
+      qb[c] = *reinterpret_cast<const half8*>(p.q + (r * kAttHeads + n) * kAttDim + 32 * c + 8 * g);
+    }
+  }
+
+  const int wave_positions = p.split_positions / kWaves;
+  const int pos_begin = split * p.split_positions + wave * wave_positions;
+  const int pos_end = min(kOutWidth, pos_begin + wave_positions);
+  const int32_t* idx_row = p.indices + r * kOutWidth;
+
+  float m_run = -INFINITY;  // running max of head n (base-2 logits)
+  float l_run = 0.f;        // this lane's share of the running sum of head n
+  float o[kAttHeads][4];
+#pragma unroll
+  for (int h = 0; h < kAttHeads; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
+
+#pragma unroll 1
+  for (int tile = pos_begin; tile < pos_end; tile += 16) {
+    const int pos = tile + n;
+    int32_t idx = -1;
+    if (pos < pos_end) idx = idx_row[pos];
+    const bool valid = idx >= 0 && idx < p.num_tokens;
+    const int64_t tok = valid ? idx : 0;
+    const uint64_t vmask = __ballot(valid);  // bit t: position tile + t is valid
+
+    // K rows of the 16 positions (A operand) and this lane's slice of the
+    // 16 V rows, all issued before any math.
+    const half8* kp = reinterpret_cast<const half8*>(p.kv + tok * kKvRow) + g;
+    half8 ka[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ka[c] = kp[4 * c];
+    half4 vv[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int64_t tt = __builtin_amdgcn_readlane((int)tok, t);
+      vv[t] = *reinterpret_cast<const half4*>(p.kv + tt * kKvRow + kAttDim + 4 * lane);
+    }
+
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[c], qb[c], acc, 0, 0, 0);
+    }
+    // lane (h + 16g): logits of head h for positions 4g + v
+    float s[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const bool ok = (vmask >> (4 * g + v)) & 1ull;
+      s[v] = ok ? acc[v] * p.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[v]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    float alpha = 1.f;
+    float pr[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m_new != -INFINITY) {
+      alpha = exp2_fast(m_run - m_new);  // 0 when m_run is -inf
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pr[v] = exp2_fast(s[v] - m_new);
+    }
+    m_run = m_new;
+    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+
+#pragma unroll
+    for (int h = 0; h < kAttHeads; ++h) {
+      const float a = readlane_f(alpha, h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[h][e] *= a;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float vf[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vf[e] = (float)vv[t][e];
+#pragma unroll
+      for (int h = 0; h < kAttHeads; ++h) {
+        const float pw = readlane_f(pr[t & 3], h + 16 * (t >> 2));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[h][e] = fmaf(pw, vf[e], o[h][e]);
+      }
+    }
+  }
+
+  // per-wave partial: reduce the sum over the four lane groups of a head
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (lane < kAttHeads) {
+    sm.m[wave][lane] = m_run;
+    sm.l[wave][lane] = l_run;
+  }
+#pragma unroll
+  for (int h = 0; h < kAttHeads; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.o[wave][h][4 * lane + e] = o[h][e];
+  __syncthreads();
+
+  // merge the 4 waves: thread tid owns dim tid of every head
+  const int e = tid;
+#pragma unroll
+  for (int h = 0; h < kAttHeads; ++h) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2_fast(sm.m[w][h] - M);
+        L = fmaf(f, sm.l[w][h], L);
+        O = fmaf(f, sm.o[w][h][e], O);
+      }
+    }
+    if (p.splits == 1) {
+      const float y = L > 0.f ? O / L : 0.f;
+      const _Float16 yh = (_Float16)y;
+      p.out[(r * kAttHeads + h) * kAttDim + e] = *reinterpret_cast<const uint16_t*>(&yh);
+    } else {
+      const int64_t slot = (r * p.splits + split) * kAttHeads + h;
+      p.partial[slot * kAttDim + e] = O;
+      if (e == 0) {
+        p.stats[slot * 2 + 0] = M;
+        p.stats[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// One workgroup per row: merge the row's split partials, normalise, round.
+__global__ __launch_bounds__(kThreads) void qsa_attn_combine_kernel(AttnParams p) {
+  const int64_t r = blockIdx.x;
+  const int e = threadIdx.x;
+  if (r >= p.rows) return;
+#pragma unroll
+  for (int h = 0; h < kAttHeads; ++h) {
+    float M = -INFINITY;
+    for (int s = 0; s < p.splits; ++s) {
+      M = fmaxf(M, p.stats[((r * p.splits + s) * kAttHeads + h) * 2]);
+    }
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < p.splits; ++s) {
+        const int64_t slot = (r * p.splits + s) * kAttHeads + h;
+        const float f = exp2_fast(p.stats[slot * 2] - M);
+        L = fmaf(f, p.stats[slot * 2 + 1], L);
+        O = fmaf(f, p.partial[slot * kAttDim + e], O);
+      }
+    }
+    const float y = L > 0.f ? O / L : 0.f;
+    const _Float16 yh = (_Float16)y;
+    p.out[(r * kAttHeads + h) * kAttDim + e] = *reinterpret_cast<const uint16_t*>(&yh);
+  }
+}
+
+}  // namespace
+
+int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
+  if (a.rows == 0) return 0;
+  AttnParams p;
+  p.q = a.q;
+  p.kv = a.kv;
+  p.indices = a.indices;
+  p.out = a.out;
+  char* ws = static_cast<char*>(a.workspace);
+  p.partial = plan.bytes ? reinterpret_cast<float*>(ws + plan.partial_off) : nullptr;
+  p.stats = plan.bytes ? reinterpret_cast<float*>(ws + plan.stats_off) : nullptr;
+  p.rows = a.rows;
+  p.num_tokens = a.num_tokens;
+  p.scale_log2 = a.scale_log2;
+  p.splits = plan.splits;
+  p.split_positions = plan.split_positions;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(qsa_attn_kernel, dim3((unsigned)(a.rows * plan.splits)), dim3(kThreads), 0,
+                     s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || plan.splits == 1) return (int)err;
+  hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)a.rows), dim3(kThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,464 @@
+// qsa_capi.cpp -- the C ABI declared in include/qsa.h: fail-closed argument
+// validation, launch planning and dispatch.  Plain host C++: no HIP header,
+// no device code; every check runs before anything is enqueued.
+//
+// The checks follow the contracts of the page "vLLM: integrate FP16 packed
+// QSA extension" ("Exact contracts": dtypes, shapes, the exact-packed K/V
+// strides [262144,512,256,1] and V storage offset 256, caller-owned
+// outputs, unchanged inputs; "Validation": fail-closed dtype/layout/output
+// checks).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/qsa.h"
+#include "qsa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int64_t elem_size(int32_t dtype) {
+  switch (dtype) {
+    case QSA_DTYPE_F16: return 2;
+    case QSA_DTYPE_I32: return 4;
+    case QSA_DTYPE_I64: return 8;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int32_t dtype) {
+  switch (dtype) {
+    case QSA_DTYPE_F16: return "f16";
+    case QSA_DTYPE_I32: return "i32";
+    case QSA_DTYPE_I64: return "i64";
+    default: return "unknown";
+  }
+}
+
+// Byte range [lo, hi) a tensor can touch (empty when any extent is 0).
+struct Span {
+  uintptr_t lo = 0, hi = 0;
+};
+
+Span span_of(const qsa_tensor* t) {
+  Span s;
+  int64_t last = 0;
+  for (int d = 0; d < t->ndim; ++d) {
+    if (t->shape[d] == 0) return s;
+    last += (t->shape[d] - 1) * t->stride[d];
+  }
+  s.lo = reinterpret_cast<uintptr_t>(t->data);
+  s.hi = s.lo + static_cast<uintptr_t>((last + 1) * elem_size(t->dtype));
+  return s;
+}
+
+bool overlaps(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+// Checks dtype, rank and (when want[d] >= 0) each extent.
+int check_tensor(const char* name, const qsa_tensor* t, int32_t dtype, int ndim,
+                 const int64_t* want) {
+  if (!t) return fail(QSA_ERR_NULL, "%s: descriptor is NULL", name);
+  if (t->dtype != dtype) {
+    return fail(QSA_ERR_DTYPE, "%s: dtype %s (code %d), expected %s", name, dtype_name(t->dtype),
+                (int)t->dtype, dtype_name(dtype));
+  }
+  if (t->ndim != ndim) return fail(QSA_ERR_SHAPE, "%s: rank %d, expected %d", name, (int)t->ndim, ndim);
+  for (int d = 0; d < ndim; ++d) {
+    if (t->shape[d] < 0) return fail(QSA_ERR_SHAPE, "%s: negative extent in dim %d", name, d);
+    if (want[d] >= 0 && t->shape[d] != want[d]) {
+      return fail(QSA_ERR_SHAPE, "%s: dim %d is %lld, expected %lld", name, d,
+                  (long long)t->shape[d], (long long)want[d]);
+    }
+  }
+  int64_t numel = 1;
+  for (int d = 0; d < ndim; ++d) numel *= t->shape[d];
+  if (numel > 0 && !t->data) return fail(QSA_ERR_NULL, "%s: data pointer is NULL", name);
+  return QSA_OK;
+}
+
+int check_contiguous(const char* name, const qsa_tensor* t) {
+  int64_t expect = 1;
+  for (int d = t->ndim - 1; d >= 0; --d) {
+    if (t->shape[d] > 1 && t->stride[d] != expect) {
+      return fail(QSA_ERR_LAYOUT, "%s: not contiguous (dim %d stride %lld, expected %lld)", name, d,
+                  (long long)t->stride[d], (long long)expect);
+    }
+    expect *= t->shape[d];
+  }
+  return QSA_OK;
+}
+
+int check_aligned(const char* name, const qsa_tensor* t, uintptr_t align) {
+  if (reinterpret_cast<uintptr_t>(t->data) % align) {
+    return fail(QSA_ERR_LAYOUT, "%s: data pointer not %zu-byte aligned", name, (size_t)align);
+  }
+  return QSA_OK;
+}
+
+#define QSA_TRY(expr)              \
+  do {                             \
+    int rc_ = (expr);              \
+    if (rc_ != QSA_OK) return rc_; \
+  } while (0)
+
+struct SelectView {
+  int64_t rows = 0, pages = 0, reqs = 0, width = 0, bt_stride = 0;
+};
+
+int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* bt,
+                    const qsa_tensor* t2r, const qsa_tensor* sl, const qsa_tensor* qp,
+                    const qsa_tensor* out, SelectView* v) {
+  const int64_t any3[3] = {-1, QSA_SEL_HEADS, QSA_SEL_DIM};
+  QSA_TRY(check_tensor("q", q, QSA_DTYPE_F16, 3, any3));
+  QSA_TRY(check_contiguous("q", q));
+  QSA_TRY(check_aligned("q", q, 16));
+  const int64_t R = q->shape[0];
+  const int64_t kshape[4] = {-1, QSA_PAGE_SLOTS, 1, QSA_SEL_DIM};
+  QSA_TRY(check_tensor("kcache", kcache, QSA_DTYPE_F16, 4, kshape));
+  QSA_TRY(check_contiguous("kcache", kcache));
+  QSA_TRY(check_aligned("kcache", kcache, 16));
+  if (kcache->shape[0] < 1) return fail(QSA_ERR_SHAPE, "kcache: needs at least one page");
+  const int64_t bshape[2] = {-1, -1};
+  QSA_TRY(check_tensor("block_table", bt, QSA_DTYPE_I32, 2, bshape));
+  const int64_t N = bt->shape[0], W = bt->shape[1];
+  if (W > 1 && bt->stride[1] != 1) return fail(QSA_ERR_LAYOUT, "block_table: stride[1] must be 1");
+  if (N > 1 && bt->stride[0] < W) return fail(QSA_ERR_LAYOUT, "block_table: stride[0] < width");
+  const int64_t rshape[1] = {R};
+  QSA_TRY(check_tensor("token_to_req", t2r, QSA_DTYPE_I32, 1, rshape));
+  QSA_TRY(check_contiguous("token_to_req", t2r));
+  const int64_t nshape[1] = {N};
+  QSA_TRY(check_tensor("seq_lens", sl, QSA_DTYPE_I32, 1, nshape));
+  QSA_TRY(check_contiguous("seq_lens", sl));
+  QSA_TRY(check_tensor("query_pos", qp, QSA_DTYPE_I64, 1, rshape));
+  QSA_TRY(check_contiguous("query_pos", qp));
+  const int64_t oshape[2] = {R, QSA_OUT_WIDTH};
+  QSA_TRY(check_tensor("out", out, QSA_DTYPE_I32, 2, oshape));
+  QSA_TRY(check_contiguous("out", out));
+  if (R > 0 && N < 1) return fail(QSA_ERR_SHAPE, "seq_lens/block_table: no requests for %lld rows", (long long)R);
+  if (R > (int64_t)1 << 30) return fail(QSA_ERR_SHAPE, "q: too many rows");
+  if (W > ((int64_t)1 << 22)) return fail(QSA_ERR_SHAPE, "block_table: too wide");
+  const Span so = span_of(out);
+  const qsa_tensor* ins[6] = {q, kcache, bt, t2r, sl, qp};
+  const char* names[6] = {"q", "kcache", "block_table", "token_to_req", "seq_lens", "query_pos"};
+  for (int i = 0; i < 6; ++i) {
+    if (overlaps(so, span_of(ins[i]))) return fail(QSA_ERR_ALIAS, "out overlaps %s", names[i]);
+  }
+  v->rows = R;
+  v->pages = kcache->shape[0];
+  v->reqs = N;
+  v->width = W;
+  v->bt_stride = N > 1 ? bt->stride[0] : W;
+  return QSA_OK;
+}
+
+struct AttnView {
+  int64_t rows = 0, tokens = 0;
+};
+
+int validate_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_tensor* v,
+                  const qsa_tensor* idx, float scale, const qsa_tensor* out, bool idx_is_output,
+                  AttnView* view) {
+  const int64_t qshape[3] = {-1, QSA_ATT_HEADS, QSA_ATT_DIM};
+  QSA_TRY(check_tensor("q", q, QSA_DTYPE_F16, 3, qshape));
+  QSA_TRY(check_contiguous("q", q));
+  QSA_TRY(check_aligned("q", q, 16));
+  const int64_t R = q->shape[0];
+  const int64_t kshape[4] = {-1, QSA_KV_PAGE_TOKENS, 1, QSA_ATT_DIM};
+  QSA_TRY(check_tensor("k", k, QSA_DTYPE_F16, 4, kshape));
+  QSA_TRY(check_tensor("v", v, QSA_DTYPE_F16, 4, kshape));
+  static const int64_t packed[4] = {262144, 512, 256, 1};
+  for (int d = 0; d < 4; ++d) {
+    if (k->stride[d] != packed[d]) {
+      return fail(QSA_ERR_LAYOUT, "k: strides must be exactly [262144,512,256,1] (dim %d is %lld)",
+                  d, (long long)k->stride[d]);
+    }
+    if (v->stride[d] != packed[d]) {
+      return fail(QSA_ERR_LAYOUT, "v: strides must be exactly [262144,512,256,1] (dim %d is %lld)",
+                  d, (long long)v->stride[d]);
+    }
+  }
+  if (v->shape[0] != k->shape[0]) return fail(QSA_ERR_SHAPE, "v: page count differs from k");
+  if (k->shape[0] < 1) return fail(QSA_ERR_SHAPE, "k: needs at least one page");
+  if (static_cast<char*>(v->data) != static_cast<char*>(k->data) + 2 * QSA_ATT_DIM) {
+    return fail(QSA_ERR_LAYOUT, "v: must start 256 elements after k (packed K|V rows)");
+  }
+  QSA_TRY(check_aligned("k", k, 16));
+  if (k->shape[0] > ((int64_t)1 << 31) / QSA_KV_PAGE_TOKENS - 1) {
+    return fail(QSA_ERR_SHAPE, "k: too many tokens for int32 indices");
+  }
+  const int64_t ishape[2] = {R, QSA_OUT_WIDTH};
+  QSA_TRY(check_tensor("indices", idx, QSA_DTYPE_I32, 2, ishape));
+  QSA_TRY(check_contiguous("indices", idx));
+  QSA_TRY(check_tensor("out", out, QSA_DTYPE_F16, 3, qshape));
+  if (out->shape[0] != R) return fail(QSA_ERR_SHAPE, "out: rows differ from q");
+  QSA_TRY(check_contiguous("out", out));
+  if (!std::isfinite(scale) || !(scale > 0.f)) {
+    return fail(QSA_ERR_ARG, "softmax_scale must be finite and > 0");
+  }
+  if (R > (int64_t)1 << 30) return fail(QSA_ERR_SHAPE, "q: too many rows");
+  // the packed cache as one span: pages x 512 rows x 512 elements
+  qsa_tensor whole = *k;
+  whole.ndim = 2;
+  whole.shape[0] = k->shape[0] * QSA_KV_PAGE_TOKENS;
+  whole.shape[1] = 2 * QSA_ATT_DIM;
+  whole.stride[0] = 2 * QSA_ATT_DIM;
+  whole.stride[1] = 1;
+  const Span so = span_of(out);
+  if (overlaps(so, span_of(q))) return fail(QSA_ERR_ALIAS, "out overlaps q");
+  if (overlaps(so, span_of(&whole))) return fail(QSA_ERR_ALIAS, "out overlaps k/v");
+  if (overlaps(so, span_of(idx))) return fail(QSA_ERR_ALIAS, "out overlaps indices");
+  if (idx_is_output) {
+    const Span si = span_of(idx);
+    if (overlaps(si, span_of(q))) return fail(QSA_ERR_ALIAS, "indices overlap q_attn");
+    if (overlaps(si, span_of(&whole))) return fail(QSA_ERR_ALIAS, "indices overlap k/v");
+  }
+  view->rows = R;
+  view->tokens = k->shape[0] * QSA_KV_PAGE_TOKENS;
+  return QSA_OK;
+}
+
+int check_workspace(void* ws, size_t have, size_t need, Span guarded[], int nguarded) {
+  if (need == 0) return QSA_OK;
+  if (!ws) return fail(QSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(QSA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (have < need) return fail(QSA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  Span w;
+  w.lo = reinterpret_cast<uintptr_t>(ws);
+  w.hi = w.lo + need;
+  for (int i = 0; i < nguarded; ++i) {
+    if (overlaps(w, guarded[i])) return fail(QSA_ERR_ALIAS, "workspace overlaps a tensor argument");
+  }
+  return QSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace qsa {
+
+// Chunk size: the largest of 16/8/4/2/1 pages that still gives the launch
+// about 2048 workgroups (8 per compute unit on 256 CUs), so long rows are
+// split across the chip while short batches keep chunks small.
+SelectPlan plan_select(int64_t rows, int64_t table_width) {
+  SelectPlan p;
+  const int64_t w = table_width > 0 ? table_width : 1;
+  int pages = 16;
+  while (pages > 1 && rows * ((w + pages - 1) / pages) < 2048) pages >>= 1;
+  p.chunk_pages = pages;
+  p.chunks_per_row = (w + pages - 1) / pages;
+  p.cand_cap = std::min<int64_t>(kTopKBlocks, (int64_t)pages * kPageSlots);
+  if (rows == 0 || p.chunks_per_row == 1) {
+    p.bytes = 0;
+    return p;
+  }
+  size_t off = 0;
+  p.counters_off = off;
+  off = align256(off + (size_t)rows * sizeof(uint32_t));
+  const size_t cands = (size_t)rows * (size_t)p.chunks_per_row * (size_t)p.cand_cap;
+  p.keys_off = off;
+  off = align256(off + cands * sizeof(uint32_t));
+  p.blocks_off = off;
+  off = align256(off + cands * sizeof(uint32_t));
+  p.bytes = off;
+  return p;
+}
+
+// Split length: 128 index positions per workgroup (two 16-position tiles
+// per wave) for batches, shorter for small batches so that a single row
+// still spreads over enough workgroups.
+AttnPlan plan_attn(int64_t rows) {
+  AttnPlan p;
+  p.split_positions = rows >= 16 ? 128 : 64;
+  p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
+  if (rows == 0) return p;
+  size_t off = 0;
+  p.partial_off = off;
+  off = align256(off + (size_t)rows * p.splits * kAttHeads * kAttDim * sizeof(float));
+  p.stats_off = off;
+  off = align256(off + (size_t)rows * p.splits * kAttHeads * 2 * sizeof(float));
+  p.bytes = p.splits > 1 ? off : 0;
+  return p;
+}
+
+}  // namespace qsa
+
+extern "C" {
+
+QSA_API const char* qsa_status_string(int status) {
+  switch (status) {
+    case QSA_OK: return "QSA_OK";
+    case QSA_ERR_NULL: return "QSA_ERR_NULL";
+    case QSA_ERR_DTYPE: return "QSA_ERR_DTYPE";
+    case QSA_ERR_SHAPE: return "QSA_ERR_SHAPE";
+    case QSA_ERR_LAYOUT: return "QSA_ERR_LAYOUT";
+    case QSA_ERR_ALIAS: return "QSA_ERR_ALIAS";
+    case QSA_ERR_WORKSPACE: return "QSA_ERR_WORKSPACE";
+    case QSA_ERR_ARG: return "QSA_ERR_ARG";
+    case QSA_ERR_LAUNCH: return "QSA_ERR_LAUNCH";
+    default: return "QSA_ERR_UNKNOWN";
+  }
+}
+
+QSA_API const char* qsa_last_error(void) { return g_last_error; }
+
+QSA_API void qsa_constants(int32_t* token_topk, int32_t* compress_ratio, int32_t* out_width,
+                           int32_t* topk_blocks) {
+  if (token_topk) *token_topk = QSA_TOKEN_TOPK;
+  if (compress_ratio) *compress_ratio = QSA_COMPRESS_RATIO;
+  if (out_width) *out_width = QSA_OUT_WIDTH;
+  if (topk_blocks) *topk_blocks = QSA_TOPK_BLOCKS;
+}
+
+QSA_API size_t qsa_select_workspace_bytes(int64_t rows, int64_t table_width) {
+  if (rows <= 0) return 0;
+  return qsa::plan_select(rows, table_width).bytes;
+}
+
+QSA_API size_t qsa_sparse_attn_workspace_bytes(int64_t rows) {
+  if (rows <= 0) return 0;
+  return qsa::plan_attn(rows).bytes;
+}
+
+QSA_API size_t qsa_decode_step_workspace_bytes(int64_t rows, int64_t table_width) {
+  if (rows <= 0) return 0;
+  return align256(qsa_select_workspace_bytes(rows, table_width)) +
+         qsa_sparse_attn_workspace_bytes(rows);
+}
+
+QSA_API int qsa_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* block_table,
+                       const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                       const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
+                       size_t workspace_bytes, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  SelectView v;
+  QSA_TRY(validate_select(q, kcache, block_table, token_to_req, seq_lens, query_pos, out, &v));
+  if (v.rows == 0) return QSA_OK;
+  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
+  Span guarded[7] = {span_of(q), span_of(kcache), span_of(block_table), span_of(token_to_req),
+                     span_of(seq_lens), span_of(query_pos), span_of(out)};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 7));
+  qsa::SelectArgs a;
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.kcache = static_cast<const uint16_t*>(kcache->data);
+  a.block_table = static_cast<const int32_t*>(block_table->data);
+  a.token_to_req = static_cast<const int32_t*>(token_to_req->data);
+  a.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  a.query_pos = static_cast<const int64_t*>(query_pos->data);
+  a.out = static_cast<int32_t*>(out->data);
+  a.workspace = workspace;
+  a.rows = v.rows;
+  a.num_pages = v.pages;
+  a.num_reqs = v.reqs;
+  a.table_width = v.width;
+  a.bt_stride = v.bt_stride;
+  const int err = qsa::launch_select(a, plan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+QSA_API int qsa_sparse_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_tensor* v,
+                            const qsa_tensor* indices, float softmax_scale, const qsa_tensor* out,
+                            void* workspace, size_t workspace_bytes, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  AttnView view;
+  QSA_TRY(validate_attn(q, k, v, indices, softmax_scale, out, false, &view));
+  if (view.rows == 0) return QSA_OK;
+  const qsa::AttnPlan plan = qsa::plan_attn(view.rows);
+  qsa_tensor whole = *k;
+  whole.ndim = 1;
+  whole.shape[0] = view.tokens * 2 * QSA_ATT_DIM;
+  whole.stride[0] = 1;
+  Span guarded[4] = {span_of(q), span_of(&whole), span_of(indices), span_of(out)};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 4));
+  qsa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.kv = static_cast<const uint16_t*>(k->data);
+  a.indices = static_cast<const int32_t*>(indices->data);
+  a.out = static_cast<uint16_t*>(out->data);
+  a.workspace = workspace;
+  a.rows = view.rows;
+  a.num_tokens = view.tokens;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  const int err = qsa::launch_attn(a, plan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "attention launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+QSA_API int qsa_decode_step(const qsa_tensor* q_sel, const qsa_tensor* kcache,
+                            const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                            const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                            const qsa_tensor* q_attn, const qsa_tensor* k, const qsa_tensor* v,
+                            float softmax_scale, const qsa_tensor* indices, const qsa_tensor* out,
+                            void* workspace, size_t workspace_bytes, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  SelectView sv;
+  QSA_TRY(validate_select(q_sel, kcache, block_table, token_to_req, seq_lens, query_pos, indices, &sv));
+  AttnView av;
+  QSA_TRY(validate_attn(q_attn, k, v, indices, softmax_scale, out, true, &av));
+  if (av.rows != sv.rows) return fail(QSA_ERR_SHAPE, "q_attn rows differ from q_sel rows");
+  // the attention output must not overlap any selection input either
+  const qsa_tensor* sel_in[6] = {q_sel, kcache, block_table, token_to_req, seq_lens, query_pos};
+  for (int i = 0; i < 6; ++i) {
+    if (overlaps(span_of(out), span_of(sel_in[i]))) {
+      return fail(QSA_ERR_ALIAS, "out overlaps a selection input");
+    }
+  }
+  if (sv.rows == 0) return QSA_OK;
+  const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width);
+  const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
+  const size_t sel_bytes = align256(splan.bytes);
+  const size_t need = sel_bytes + aplan.bytes;
+  qsa_tensor whole = *k;
+  whole.ndim = 1;
+  whole.shape[0] = av.tokens * 2 * QSA_ATT_DIM;
+  whole.stride[0] = 1;
+  Span guarded[10] = {span_of(q_sel),     span_of(kcache),       span_of(block_table),
+                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
+                      span_of(q_attn),    span_of(&whole),       span_of(indices),
+                      span_of(out)};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, need, guarded, 10));
+
+  qsa::SelectArgs s;
+  s.q = static_cast<const uint16_t*>(q_sel->data);
+  s.kcache = static_cast<const uint16_t*>(kcache->data);
+  s.block_table = static_cast<const int32_t*>(block_table->data);
+  s.token_to_req = static_cast<const int32_t*>(token_to_req->data);
+  s.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  s.query_pos = static_cast<const int64_t*>(query_pos->data);
+  s.out = static_cast<int32_t*>(indices->data);
+  s.workspace = workspace;
+  s.rows = sv.rows;
+  s.num_pages = sv.pages;
+  s.num_reqs = sv.reqs;
+  s.table_width = sv.width;
+  s.bt_stride = sv.bt_stride;
+  int err = qsa::launch_select(s, splan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
+
+  qsa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q_attn->data);
+  a.kv = static_cast<const uint16_t*>(k->data);
+  a.indices = static_cast<const int32_t*>(indices->data);
+  a.out = static_cast<uint16_t*>(out->data);
+  a.workspace = aplan.bytes ? static_cast<char*>(workspace) + sel_bytes : nullptr;
+  a.rows = av.rows;
+  a.num_tokens = av.tokens;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  err = qsa::launch_attn(a, aplan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "attention launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+}  // extern "C"

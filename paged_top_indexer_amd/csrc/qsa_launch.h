@@ -1,0 +1,77 @@
+// qsa_launch.h -- internal interface between the host-side validation and
+// planning code (qsa_capi.cpp, plain C++) and the HIP kernels (*.hip).
+// Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace qsa {
+
+// Fixed contract: 512 blocks of 4 tokens plus a tail of at most 3 tokens.
+constexpr int kTopKBlocks = 512;
+constexpr int kRatio = 4;
+constexpr int kOutWidth = 2051;
+constexpr int kPageSlots = 128;
+constexpr int kSelHeads = 4;
+constexpr int kSelDim = 128;
+constexpr int kAttHeads = 3;
+constexpr int kAttDim = 256;
+constexpr int kKvRow = 512;
+constexpr int kKvPageTokens = 512;
+
+// Launch plan of the selection kernel.  A row's visible blocks are cut into
+// chunks of `chunk_pages` cache pages; one workgroup scores one chunk and
+// keeps its best min(512, chunk) blocks; the last workgroup of a row to
+// finish merges the row's candidates.
+struct SelectPlan {
+  int chunk_pages = 1;       // pages per chunk (1, 2, 4, 8 or 16)
+  int64_t chunks_per_row = 1;  // grid columns per row (ceil(W / chunk_pages))
+  int64_t cand_cap = 0;      // candidate slots per chunk: min(512, 128*chunk_pages)
+  size_t counters_off = 0;   // byte offsets inside the workspace
+  size_t keys_off = 0;
+  size_t blocks_off = 0;
+  size_t bytes = 0;          // total workspace bytes (0 = none needed)
+};
+
+SelectPlan plan_select(int64_t rows, int64_t table_width);
+
+// Launch plan of the attention kernel: `splits` workgroups per row, each
+// covering `split_positions` index positions (4 waves x tiles of 16).
+struct AttnPlan {
+  int split_positions = 128;
+  int splits = 1;
+  size_t partial_off = 0;  // [rows][splits][3][256] fp32 unnormalised outputs
+  size_t stats_off = 0;    // [rows][splits][3][2] fp32 (running max, sum)
+  size_t bytes = 0;
+};
+
+AttnPlan plan_attn(int64_t rows);
+
+struct SelectArgs {
+  const uint16_t* q;          // [R,4,128] fp16
+  const uint16_t* kcache;     // [P,128,1,128] fp16
+  const int32_t* block_table; // [N, >=W], row stride bt_stride
+  const int32_t* token_to_req;
+  const int32_t* seq_lens;
+  const int64_t* query_pos;
+  int32_t* out;               // [R,2051]
+  void* workspace;
+  int64_t rows, num_pages, num_reqs, table_width, bt_stride;
+};
+
+struct AttnArgs {
+  const uint16_t* q;       // [R,3,256] fp16
+  const uint16_t* kv;      // packed rows of 512 fp16 (K at +0, V at +256)
+  const int32_t* indices;  // [R,2051]
+  uint16_t* out;           // [R,3,256] fp16
+  void* workspace;
+  int64_t rows, num_tokens;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+// Enqueue the kernels; return the hipError_t of the launch (0 = success).
+int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream);
+int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
+
+}  // namespace qsa

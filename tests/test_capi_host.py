@@ -1,0 +1,236 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+reports the contract constants and rejects bad arguments before launching
+anything (descriptors point at fake device addresses; no call here reaches
+a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_top_indexer_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+OK, NULL, DTYPE, SHAPE, LAYOUT, ALIAS, WORKSPACE, ARG = 0, 1, 2, 3, 4, 5, 6, 7
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"QSA_API\s+[\w\s\*]+?\b(qsa_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol():
+    lib = B.library()
+    names = declared_symbols()
+    assert {"qsa_select", "qsa_sparse_attn", "qsa_decode_step"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_constants_and_status_strings():
+    assert B.constants() == (2048, 4, 2051, 512)
+    lib = B.library()
+    assert lib.qsa_status_string(0) == b"QSA_OK"
+    assert lib.qsa_status_string(4) == b"QSA_ERR_LAYOUT"
+
+
+def test_workspace_sizes():
+    assert B.select_workspace_bytes(0, 256) == 0
+    assert B.sparse_attn_workspace_bytes(0) == 0
+    # one chunk per row needs no workspace
+    assert B.select_workspace_bytes(1, 1) == 0
+    big = B.select_workspace_bytes(128, 256)
+    assert big >= 128 * 16 * 512 * 8
+    assert B.decode_step_workspace_bytes(128, 256) >= big + B.sparse_attn_workspace_bytes(128)
+    assert B.sparse_attn_workspace_bytes(128) > 0
+
+
+# ---------------------------------------------------------------------------
+# fake device memory: disjoint, 256-aligned address ranges
+
+class Fake:
+    next = 1 << 40  # shared by every instance: no two fake buffers overlap
+
+    def alloc(self, nbytes):
+        p = Fake.next
+        Fake.next += ((nbytes + 4095) // 4096 + 1) * 4096
+        return p
+
+
+def contig(shape):
+    st, acc = [], 1
+    for s in reversed(shape):
+        st.append(acc)
+        acc *= s
+    return tuple(reversed(st))
+
+
+def mk(fake, dtype, shape, esize, stride=None, ptr=None):
+    stride = stride or contig(shape)
+    n = 1
+    for s in shape:
+        n *= s
+    p = ptr if ptr is not None else fake.alloc(n * esize)
+    return B.descriptor(p, dtype, shape, stride)
+
+
+def select_args(R=4, P=8, N=4, W=3):
+    f = Fake()
+    a = dict(
+        q=mk(f, B.F16, (R, 4, 128), 2),
+        kcache=mk(f, B.F16, (P, 128, 1, 128), 2),
+        bt=mk(f, B.I32, (N, W), 4),
+        t2r=mk(f, B.I32, (R,), 4),
+        sl=mk(f, B.I32, (N,), 4),
+        qp=mk(f, B.I64, (R,), 8),
+        out=mk(f, B.I32, (R, 2051), 4),
+    )
+    ws_bytes = B.select_workspace_bytes(R, W)
+    return f, a, f.alloc(ws_bytes), ws_bytes
+
+
+def call_select(a, ws, ws_bytes):
+    lib = B.library()
+    order = ["q", "kcache", "bt", "t2r", "sl", "qp", "out"]
+    ptrs = [ctypes.byref(a[k]) if a[k] is not None else None for k in order]
+    return lib.qsa_select(*ptrs, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def attn_args(R=2, NP=4):
+    f = Fake()
+    base = f.alloc(NP * 512 * 512 * 2)
+    k = B.descriptor(base, B.F16, (NP, 512, 1, 256), (262144, 512, 256, 1))
+    v = B.descriptor(base + 512, B.F16, (NP, 512, 1, 256), (262144, 512, 256, 1))
+    a = dict(q=mk(f, B.F16, (R, 3, 256), 2), k=k, v=v,
+             idx=mk(f, B.I32, (R, 2051), 4), out=mk(f, B.F16, (R, 3, 256), 2))
+    ws_bytes = B.sparse_attn_workspace_bytes(R)
+    return f, a, f.alloc(ws_bytes), ws_bytes, base
+
+
+def call_attn(a, ws, ws_bytes, scale=0.0625):
+    lib = B.library()
+    return lib.qsa_sparse_attn(ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]),
+                               ctypes.byref(a["idx"]), ctypes.c_float(scale),
+                               ctypes.byref(a["out"]), ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_select_zero_rows_is_noop():
+    f, a, ws, wsb = select_args(R=0)
+    assert call_select(a, 0, 0) == OK
+
+
+SELECT_CASES = {
+    "q_dtype": (lambda f, a: a.__setitem__("q", mk(f, 0, (4, 4, 128), 4)), DTYPE),
+    "q_heads": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 3, 128), 2)), SHAPE),
+    "q_rank": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 512), 2)), SHAPE),
+    "q_strided": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 4, 128), 2, stride=(1024, 256, 1))), LAYOUT),
+    "q_misaligned": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 4, 128), 2, ptr=f.alloc(8192) + 2)), LAYOUT),
+    "kcache_bf16": (lambda f, a: a.__setitem__("kcache", mk(f, 0, (8, 128, 1, 128), 2)), DTYPE),
+    "kcache_slots": (lambda f, a: a.__setitem__("kcache", mk(f, B.F16, (8, 64, 1, 128), 2)), SHAPE),
+    "kcache_heads": (lambda f, a: a.__setitem__("kcache", mk(f, B.F16, (8, 128, 2, 128), 2)), SHAPE),
+    "kcache_empty": (lambda f, a: a.__setitem__("kcache", mk(f, B.F16, (0, 128, 1, 128), 2)), SHAPE),
+    "table_i64": (lambda f, a: a.__setitem__("bt", mk(f, B.I64, (4, 3), 8)), DTYPE),
+    "table_col_stride": (lambda f, a: a.__setitem__("bt", mk(f, B.I32, (4, 3), 4, stride=(6, 2))), LAYOUT),
+    "t2r_rows": (lambda f, a: a.__setitem__("t2r", mk(f, B.I32, (5,), 4)), SHAPE),
+    "seq_lens_i64": (lambda f, a: a.__setitem__("sl", mk(f, B.I64, (4,), 8)), DTYPE),
+    "seq_lens_count": (lambda f, a: a.__setitem__("sl", mk(f, B.I32, (3,), 4)), SHAPE),
+    "qpos_i32": (lambda f, a: a.__setitem__("qp", mk(f, B.I32, (4,), 4)), DTYPE),
+    "out_width": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2048), 4)), SHAPE),
+    "out_i64": (lambda f, a: a.__setitem__("out", mk(f, B.I64, (4, 2051), 8)), DTYPE),
+    "out_strided": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2051), 4, stride=(4096, 1))), LAYOUT),
+    "out_aliases_kcache": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2051), 4, ptr=a["kcache"].data)), ALIAS),
+    "out_aliases_q": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2051), 4, ptr=a["q"].data + 64)), ALIAS),
+    "null_table": (lambda f, a: a.__setitem__("bt", None), NULL),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SELECT_CASES))
+def test_select_fail_closed(case):
+    mutate, want = SELECT_CASES[case]
+    f, a, ws, wsb = select_args(R=4, W=40)
+    mutate(f, a)
+    rc = call_select(a, ws, wsb)
+    assert rc == want, (rc, B.library().qsa_last_error())
+    assert B.library().qsa_last_error() != b""
+
+
+def test_select_workspace_checks():
+    f, a, ws, wsb = select_args(R=4, W=40)
+    assert wsb > 0
+    assert call_select(a, 0, wsb) == WORKSPACE
+    assert call_select(a, ws, wsb - 1) == WORKSPACE
+    assert call_select(a, ws + 16, wsb) == WORKSPACE
+    assert call_select(a, a["out"].data, wsb) == ALIAS
+
+
+ATTN_CASES = {
+    "q_heads": (lambda f, a, base: a.__setitem__("q", mk(f, B.F16, (2, 4, 256), 2)), SHAPE),
+    "q_dtype": (lambda f, a, base: a.__setitem__("q", mk(f, B.I32, (2, 3, 256), 4)), DTYPE),
+    "k_strides": (lambda f, a, base: a.__setitem__("k", B.descriptor(base, B.F16, (4, 512, 1, 256), (131072, 256, 256, 1))), LAYOUT),
+    "v_strides": (lambda f, a, base: a.__setitem__("v", B.descriptor(base + 512, B.F16, (4, 512, 1, 256), (262144, 512, 512, 1))), LAYOUT),
+    "v_offset": (lambda f, a, base: a.__setitem__("v", B.descriptor(base + 256, B.F16, (4, 512, 1, 256), (262144, 512, 256, 1))), LAYOUT),
+    "v_pages": (lambda f, a, base: a.__setitem__("v", B.descriptor(base + 512, B.F16, (3, 512, 1, 256), (262144, 512, 256, 1))), SHAPE),
+    "k_page_rows": (lambda f, a, base: a.__setitem__("k", B.descriptor(base, B.F16, (4, 256, 1, 256), (262144, 512, 256, 1))), SHAPE),
+    "indices_i64": (lambda f, a, base: a.__setitem__("idx", mk(f, B.I64, (2, 2051), 8)), DTYPE),
+    "indices_width": (lambda f, a, base: a.__setitem__("idx", mk(f, B.I32, (2, 2048), 4)), SHAPE),
+    "out_bf16": (lambda f, a, base: a.__setitem__("out", mk(f, 0, (2, 3, 256), 2)), DTYPE),
+    "out_rows": (lambda f, a, base: a.__setitem__("out", mk(f, B.F16, (3, 3, 256), 2)), SHAPE),
+    "out_aliases_kv": (lambda f, a, base: a.__setitem__("out", mk(f, B.F16, (2, 3, 256), 2, ptr=base + 4096)), ALIAS),
+    "out_aliases_indices": (lambda f, a, base: a.__setitem__("out", mk(f, B.F16, (2, 3, 256), 2, ptr=a["idx"].data)), ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ATTN_CASES))
+def test_attn_fail_closed(case):
+    mutate, want = ATTN_CASES[case]
+    f, a, ws, wsb, base = attn_args()
+    mutate(f, a, base)
+    rc = call_attn(a, ws, wsb)
+    assert rc == want, (rc, B.library().qsa_last_error())
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan"), float("inf")])
+def test_attn_scale_checked(scale):
+    f, a, ws, wsb, base = attn_args()
+    assert call_attn(a, ws, wsb, scale) == ARG
+
+
+def test_decode_step_checks():
+    lib = B.library()
+    f, s, sws, swsb = select_args(R=2, W=40)
+    g, a, aws, awsb, base = attn_args(R=2)
+    wsb = B.decode_step_workspace_bytes(2, 40)
+    ws = f.alloc(wsb)
+
+    def call(q_attn=None, idx=None):
+        qa = q_attn or a["q"]
+        ix = idx or s["out"]
+        return lib.qsa_decode_step(
+            ctypes.byref(s["q"]), ctypes.byref(s["kcache"]), ctypes.byref(s["bt"]),
+            ctypes.byref(s["t2r"]), ctypes.byref(s["sl"]), ctypes.byref(s["qp"]),
+            ctypes.byref(qa), ctypes.byref(a["k"]), ctypes.byref(a["v"]), ctypes.c_float(0.0625),
+            ctypes.byref(ix), ctypes.byref(a["out"]), ctypes.c_void_p(ws), wsb, None)
+
+    assert call(q_attn=mk(g, B.F16, (3, 3, 256), 2)) == SHAPE
+    assert call(idx=mk(g, B.I32, (2, 2051), 4, ptr=base)) == ALIAS
+    assert call(idx=mk(g, B.I32, (2, 2051), 4, ptr=s["q"].data)) == ALIAS
+    # a too-small workspace is rejected before anything is launched
+    assert lib.qsa_decode_step(
+        ctypes.byref(s["q"]), ctypes.byref(s["kcache"]), ctypes.byref(s["bt"]),
+        ctypes.byref(s["t2r"]), ctypes.byref(s["sl"]), ctypes.byref(s["qp"]),
+        ctypes.byref(a["q"]), ctypes.byref(a["k"]), ctypes.byref(a["v"]), ctypes.c_float(0.0625),
+        ctypes.byref(s["out"]), ctypes.byref(a["out"]), ctypes.c_void_p(ws), wsb - 256, None) == WORKSPACE
+
+
+def test_torch_descriptor_dtype_refused():
+    """A float32 tensor gets dtype code 0 from the binding and the library
+    refuses it; the binding turns the status into RuntimeError."""
+    import torch
+    q = torch.zeros((1, 4, 128), dtype=torch.float32)
+    f, a, ws, wsb = select_args(R=1)
+    a["q"] = B.tensor_desc(q)
+    with pytest.raises(RuntimeError, match="QSA_ERR_DTYPE"):
+        B.check(call_select(a, ws, wsb))
