@@ -223,9 +223,9 @@ def main() -> int:
         base = cpu_baseline(w, scale)
         outs = base.pop("_outs")
         # the timed configuration's output on the rows the oracle finished
-        same = sum(np.array_equal(s[0], got_idx[i]) for i, s in enumerate(outs))
+        same = sum(np.array_equal(sel[0], got_idx[i]) for i, (sel, _) in enumerate(outs))
         errs = [float(np.max(np.abs(got_out[i].astype(np.float64) - a)))
-                for i, (s, a) in enumerate(outs) if np.array_equal(s[0], got_idx[i])]
+                for i, (sel, a) in enumerate(outs) if np.array_equal(sel[0], got_idx[i])]
         result["cpu_baseline"] = base
         result["parity"] = {"rows_checked": len(outs), "selection_identical": int(same),
                             "attention_max_abs_err": max(errs) if errs else None}

@@ -40,11 +40,10 @@
  *   read, an index outside [-1, NT) as a hole) but the result is then
  *   unspecified.
  * - Workspaces: device memory of at least the queried size, 256-byte
- *   aligned, ZERO-FILLED BEFORE ITS FIRST USE.  Every call that returns
- *   QSA_OK leaves the workspace's counters at zero again once the call has
- *   completed on the stream, so a workspace can be reused by consecutive
- *   calls on one stream.  Calls that run concurrently (different streams)
- *   must not share a workspace.
+ *   aligned, with any content (the library keeps no state in it between
+ *   calls: every byte it reads there was written earlier in the same call).
+ *   Calls that may run concurrently (different streams) must not share a
+ *   workspace; consecutive calls on one stream may.
  * - Thread safety: any host thread may call; qsa_last_error() is per thread.
  */
 #ifndef QSA_H_

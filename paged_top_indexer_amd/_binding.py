@@ -133,14 +133,14 @@ def kv_views(kv):
 _workspaces: dict = {}
 
 
-def workspace(nbytes: int, device, stream_handle: int):
-    """A zero-filled device buffer of at least nbytes, cached per
-    (device, stream).  The library leaves its counters at zero after every
-    call, so consecutive calls on one stream may share it."""
+def workspace(nbytes: int, device, stream_handle: int, kind: str):
+    """A device buffer of at least nbytes, cached per (device, stream, entry
+    point).  The library keeps no state in a workspace between calls, so
+    consecutive calls on one stream may share it."""
     torch = _torch()
     if nbytes == 0:
         return None
-    key = (str(device), int(stream_handle))
+    key = (str(device), int(stream_handle), kind)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -154,9 +154,9 @@ def _stream(stream, device):
     return s.cuda_stream
 
 
-def _ws_args(nbytes, device, stream_handle, ws):
+def _ws_args(nbytes, device, stream_handle, ws, kind):
     if ws is None:
-        ws = workspace(nbytes, device, stream_handle)
+        ws = workspace(nbytes, device, stream_handle, kind)
     if ws is None:
         return None, 0
     return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
@@ -172,7 +172,7 @@ def qsa_select(q, kcache, block_table, token_to_req, seq_lens, query_pos, out=No
         out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
     sh = _stream(stream, q.device)
     need = select_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
-    ws, ws_bytes = _ws_args(need, q.device, sh, workspace)
+    ws, ws_bytes = _ws_args(need, q.device, sh, workspace, "select")
     descs = [tensor_desc(t) for t in (q, kcache, block_table, token_to_req, seq_lens, query_pos, out)]
     check(lib.qsa_select(*[ctypes.byref(d) for d in descs], ws, ws_bytes, ctypes.c_void_p(sh)))
     return out
@@ -186,7 +186,7 @@ def qsa_sparse_attn(q, k, v, indices, softmax_scale: float, out=None, workspace=
     if out is None:
         out = torch.empty((R, 3, 256), dtype=torch.float16, device=q.device)
     sh = _stream(stream, q.device)
-    ws, ws_bytes = _ws_args(sparse_attn_workspace_bytes(R), q.device, sh, workspace)
+    ws, ws_bytes = _ws_args(sparse_attn_workspace_bytes(R), q.device, sh, workspace, "attn")
     descs = [tensor_desc(t) for t in (q, k, v, indices)]
     od = tensor_desc(out)
     check(lib.qsa_sparse_attn(*[ctypes.byref(d) for d in descs], ctypes.c_float(softmax_scale),
@@ -206,7 +206,7 @@ def qsa_decode_step(q_sel, kcache, block_table, token_to_req, seq_lens, query_po
         out = torch.empty((R, 3, 256), dtype=torch.float16, device=q_sel.device)
     sh = _stream(stream, q_sel.device)
     need = decode_step_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
-    ws, ws_bytes = _ws_args(need, q_sel.device, sh, workspace)
+    ws, ws_bytes = _ws_args(need, q_sel.device, sh, workspace, "decode")
     first = [tensor_desc(t) for t in (q_sel, kcache, block_table, token_to_req, seq_lens,
                                       query_pos, q_attn, k, v)]
     idd, od = tensor_desc(indices), tensor_desc(out)

@@ -248,14 +248,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace qsa {
 
-// Chunk size: the largest of 16/8/4/2/1 pages that still gives the launch
-// about 2048 workgroups (8 per compute unit on 256 CUs), so long rows are
-// split across the chip while short batches keep chunks small.
+// Chunk size: the largest of 32/16/8/4/2/1 pages that still gives the chunk
+// kernel about 1024 workgroups (4 per compute unit on 256 CUs, its
+// occupancy), so long rows are split across the chip while short batches
+// keep chunks small.
 SelectPlan plan_select(int64_t rows, int64_t table_width) {
   SelectPlan p;
   const int64_t w = table_width > 0 ? table_width : 1;
-  int pages = 16;
-  while (pages > 1 && rows * ((w + pages - 1) / pages) < 2048) pages >>= 1;
+  int pages = 32;
+  while (pages > 1 && rows * ((w + pages - 1) / pages) < 1024) pages >>= 1;
   p.chunk_pages = pages;
   p.chunks_per_row = (w + pages - 1) / pages;
   p.cand_cap = std::min<int64_t>(kTopKBlocks, (int64_t)pages * kPageSlots);
@@ -264,8 +265,6 @@ SelectPlan plan_select(int64_t rows, int64_t table_width) {
     return p;
   }
   size_t off = 0;
-  p.counters_off = off;
-  off = align256(off + (size_t)rows * sizeof(uint32_t));
   const size_t cands = (size_t)rows * (size_t)p.chunks_per_row * (size_t)p.cand_cap;
   p.keys_off = off;
   off = align256(off + cands * sizeof(uint32_t));

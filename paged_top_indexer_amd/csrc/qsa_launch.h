@@ -20,18 +20,18 @@ constexpr int kAttDim = 256;
 constexpr int kKvRow = 512;
 constexpr int kKvPageTokens = 512;
 
-// Launch plan of the selection kernel.  A row's visible blocks are cut into
-// chunks of `chunk_pages` cache pages; one workgroup scores one chunk and
-// keeps its best min(512, chunk) blocks; the last workgroup of a row to
-// finish merges the row's candidates.
+// Launch plan of the selection.  A row's visible blocks are cut into chunks
+// of `chunk_pages` cache pages; one workgroup of the chunk kernel scores one
+// chunk and keeps its best min(512, chunk) blocks (a row with a single
+// chunk is finished there).  The merge kernel then takes each multi-chunk
+// row's candidates to the final top-512.
 struct SelectPlan {
-  int chunk_pages = 1;       // pages per chunk (1, 2, 4, 8 or 16)
+  int chunk_pages = 1;         // pages per chunk (1, 2, 4, 8, 16 or 32)
   int64_t chunks_per_row = 1;  // grid columns per row (ceil(W / chunk_pages))
-  int64_t cand_cap = 0;      // candidate slots per chunk: min(512, 128*chunk_pages)
-  size_t counters_off = 0;   // byte offsets inside the workspace
-  size_t keys_off = 0;
+  int64_t cand_cap = 0;        // candidate slots per chunk: min(512, 128*chunk_pages)
+  size_t keys_off = 0;         // byte offsets inside the workspace
   size_t blocks_off = 0;
-  size_t bytes = 0;          // total workspace bytes (0 = none needed)
+  size_t bytes = 0;            // total workspace bytes (0 = none needed)
 };
 
 SelectPlan plan_select(int64_t rows, int64_t table_width);

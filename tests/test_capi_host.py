@@ -43,7 +43,8 @@ def test_workspace_sizes():
     # one chunk per row needs no workspace
     assert B.select_workspace_bytes(1, 1) == 0
     big = B.select_workspace_bytes(128, 256)
-    assert big >= 128 * 16 * 512 * 8
+    # 32-page chunks: 8 chunks per row, 512 candidates (key + block) each
+    assert big >= 128 * 8 * 512 * 8
     assert B.decode_step_workspace_bytes(128, 256) >= big + B.sparse_attn_workspace_bytes(128)
     assert B.sparse_attn_workspace_bytes(128) > 0
 
