@@ -32,7 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = "select+sparse-attn decode rows/sec and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-COUNTERS = os.path.join(ROOT, "profiles", "select_long_context_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "select_long_context_R128_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
                   for f in ("qsa_select.hip", "qsa_launch.h", "qsa_capi.cpp")]
 
@@ -114,6 +114,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the bench, run a plain device copy of MIB MiB three "
+                         "times (reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -123,6 +126,16 @@ def main() -> int:
     import torch
     import paged_top_indexer_amd as qsa
     from paged_top_indexer_amd import workloads as wl
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 2, dtype=torch.float16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return 0
 
     t0 = time.perf_counter()
     w = wl.long_context(args.seed)
@@ -210,7 +223,8 @@ def main() -> int:
                    "index_width": 2051},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "qsa_select_kernel",
+                     "traffic": traffic,
+                     "kernel": "qsa_select (qsa_select_chunk_kernel + qsa_select_merge_kernel)",
                      "bytes_per_launch": sel_bytes, "avg_launch_ms": round(sel_avg_s * 1e3, 4)},
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
                    "attention_bytes": att_bytes,
