@@ -213,30 +213,46 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
   }
 }
 
-// One workgroup per row: merge the row's split partials, normalise, round.
+// One workgroup per (row, head): wave 0 turns the splits' (max, sum) into
+// weights 2^(m_s - M) and the total sum; then thread e sums the weighted
+// partials of dim e (independent loads, one per split), normalises, rounds.
+constexpr int kMaxSplits = 64;
+
 __global__ __launch_bounds__(kThreads) void qsa_attn_combine_kernel(AttnParams p) {
-  const int64_t r = blockIdx.x;
-  const int e = threadIdx.x;
+  __shared__ float weight[kMaxSplits];
+  __shared__ float total;
+  const int64_t r = blockIdx.x / kAttHeads;
+  const int h = blockIdx.x % kAttHeads;
+  const int tid = threadIdx.x;
   if (r >= p.rows) return;
+  if (tid < 64) {
+    const int s = tid;
+    float m = -INFINITY, l = 0.f;
+    if (s < p.splits) {
+      const int64_t slot = (r * p.splits + s) * kAttHeads + h;
+      m = p.stats[slot * 2];
+      l = p.stats[slot * 2 + 1];
+    }
+    float M = m;
 #pragma unroll
-  for (int h = 0; h < kAttHeads; ++h) {
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) {
-      M = fmaxf(M, p.stats[((r * p.splits + s) * kAttHeads + h) * 2]);
-    }
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < p.splits; ++s) {
-        const int64_t slot = (r * p.splits + s) * kAttHeads + h;
-        const float f = exp2_fast(p.stats[slot * 2] - M);
-        L = fmaf(f, p.stats[slot * 2 + 1], L);
-        O = fmaf(f, p.partial[slot * kAttDim + e], O);
-      }
-    }
-    const float y = L > 0.f ? O / L : 0.f;
-    const _Float16 yh = (_Float16)y;
-    p.out[(r * kAttHeads + h) * kAttDim + e] = *reinterpret_cast<const uint16_t*>(&yh);
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float w = (M == -INFINITY || m == -INFINITY) ? 0.f : exp2_fast(m - M);
+    float L = w * l;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (s < kMaxSplits) weight[s] = w;
+    if (tid == 0) total = L;
   }
+  __syncthreads();
+  const int e = tid;
+  const float* part = p.partial + ((r * p.splits) * kAttHeads + h) * kAttDim + e;
+  float O = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < p.splits; ++s) O = fmaf(weight[s], part[(int64_t)s * kAttHeads * kAttDim], O);
+  const float L = total;
+  const float y = L > 0.f ? O / L : 0.f;
+  const _Float16 yh = (_Float16)y;
+  p.out[(r * kAttHeads + h) * kAttDim + e] = *reinterpret_cast<const uint16_t*>(&yh);
 }
 
 }  // namespace
@@ -261,7 +277,8 @@ int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
                      s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return (int)err;
-  hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)a.rows), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)(a.rows * kAttHeads)), dim3(kThreads),
+                     0, s, p);
   return (int)hipGetLastError();
 }
 

@@ -20,18 +20,19 @@
 //    bytes.  The 4 head dots of key n land in lane n, so ReLU + head sum is
 //    lane-local.  Scores go to LDS as order-preserving uint32 keys (a score
 //    is >= 0, so its IEEE bit pattern with the sign bit cleared orders like
-//    the value and maps -0 onto +0).
+//    the value and maps -0 onto +0), and the first radix histogram is
+//    counted as the scores arrive, under the memory latency.
 //  * Chunk top-k: an MSB-first radix select (digits of 11, 11 and 9 bits)
-//    over the LDS keys finds the k-th largest key T; keys > T are in, keys
-//    equal to T are taken in block order until k are in.  Survivors keep
-//    block order.  A row that fits in one chunk is sorted, expanded and
+//    finds the k-th largest key; it stops early once the bin holding the
+//    k-th key is taken whole.  Survivors are compacted in block order with
+//    wave ballots.  A row that fits in one chunk is sorted, expanded and
 //    written right there (one launch does all the work).
-//  * Merge kernel, one 1024-thread workgroup per multi-chunk row: the
-//    chunks' candidate lists, concatenated in chunk order, are in block
-//    order; they are staged through LDS in batches (the running best 512
-//    first, so list order stays block order) and reduced with the same radix
-//    select.  The winners are bitonic-sorted on the 64-bit key
-//    (score << 32 | ~block), expanded and written.
+//  * Merge kernel, one workgroup per multi-chunk row: the chunks' candidate
+//    lists, concatenated in chunk order, are in block order; they are staged
+//    through LDS in batches (the running best 512 first, so list order stays
+//    block order) and reduced with the same radix select.  The winners are
+//    bitonic-sorted on the 64-bit key (score << 32 | ~block), expanded and
+//    written.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -42,7 +43,7 @@ namespace qsa {
 namespace {
 
 constexpr int kChunkThreads = 256;
-constexpr int kMergeThreads = 1024;
+constexpr int kMergeThreads = 256;
 constexpr int kMaxChunkPages = 32;
 constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
 constexpr int kUnroll = 4;        // tiles in flight per wave
@@ -51,6 +52,7 @@ constexpr int kMergeList = 8192 + kTopKBlocks;  // LDS list of the merge
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct SelectParams {
   const uint16_t* q;
@@ -68,11 +70,13 @@ struct SelectParams {
   int cand_cap;
 };
 
-// Scratch shared by the block-wide helpers.
+// Small scratch of the block-wide helpers (at most 4 waves per workgroup).
+// The radix histograms are passed separately so that each kernel can place
+// them next to data that is dead by then.
 struct Scratch {
-  uint32_t hist[kBins];
-  uint32_t wave_sum[16];
-  uint32_t pick[2];
+  uint32_t wave_gt[4];
+  uint32_t wave_eq[4];
+  uint32_t pick[3];  // digit, rank inside the digit, keys in the digit
 };
 
 struct Row {
@@ -104,101 +108,157 @@ __device__ Row row_setup(const SelectParams& p, int64_t r) {
   return row;
 }
 
-template <int NT>
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, Scratch& s) {
-  constexpr int kWaves = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o, 64);
-    if (lane >= o) v += y;
+__device__ __forceinline__ uint32_t digit0(uint32_t key) { return (key >> 20) & (kBins - 1); }
+
+// Count the keys that match `prefix` under `mask` into h by the digit
+// (key >> SHIFT) & (NB - 1).
+template <int NT, int SHIFT, int NB, typename KeyAt>
+__device__ void radix_count(KeyAt key_at, int n, uint32_t mask, uint32_t prefix, uint32_t* h) {
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint32_t x = key_at(i);
+    if ((x & mask) == prefix) atomicAdd(&h[(x >> SHIFT) & (NB - 1)], 1u);
   }
-  if (lane == 63) s.wave_sum[wave] = v;
-  __syncthreads();
-  uint32_t add = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) add += (w < wave) ? s.wave_sum[w] : 0u;
-  __syncthreads();
-  return v + add;
 }
 
-// Radix select: the k-th largest (1 <= k <= n) of the uint32 keys
-// key_at(i), i < n, whose bit 31 is clear.  Returns that key T and how many
-// keys equal to T belong to the top-k.
-template <int NT, typename KeyAt>
-__device__ void radix_threshold(KeyAt key_at, int n, int k, Scratch& s, uint32_t& T,
-                                int& need_eq) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  uint32_t krem = (uint32_t)k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 9 : 0);
-    const int nb = pass == 2 ? 512 : 2048;
-    for (int i = tid; i < nb; i += NT) s.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t x = key_at(i);
-      if ((x & mask) == prefix) atomicAdd(&s.hist[(x >> shift) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    // thread t owns digits nb-1-t*per .. (descending); the scan counts keys
-    // at or above each thread's lowest digit
-    const int per = (nb + NT - 1) / NT;
-    uint32_t local = 0;
-    for (int j = 0; j < per; ++j) {
-      const int d = nb - 1 - (tid * per + j);
-      if (d >= 0) local += s.hist[d];
-    }
-    const uint32_t incl = block_incl_scan<NT>(local, s);
-    uint32_t excl = incl - local;
-    if (excl < krem && krem <= incl) {
-      for (int j = 0; j < per; ++j) {
-        const int d = nb - 1 - (tid * per + j);
-        if (d < 0) break;
-        const uint32_t c = s.hist[d];
-        if (excl + c >= krem) {
-          s.pick[0] = (uint32_t)d;
-          s.pick[1] = krem - excl;
-          break;
-        }
-        excl += c;
-      }
-    }
-    __syncthreads();
-    prefix |= s.pick[0] << shift;
-    mask |= (uint32_t)(nb - 1) << shift;
-    krem = s.pick[1];
-    __syncthreads();
+// Wave 0 only: find the digit of histogram h (NB bins) that holds the
+// krem-th largest counted key.  Lane l reads its NB/64 bins (the digits
+// [NB - (l+1)NB/64, NB - l NB/64)) as 16-byte vectors, the wave scans the
+// lane sums from the top digit down, and the owning lane walks its bins in
+// registers.  Writes (digit, rank inside the digit, keys in the digit).
+template <int NB>
+__device__ void radix_pick(const uint32_t* h, uint32_t krem, Scratch& s) {
+  constexpr int kPer = NB / 64;
+  const int lane = threadIdx.x & 63;
+  const int lo = NB - kPer * (lane + 1);
+  uint32_t c[kPer];
+  const uint4* hv = reinterpret_cast<const uint4*>(h + lo);
+#pragma unroll
+  for (int j = 0; j < kPer / 4; ++j) {
+    const uint4 x = hv[j];
+    c[4 * j] = x.x;
+    c[4 * j + 1] = x.y;
+    c[4 * j + 2] = x.z;
+    c[4 * j + 3] = x.w;
   }
-  T = prefix;
-  need_eq = (int)krem;
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) local += c[j];
+  uint32_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  const uint32_t excl = incl - local;
+  if (excl < krem && krem <= incl) {
+    uint32_t acc = excl;
+    bool done = false;
+#pragma unroll
+    for (int j = kPer - 1; j >= 0; --j) {
+      if (!done && acc + c[j] >= krem) {
+        s.pick[0] = (uint32_t)(lo + j);
+        s.pick[1] = krem - acc;
+        s.pick[2] = c[j];
+        done = true;
+      }
+      acc += c[j];
+    }
+  }
+}
+
+// Radix select of the k-th largest (1 <= k <= n) of the keys key_at(i),
+// i < n (bit 31 clear).  On entry hist0 holds the histogram of digit0 over
+// all n keys and every thread has passed a barrier since; hist1 is a second
+// histogram; both have kBins entries, are 16-byte aligned and may be
+// overwritten.  Returns (T, need_eq) such that the top-k are the keys > T
+// plus the first need_eq keys == T in list order.
+template <int NT, typename KeyAt>
+__device__ void radix_select(KeyAt key_at, int n, int k, Scratch& s, uint32_t* hist0,
+                             uint32_t* hist1, uint32_t& T, int& need_eq) {
+  static_assert(NT <= 256, "Scratch holds 4 waves");
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins; i += NT) hist1[i] = 0;
+  if (tid < 64) radix_pick<kBins>(hist0, (uint32_t)k, s);
+  __syncthreads();
+  uint32_t prefix = s.pick[0] << 20;
+  uint32_t mask = (uint32_t)(kBins - 1) << 20;
+  uint32_t krem = s.pick[1];
+  bool whole = s.pick[2] == krem;  // the boundary bin is taken entirely
+  if (!whole) {
+    radix_count<NT, 9, kBins>(key_at, n, mask, prefix, hist1);
+    for (int i = tid; i < 512; i += NT) hist0[i] = 0;
+    __syncthreads();
+    if (tid < 64) radix_pick<kBins>(hist1, krem, s);
+    __syncthreads();
+    prefix |= s.pick[0] << 9;
+    mask |= (uint32_t)(kBins - 1) << 9;
+    krem = s.pick[1];
+    whole = s.pick[2] == krem;
+    if (!whole) {
+      radix_count<NT, 0, 512>(key_at, n, mask, prefix, hist0);
+      __syncthreads();
+      if (tid < 64) radix_pick<512>(hist0, krem, s);
+      __syncthreads();
+      T = prefix | s.pick[0];
+      need_eq = (int)s.pick[1];
+      return;
+    }
+  }
+  // every key >= prefix (lower bits free) is in, nothing else
+  if (prefix == 0) {
+    T = 0;
+    need_eq = n;
+  } else {
+    T = prefix - 1;
+    need_eq = 0;
+  }
 }
 
 // Emit the top-k of key_at(0..n) in list order: keys > T and the first
-// need_eq keys == T.  emit(slot, i, key) is called with slots 0..k-1.
+// need_eq keys == T.  emit(slot, i, key) is called with slots 0..k-1.  Each
+// wave owns a contiguous segment; ranks come from ballots, the waves'
+// offsets from one barrier.
 template <int NT, typename KeyAt, typename Emit>
 __device__ void compact_topk(KeyAt key_at, int n, uint32_t T, int need_eq, Emit emit,
                              Scratch& s) {
-  const int tid = threadIdx.x;
-  const int per = (n + NT - 1) / NT;
-  const int beg = min(n, tid * per), end = min(n, beg + per);
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int seg = ((n + NT - 1) / NT) * 64;
+  const int beg = min(n, wave * seg), end = min(n, beg + seg);
   uint32_t gt = 0, eq = 0;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t x = key_at(i);
-    gt += x > T;
-    eq += x == T;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    const bool ok = i < end;
+    const uint32_t x = ok ? key_at(i) : 0u;
+    gt += __popcll(__ballot(ok && x > T));
+    eq += __popcll(__ballot(ok && x == T));
   }
-  const uint32_t eq_before = block_incl_scan<NT>(eq, s) - eq;
-  const int eq_take = max(0, min((int)eq, need_eq - (int)eq_before));
-  const uint32_t mine = gt + (uint32_t)eq_take;
-  uint32_t slot = block_incl_scan<NT>(mine, s) - mine;
-  int eq_seen = 0;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t x = key_at(i);
-    bool take = x > T;
-    if (x == T) take = eq_seen++ < eq_take;
-    if (take) emit(slot++, i, x);
+  if (lane == 0) {
+    s.wave_gt[wave] = gt;
+    s.wave_eq[wave] = eq;
+  }
+  __syncthreads();
+  uint32_t gt_b = 0, eq_b = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    gt_b += w < wave ? s.wave_gt[w] : 0u;
+    eq_b += w < wave ? s.wave_eq[w] : 0u;
+  }
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    const bool ok = i < end;
+    const uint32_t x = ok ? key_at(i) : 0u;
+    const uint64_t mg = __ballot(ok && x > T);
+    const uint64_t me = __ballot(ok && x == T);
+    const uint32_t eq_here = eq_b + (uint32_t)__popcll(me & below);
+    const bool take = ok && (x > T || (x == T && eq_here < (uint32_t)need_eq));
+    if (take) {
+      const uint32_t slot = gt_b + (uint32_t)__popcll(mg & below) + min(eq_here, (uint32_t)need_eq);
+      emit(slot, i, x);
+    }
+    gt_b += (uint32_t)__popcll(mg);
+    eq_b += (uint32_t)__popcll(me);
   }
 }
 
@@ -221,8 +281,8 @@ __device__ void finalize_row(uint64_t* sorted, int k, int64_t visible, int tail,
   for (int size = 2; size <= kTopKBlocks; size <<= 1) {
 #pragma unroll 1
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (tid < kTopKBlocks / 2) {
-        const int i = 2 * tid - (tid & (stride - 1));
+      for (int t = tid; t < kTopKBlocks / 2; t += NT) {
+        const int i = 2 * t - (t & (stride - 1));
         const int j = i + stride;
         const bool desc = (i & size) == 0;
         const uint64_t a = sorted[i], b = sorted[j];
@@ -247,10 +307,24 @@ __device__ void finalize_row(uint64_t* sorted, int k, int64_t visible, int tail,
   }
 }
 
+constexpr int kChunkWaves = kChunkThreads / 64;
+
+// 40 KiB: four workgroups per CU.
 struct ChunkSmem {
   uint32_t keys[kMaxChunkBlocks];
-  uint64_t sorted[kTopKBlocks];
-  Scratch s;
+  alignas(16) uint32_t hist0[kBins];  // counted while scoring
+  union {
+    // scoring: one 16-key tile per wave, 16-byte chunk j of key n stored at
+    // [n][j ^ n] so that both the coalesced write and the MFMA-layout read
+    // touch 16 distinct bank groups
+    u32x4 stage[kChunkWaves][16][16];
+    // selection (after scoring)
+    struct {
+      alignas(16) uint32_t hist1[kBins];
+      uint64_t sorted[kTopKBlocks];
+      Scratch s;
+    } sel;
+  } u;
 };
 
 __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectParams p) {
@@ -265,6 +339,11 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
   if (chunk >= row.nchunks) return;
   const int64_t chunk_base = chunk * p.chunk_blocks;
   const int nblk = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
+  const bool select = nblk > kTopKBlocks;
+  if (select) {
+    for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
+    __syncthreads();
+  }
 
   // ---- scoring (MFMA) ----------------------------------------------------
   const int n = lane & 15;  // key column of B / head row of A
@@ -279,41 +358,60 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
   }
   const int32_t* bt_row = p.block_table + row.req * p.bt_stride;
   const int ntiles = (nblk + 15) >> 4;
-  constexpr int kWaves = kChunkThreads / 64;
+  u32x4(*stage)[16] = sm.u.stage[wave];
+  const int s16 = lane & 15;  // 16-byte chunk of a key this lane loads
 #pragma unroll 1
-  for (int t0 = wave; t0 < ntiles; t0 += kWaves * kUnroll) {
-    half8 kb[kUnroll][4];
-    bool live[kUnroll];
+  for (int t0 = wave; t0 < ntiles; t0 += kChunkWaves * kUnroll) {
+    // Coalesced nontemporal loads: instruction c reads keys 4c..4c+3 of the
+    // tile (1 KiB contiguous), lane l taking chunk l % 16 of key 4c + l / 16.
+    // Keys are read exactly once; nontemporal loads stream page-permuted
+    // reads at the linear-read rate.
+    u32x4 raw[kUnroll][4];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kWaves;
-      live[u] = 16 * t + n < nblk;
-      bool load = false;
-      const half8* kp = nullptr;
+      const int t = t0 + u * kChunkWaves;
+      bool page_ok = false;
+      const u32x4* kp = nullptr;
       if (t < ntiles) {
         const int64_t b0 = chunk_base + 16 * t;  // 16-aligned: one page per tile
         const int64_t page = bt_row[b0 >> 7];
-        load = live[u] && page >= 0 && page < p.num_pages;
-        const int64_t slot = (b0 & (kPageSlots - 1)) + n;
-        kp = reinterpret_cast<const half8*>(p.kcache + (page * kPageSlots + slot) * kSelDim) + g;
+        page_ok = page >= 0 && page < p.num_pages;
+        kp = reinterpret_cast<const u32x4*>(p.kcache + (page * kPageSlots + (b0 & (kPageSlots - 1))) *
+                                                           kSelDim) + lane;
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        kb[u][c] = load ? kp[4 * c] : half8{0, 0, 0, 0, 0, 0, 0, 0};
+        const bool ok = page_ok && 16 * t + 4 * c + g < nblk;
+        raw[u][c] = ok ? __builtin_nontemporal_load(kp + 64 * c) : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      const int t = t0 + u * kChunkWaves;
+      if (t >= ntiles) break;
+      // transpose through the wave's LDS tile
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int key = 4 * c + g;
+        stage[key][s16 ^ key] = raw[u][c];
+      }
+      __builtin_amdgcn_wave_barrier();
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb[u][c], acc, 0, 0, 0);
+        // B operand: lane (n + 16g) holds dims [32c + 8g, +8) of key n
+        const half8 kb = __builtin_bit_cast(half8, stage[n][(4 * c + g) ^ n]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb, acc, 0, 0, 0);
       }
+      __builtin_amdgcn_wave_barrier();
       // lanes 0..15 hold heads 0..3 of key n
       const float sc = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) +
                        fmaxf(acc[3], 0.f);
-      const int t = t0 + u * kWaves;
-      if (g == 0 && live[u]) sm.keys[16 * t + n] = __float_as_uint(sc) & 0x7FFFFFFFu;
+      if (g == 0 && 16 * t + n < nblk) {
+        const uint32_t key = __float_as_uint(sc) & 0x7FFFFFFFu;
+        sm.keys[16 * t + n] = key;
+        if (select) atomicAdd(&sm.hist0[digit0(key)], 1u);
+      }
     }
   }
   __syncthreads();
@@ -323,14 +421,18 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
   uint32_t T = 0;
   int need_eq = nblk;  // T = 0 and every key >= 0: all are taken
   auto lds_key = [&](int i) { return sm.keys[i]; };
-  if (nblk > kTopKBlocks) radix_threshold<kChunkThreads>(lds_key, nblk, k_local, sm.s, T, need_eq);
+  Scratch& s = sm.u.sel.s;
+  if (select) {
+    radix_select<kChunkThreads>(lds_key, nblk, k_local, s, sm.hist0, sm.u.sel.hist1, T, need_eq);
+  }
 
   if (row.nchunks == 1) {
+    uint64_t* sorted = sm.u.sel.sorted;
     compact_topk<kChunkThreads>(
         lds_key, nblk, T, need_eq,
-        [&](uint32_t slot, int i, uint32_t x) { sm.sorted[slot] = pack(x, (uint32_t)(chunk_base + i)); },
-        sm.s);
-    finalize_row<kChunkThreads>(sm.sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth);
+        [&](uint32_t slot, int i, uint32_t x) { sorted[slot] = pack(x, (uint32_t)(chunk_base + i)); },
+        s);
+    finalize_row<kChunkThreads>(sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth);
     return;
   }
   const int64_t cbase = (r * p.chunks_per_row + chunk) * p.cand_cap;
@@ -342,7 +444,7 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
         ckeys[slot] = x;
         cblocks[slot] = (uint32_t)(chunk_base + i);
       },
-      sm.s);
+      s);
 }
 
 struct MergeSmem {
@@ -351,6 +453,8 @@ struct MergeSmem {
   uint32_t best_keys[kTopKBlocks];
   uint32_t best_blocks[kTopKBlocks];
   uint64_t sorted[kTopKBlocks];
+  alignas(16) uint32_t hist0[kBins];
+  alignas(16) uint32_t hist1[kBins];
   Scratch s;
 };
 
@@ -375,14 +479,53 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
 #pragma unroll 1
   for (int base = 0; base < m; base += kBatch) {
     const int nb = min(kBatch, m - base);
-    // list = [running best (earlier blocks)] + [next batch]
+    for (int i = tid; i < kBins; i += kMergeThreads) sm.hist0[i] = 0;
+    __syncthreads();
+    // list = [running best (earlier blocks)] + [next batch]; the first radix
+    // histogram is counted on the way into LDS
     for (int i = tid; i < best_n; i += kMergeThreads) {
-      sm.keys[i] = sm.best_keys[i];
+      const uint32_t x = sm.best_keys[i];
+      sm.keys[i] = x;
       sm.blocks[i] = sm.best_blocks[i];
+      atomicAdd(&sm.hist0[digit0(x)], 1u);
     }
-    for (int i = tid; i < nb; i += kMergeThreads) {
-      sm.keys[best_n + i] = ckeys[base + i];
+    // 16-byte loads, kLoadUnroll of them in flight per thread (the batch
+    // start is a multiple of 4 candidates and the workspace is 256-aligned)
+    constexpr int kLoadUnroll = 4;
+    const int nb4 = nb >> 2;
+    const uint4* k4 = reinterpret_cast<const uint4*>(ckeys + base);
+    const uint4* b4 = reinterpret_cast<const uint4*>(cblocks + base);
+    for (int j0 = tid; j0 < nb4; j0 += kMergeThreads * kLoadUnroll) {
+      uint4 kv[kLoadUnroll], bv[kLoadUnroll];
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const int j = j0 + u * kMergeThreads;
+        if (j < nb4) {
+          kv[u] = k4[j];
+          bv[u] = b4[j];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kLoadUnroll; ++u) {
+        const int j = j0 + u * kMergeThreads;
+        if (j < nb4) {
+          const int at = best_n + 4 * j;
+          const uint32_t xs[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+          const uint32_t bs[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sm.keys[at + e] = xs[e];
+            sm.blocks[at + e] = bs[e];
+            atomicAdd(&sm.hist0[digit0(xs[e])], 1u);
+          }
+        }
+      }
+    }
+    for (int i = 4 * nb4 + tid; i < nb; i += kMergeThreads) {
+      const uint32_t x = ckeys[base + i];
+      sm.keys[best_n + i] = x;
       sm.blocks[best_n + i] = cblocks[base + i];
+      atomicAdd(&sm.hist0[digit0(x)], 1u);
     }
     __syncthreads();
     const int n_list = best_n + nb;
@@ -390,7 +533,9 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
     uint32_t T = 0;
     int need_eq = n_list;
     auto lds_key = [&](int i) { return sm.keys[i]; };
-    if (n_list > kk) radix_threshold<kMergeThreads>(lds_key, n_list, kk, sm.s, T, need_eq);
+    if (n_list > kk) {
+      radix_select<kMergeThreads>(lds_key, n_list, kk, sm.s, sm.hist0, sm.hist1, T, need_eq);
+    }
     compact_topk<kMergeThreads>(
         lds_key, n_list, T, need_eq,
         [&](uint32_t slot, int i, uint32_t x) {
