@@ -24,14 +24,17 @@
 //    counted as the scores arrive, under the memory latency.
 //  * Chunk top-k: an MSB-first radix select (digits of 11, 11 and 9 bits)
 //    finds the k-th largest key; it stops early once the bin holding the
-//    k-th key is taken whole.  Survivors are compacted in block order with
-//    wave ballots.  A row that fits in one chunk is sorted, expanded and
-//    written right there (one launch does all the work).
+//    k-th key is taken whole.  When keys equal to that threshold are only
+//    partly in, a second radix select over the complemented block index of
+//    those keys finds the last block that is in, so the tie rule (smaller
+//    block first) is decided explicitly and survivors can be compacted in
+//    any order (one pass, wave ballots, one LDS atomic per batch).  A row
+//    that fits in one chunk is sorted, expanded and written right there
+//    (one launch does all the work).
 //  * Merge kernel, one workgroup per multi-chunk row: the chunks' candidate
-//    lists, concatenated in chunk order, are in block order; they are staged
-//    through LDS in batches (the running best 512 first, so list order stays
-//    block order) and reduced with the same radix select.  The winners are
-//    bitonic-sorted on the 64-bit key (score << 32 | ~block), expanded and
+//    lists are staged through LDS in batches (behind the running best 512)
+//    and reduced with the same select.  The winners are bitonic-sorted in
+//    registers on the 64-bit key (score << 32 | ~block), expanded and
 //    written.
 #include <hip/hip_runtime.h>
 
@@ -74,9 +77,8 @@ struct SelectParams {
 // The radix histograms are passed separately so that each kernel can place
 // them next to data that is dead by then.
 struct Scratch {
-  uint32_t wave_gt[4];
-  uint32_t wave_eq[4];
   uint32_t pick[3];  // digit, rank inside the digit, keys in the digit
+  uint32_t count;    // slots handed out by compact_topk
 };
 
 struct Row {
@@ -114,10 +116,31 @@ __device__ __forceinline__ uint32_t digit0(uint32_t key) { return (key >> 20) & 
 // (key >> SHIFT) & (NB - 1).
 template <int NT, int SHIFT, int NB, typename KeyAt>
 __device__ void radix_count(KeyAt key_at, int n, uint32_t mask, uint32_t prefix, uint32_t* h) {
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t x = key_at(i);
-    if ((x & mask) == prefix) atomicAdd(&h[(x >> SHIFT) & (NB - 1)], 1u);
+  constexpr int U = 8;  // keys read before any is counted
+  for (int i0 = threadIdx.x; i0 < n; i0 += NT * U) {
+    uint32_t x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = i0 + u * NT < n ? key_at(i0 + u * NT) : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * NT < n && (x[u] & mask) == prefix) {
+        atomicAdd(&h[(x[u] >> SHIFT) & (NB - 1)], 1u);
+      }
+    }
   }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row_shr 1, 2,
+// 4, 8 scan each row of 16 lanes, row_bcast 15 and 31 carry the row totals
+// into the rows above.  All lanes must be active.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false); // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false); // row_bcast:31
+  return v;
 }
 
 // Wave 0 only: find the digit of histogram h (NB bins) that holds the
@@ -143,12 +166,7 @@ __device__ void radix_pick(const uint32_t* h, uint32_t krem, Scratch& s) {
   uint32_t local = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) local += c[j];
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(local);
   const uint32_t excl = incl - local;
   if (excl < krem && krem <= incl) {
     uint32_t acc = excl;
@@ -170,11 +188,12 @@ __device__ void radix_pick(const uint32_t* h, uint32_t krem, Scratch& s) {
 // i < n (bit 31 clear).  On entry hist0 holds the histogram of digit0 over
 // all n keys and every thread has passed a barrier since; hist1 is a second
 // histogram; both have kBins entries, are 16-byte aligned and may be
-// overwritten.  Returns (T, need_eq) such that the top-k are the keys > T
-// plus the first need_eq keys == T in list order.
+// overwritten.  Returns T and need_eq such that the top-k are the keys > T
+// plus need_eq of the keys == T, and eq_total = how many keys equal T when
+// 0 < need_eq (need_eq == eq_total: all of them).
 template <int NT, typename KeyAt>
 __device__ void radix_select(KeyAt key_at, int n, int k, Scratch& s, uint32_t* hist0,
-                             uint32_t* hist1, uint32_t& T, int& need_eq) {
+                             uint32_t* hist1, uint32_t& T, int& need_eq, int& eq_total) {
   static_assert(NT <= 256, "Scratch holds 4 waves");
   const int tid = threadIdx.x;
   for (int i = tid; i < kBins; i += NT) hist1[i] = 0;
@@ -201,65 +220,96 @@ __device__ void radix_select(KeyAt key_at, int n, int k, Scratch& s, uint32_t* h
       __syncthreads();
       T = prefix | s.pick[0];
       need_eq = (int)s.pick[1];
+      eq_total = (int)s.pick[2];
       return;
     }
   }
   // every key >= prefix (lower bits free) is in, nothing else
   if (prefix == 0) {
     T = 0;
-    need_eq = n;
+    need_eq = eq_total = n;  // all keys
   } else {
     T = prefix - 1;
-    need_eq = 0;
+    need_eq = eq_total = 0;
   }
 }
 
-// Emit the top-k of key_at(0..n) in list order: keys > T and the first
-// need_eq keys == T.  emit(slot, i, key) is called with slots 0..k-1.  Each
-// wave owns a contiguous segment; ranks come from ballots, the waves'
-// offsets from one barrier.
-template <int NT, typename KeyAt, typename Emit>
-__device__ void compact_topk(KeyAt key_at, int n, uint32_t T, int need_eq, Emit emit,
-                             Scratch& s) {
-  constexpr int kWaves = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int seg = ((n + NT - 1) / NT) * 64;
-  const int beg = min(n, wave * seg), end = min(n, beg + seg);
-  uint32_t gt = 0, eq = 0;
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    const bool ok = i < end;
-    const uint32_t x = ok ? key_at(i) : 0u;
-    gt += __popcll(__ballot(ok && x > T));
-    eq += __popcll(__ballot(ok && x == T));
+// Threshold of the top-k (1 <= k <= n) under the total order (key
+// descending, block ascending): the top-k are the entries with key > T and
+// the entries with key == T and block < bcut.  Preconditions as for
+// radix_select.  When the keys equal to T are only partly in, a second
+// radix select over 0x7FFFFFFF - block of those entries (block ids are
+// distinct) finds the last block that is in.
+template <int NT, typename KeyAt, typename BlockAt>
+__device__ void topk_threshold(KeyAt key_at, BlockAt block_at, int n, int k, Scratch& s,
+                               uint32_t* hist0, uint32_t* hist1, uint32_t& T, uint32_t& bcut) {
+  int need_eq = 0, eq_total = 0;
+  radix_select<NT>(key_at, n, k, s, hist0, hist1, T, need_eq, eq_total);
+  if (need_eq == 0) {
+    bcut = 0;
+  } else if (need_eq == eq_total) {
+    bcut = 0xFFFFFFFFu;
+  } else {
+    const uint32_t t = T;
+    auto tie_key = [&](int i) { return key_at(i) == t ? 0x7FFFFFFFu - block_at(i) : 0u; };
+    for (int i = threadIdx.x; i < kBins; i += NT) hist0[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&hist0[digit0(tie_key(i))], 1u);
+    __syncthreads();
+    uint32_t t2 = 0;
+    int ne2 = 0, et2 = 0;
+    radix_select<NT>(tie_key, n, need_eq, s, hist0, hist1, t2, ne2, et2);
+    // the tie keys taken are those > t2, plus t2 itself when ne2 > 0 (tie
+    // keys of the entries equal to T are distinct, so ne2 is 0 or 1)
+    bcut = (0x7FFFFFFFu - t2) + (ne2 > 0 ? 1u : 0u);
   }
-  if (lane == 0) {
-    s.wave_gt[wave] = gt;
-    s.wave_eq[wave] = eq;
+}
+
+// Emit the top-k entries -- key > T, or key == T and block < bcut -- in no
+// particular order: emit(slot, i, key) with distinct slots 0..k-1.  One
+// pass; each wave ranks its taken lanes with a ballot and reserves slots
+// with one LDS atomic per batch of groups.  Ends with a barrier.
+template <int NT, typename KeyAt, typename BlockAt, typename Emit>
+__device__ void compact_topk(KeyAt key_at, BlockAt block_at, int n, uint32_t T, uint32_t bcut,
+                             Emit emit, Scratch& s) {
+  constexpr int U = 4;  // 64-key groups per wave and batch
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  if (tid == 0) s.count = 0;
+  __syncthreads();
+  const int wave_base = tid - lane;
+  for (int i0 = wave_base; i0 < n; i0 += NT * U) {
+    uint32_t x[U];
+    bool take[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT + lane;
+      x[u] = i < n ? key_at(i) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT + lane;
+      take[u] = i < n && (x[u] > T || (x[u] == T && block_at(i) < bcut));
+    }
+    uint64_t m[U];
+    uint32_t total = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      m[u] = __ballot(take[u]);
+      total += (uint32_t)__popcll(m[u]);
+    }
+    if (total == 0) continue;  // uniform: the whole wave skips
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&s.count, total);
+    base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (take[u]) emit(base + (uint32_t)__popcll(m[u] & below), i0 + u * NT + lane, x[u]);
+      base += (uint32_t)__popcll(m[u]);
+    }
   }
   __syncthreads();
-  uint32_t gt_b = 0, eq_b = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    gt_b += w < wave ? s.wave_gt[w] : 0u;
-    eq_b += w < wave ? s.wave_eq[w] : 0u;
-  }
-  const uint64_t below = (1ull << lane) - 1ull;
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    const bool ok = i < end;
-    const uint32_t x = ok ? key_at(i) : 0u;
-    const uint64_t mg = __ballot(ok && x > T);
-    const uint64_t me = __ballot(ok && x == T);
-    const uint32_t eq_here = eq_b + (uint32_t)__popcll(me & below);
-    const bool take = ok && (x > T || (x == T && eq_here < (uint32_t)need_eq));
-    if (take) {
-      const uint32_t slot = gt_b + (uint32_t)__popcll(mg & below) + min(eq_here, (uint32_t)need_eq);
-      emit(slot, i, x);
-    }
-    gt_b += (uint32_t)__popcll(mg);
-    eq_b += (uint32_t)__popcll(me);
-  }
 }
 
 // 64-bit sort key, larger is better: score key in the high word, the
@@ -268,42 +318,103 @@ __device__ __forceinline__ uint64_t pack(uint32_t key, uint32_t block) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - block);
 }
 
-// Sort sorted[0..k) descending (entries k..511 padded with 0, which sorts
-// last because every real entry has a nonzero low word), expand each block
-// to its 4 tokens, append the tail and pad the row with -1.
-template <int NT>
-__device__ void finalize_row(uint64_t* sorted, int k, int64_t visible, int tail,
-                             int32_t* out_row) {
+// ---- 512-entry bitonic sort held in registers ------------------------------
+// A 256-thread workgroup holds the 512 entries two per lane: thread t holds
+// entries 2t (a) and 2t+1 (b).  Stride 1 is a swap inside the thread; stride
+// s >= 2 pairs lane t with lane t ^ (s/2): inside a wave that is a DPP move
+// (lane xor 1, 2, 8), a ds_swizzle (xor 4, 16) or a bpermute (xor 32); only
+// strides 128 and 256 cross waves and go through LDS.
+
+template <int X>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  if constexpr (X == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  } else if constexpr (X == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  } else if constexpr (X == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (X == 4 || X == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (X << 10) | 0x1F);  // xor within 32
+  } else {
+    static_assert(X == 32, "lane xor inside a wave");
+    return (uint32_t)__shfl_xor((int)v, X, 64);
+  }
+}
+
+template <int X>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
+  const uint32_t lo = xor_lane<X>((uint32_t)v);
+  const uint32_t hi = xor_lane<X>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// One compare-exchange stage of the descending bitonic network.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_stage(uint64_t& a, uint64_t& b, uint64_t* xchg) {
   const int tid = threadIdx.x;
-  for (int i = k + tid; i < kTopKBlocks; i += NT) sorted[i] = 0;
-  __syncthreads();
-#pragma unroll 1
-  for (int size = 2; size <= kTopKBlocks; size <<= 1) {
-#pragma unroll 1
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < kTopKBlocks / 2; t += NT) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool desc = (i & size) == 0;
-        const uint64_t a = sorted[i], b = sorted[j];
-        if ((a < b) == desc) {
-          sorted[i] = b;
-          sorted[j] = a;
-        }
-      }
+  const bool desc = ((2 * tid) & SIZE) == 0;
+  if constexpr (STRIDE == 1) {
+    const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+    a = desc ? hi : lo;
+    b = desc ? lo : hi;
+  } else {
+    constexpr int X = STRIDE / 2;
+    uint64_t oa, ob;
+    if constexpr (X >= 64) {
+      xchg[2 * tid] = a;
+      xchg[2 * tid + 1] = b;
       __syncthreads();
+      oa = xchg[(2 * tid) ^ STRIDE];
+      ob = xchg[(2 * tid + 1) ^ STRIDE];
+      __syncthreads();
+    } else {
+      oa = xor_lane64<X>(a);
+      ob = xor_lane64<X>(b);
+    }
+    const bool keep_hi = ((tid & X) == 0) == desc;
+    a = keep_hi ? (a > oa ? a : oa) : (a > oa ? oa : a);
+    b = keep_hi ? (b > ob ? b : ob) : (b > ob ? ob : b);
+  }
+}
+
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_merge(uint64_t& a, uint64_t& b, uint64_t* xchg) {
+  bitonic_stage<SIZE, STRIDE>(a, b, xchg);
+  if constexpr (STRIDE > 1) bitonic_merge<SIZE, STRIDE / 2>(a, b, xchg);
+}
+
+template <int SIZE>
+__device__ __forceinline__ void bitonic_sort(uint64_t& a, uint64_t& b, uint64_t* xchg) {
+  if constexpr (SIZE > 2) bitonic_sort<SIZE / 2>(a, b, xchg);
+  bitonic_merge<SIZE, SIZE / 2>(a, b, xchg);
+}
+
+// The k (<= 512) selected entries list[0..k) (64-bit keys from pack(), any
+// order; missing entries count as 0, which sorts last because every real
+// entry has a nonzero low word) are sorted descending; each block is
+// expanded to its 4 tokens, the tail appended and the row padded with -1.
+// Needs 256 threads and a barrier between the writes of `list` and the
+// call; `xchg` (512 entries) may be `list` itself.
+__device__ void sort_expand_write(const uint64_t* list, int k, int64_t visible, int tail,
+                                  int32_t* out_row, uint64_t* xchg) {
+  const int tid = threadIdx.x;
+  uint64_t a = 2 * tid < k ? list[2 * tid] : 0;
+  uint64_t b = 2 * tid + 1 < k ? list[2 * tid + 1] : 0;
+  bitonic_sort<kTopKBlocks>(a, b, xchg);
+  // thread t holds ranks 2t and 2t+1: tokens 8t .. 8t+7
+  const uint64_t mine[2] = {a, b};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rank = 2 * tid + h;
+    if (rank < k) {
+      const uint32_t block = 0xFFFFFFFFu - (uint32_t)mine[h];
+#pragma unroll
+      for (int j = 0; j < kRatio; ++j) out_row[kRatio * rank + j] = (int32_t)(kRatio * block + j);
     }
   }
   const int sel_tokens = kRatio * k;
-  for (int i = tid; i < kOutWidth; i += NT) {
-    int32_t v = -1;
-    if (i < sel_tokens) {
-      const uint32_t block = 0xFFFFFFFFu - (uint32_t)sorted[i >> 2];
-      v = (int32_t)(kRatio * block + (i & 3));
-    } else if (i < sel_tokens + tail) {
-      v = (int32_t)(kRatio * visible + (i - sel_tokens));
-    }
-    out_row[i] = v;
+  for (int i = sel_tokens + tid; i < kOutWidth; i += 256) {
+    out_row[i] = i < sel_tokens + tail ? (int32_t)(kRatio * visible + (i - sel_tokens)) : -1;
   }
 }
 
@@ -418,31 +529,31 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
 
   // ---- chunk top-k ---------------------------------------------------------
   const int k_local = min(kTopKBlocks, nblk);
-  uint32_t T = 0;
-  int need_eq = nblk;  // T = 0 and every key >= 0: all are taken
+  uint32_t T = 0, bcut = 0xFFFFFFFFu;  // every key >= 0: all are taken
   auto lds_key = [&](int i) { return sm.keys[i]; };
+  auto block_of = [&](int i) { return (uint32_t)(chunk_base + i); };
   Scratch& s = sm.u.sel.s;
   if (select) {
-    radix_select<kChunkThreads>(lds_key, nblk, k_local, s, sm.hist0, sm.u.sel.hist1, T, need_eq);
+    topk_threshold<kChunkThreads>(lds_key, block_of, nblk, k_local, s, sm.hist0, sm.u.sel.hist1,
+                                  T, bcut);
   }
 
   if (row.nchunks == 1) {
     uint64_t* sorted = sm.u.sel.sorted;
     compact_topk<kChunkThreads>(
-        lds_key, nblk, T, need_eq,
-        [&](uint32_t slot, int i, uint32_t x) { sorted[slot] = pack(x, (uint32_t)(chunk_base + i)); },
-        s);
-    finalize_row<kChunkThreads>(sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth);
+        lds_key, block_of, nblk, T, bcut,
+        [&](uint32_t slot, int i, uint32_t x) { sorted[slot] = pack(x, block_of(i)); }, s);
+    sort_expand_write(sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth, sorted);
     return;
   }
   const int64_t cbase = (r * p.chunks_per_row + chunk) * p.cand_cap;
   uint32_t* ckeys = p.cand_keys + cbase;
   uint32_t* cblocks = p.cand_blocks + cbase;
   compact_topk<kChunkThreads>(
-      lds_key, nblk, T, need_eq,
+      lds_key, block_of, nblk, T, bcut,
       [&](uint32_t slot, int i, uint32_t x) {
         ckeys[slot] = x;
-        cblocks[slot] = (uint32_t)(chunk_base + i);
+        cblocks[slot] = block_of(i);
       },
       s);
 }
@@ -467,7 +578,7 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
   if (row.nchunks == 1) return;  // finished by the chunk kernel
 
   // Every chunk but the last holds cand_cap candidates, so the row's list is
-  // contiguous and in block order.
+  // contiguous.
   const int last_n = (int)(row.visible - (row.nchunks - 1) * p.chunk_blocks);
   const int m = (int)((row.nchunks - 1) * p.cand_cap) + min(p.cand_cap, last_n);
   const int k = (int)min((int64_t)kTopKBlocks, row.visible);
@@ -481,8 +592,8 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
     const int nb = min(kBatch, m - base);
     for (int i = tid; i < kBins; i += kMergeThreads) sm.hist0[i] = 0;
     __syncthreads();
-    // list = [running best (earlier blocks)] + [next batch]; the first radix
-    // histogram is counted on the way into LDS
+    // list = [running best] + [next batch]; the first radix histogram is
+    // counted on the way into LDS
     for (int i = tid; i < best_n; i += kMergeThreads) {
       const uint32_t x = sm.best_keys[i];
       sm.keys[i] = x;
@@ -530,24 +641,25 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
     __syncthreads();
     const int n_list = best_n + nb;
     const int kk = min(k, n_list);
-    uint32_t T = 0;
-    int need_eq = n_list;
+    uint32_t T = 0, bcut = 0xFFFFFFFFu;
     auto lds_key = [&](int i) { return sm.keys[i]; };
+    auto block_of = [&](int i) { return sm.blocks[i]; };
     if (n_list > kk) {
-      radix_select<kMergeThreads>(lds_key, n_list, kk, sm.s, sm.hist0, sm.hist1, T, need_eq);
+      topk_threshold<kMergeThreads>(lds_key, block_of, n_list, kk, sm.s, sm.hist0, sm.hist1, T,
+                                    bcut);
     }
     compact_topk<kMergeThreads>(
-        lds_key, n_list, T, need_eq,
+        lds_key, block_of, n_list, T, bcut,
         [&](uint32_t slot, int i, uint32_t x) {
           sm.best_keys[slot] = x;
           sm.best_blocks[slot] = sm.blocks[i];
         },
         sm.s);
-    __syncthreads();
     best_n = kk;
   }
   for (int i = tid; i < best_n; i += kMergeThreads) sm.sorted[i] = pack(sm.best_keys[i], sm.best_blocks[i]);
-  finalize_row<kMergeThreads>(sm.sorted, best_n, row.visible, row.tail, p.out + r * kOutWidth);
+  __syncthreads();
+  sort_expand_write(sm.sorted, best_n, row.visible, row.tail, p.out + r * kOutWidth, sm.sorted);
 }
 
 }  // namespace
