@@ -1,12 +1,19 @@
 """Decode-step throughput of the QSA select + sparse-attention path on one
 MI355X.
 
-Workload: the long-context decode batch -- R=128 query rows, each of a
-131072-token request (32768 compressed blocks), a 32768-page fp16 N(0,1)
-compressed-key cache (1 GiB) behind random permuted block tables, and
-full-width [128,2051] sparse attention over a 131072-token packed fp16 KV
-cache (128 MiB).  Inputs are seeded synthetic data, resident in HBM before
-timing starts.
+Workloads (``--workload``):
+
+* long_context (default): the long-context decode batch -- R=128 query rows,
+  each of a 131072-token request (32768 compressed blocks), a 32768-page
+  fp16 N(0,1) compressed-key cache (1 GiB) behind random permuted block
+  tables, and full-width [128,2051] sparse attention over a 131072-token
+  packed fp16 KV cache (128 MiB).
+* multi_token: several query rows per request -- 48 speculative-decode
+  requests with 4 draft positions each and 4 chunked-prefill requests with
+  16 positions each (R=256), lengths uniform in [8192, 65536], an 8192-page
+  N(0,1) compressed-key cache (256 MiB).
+
+Inputs are seeded synthetic data, resident in HBM before timing starts.
 
 One step = one qsa_decode_step call (selection then attention on one
 stream, no host sync); K steps are timed with HIP events at both ends.  The
@@ -14,7 +21,8 @@ steps rotate over distinct KV caches, as consecutive layers would.  A second
 pass runs the two stages through qsa_select and qsa_sparse_attn with events
 between them for the per-stage times and the roofline.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -44,15 +52,22 @@ def log(msg: str) -> None:
 
 
 def select_algorithmic_bytes(seq_lens, query_pos, token_to_req) -> int:
-    """Bytes the selection must move per launch: per row, 256 B per visible
-    compressed key, 4 B per block-table entry read, the 1 KiB query, 16 B of
-    row metadata and the 8204 B output row."""
+    """Bytes the selection must move per launch.  Per request, its compressed
+    keys once (256 B per block visible to its furthest row) and the 4 B
+    block-table entries that map them: rows of one request read the same
+    pages.  Per row, the 1 KiB query, 16 B of row metadata and the 8204 B
+    output row."""
+    furthest = {}
     total = 0
     for r in range(len(token_to_req)):
-        L = int(seq_lens[token_to_req[r]])
+        req = int(token_to_req[r])
+        L = int(seq_lens[req])
         qp = int(query_pos[r])
         v = max(0, min((qp + 1) // 4, L // 4))
-        total += 256 * v + 4 * (-(-v // 128)) + 1024 + 16 + 8204
+        furthest[req] = max(furthest.get(req, 0), v)
+        total += 1024 + 16 + 8204
+    for v in furthest.values():
+        total += 256 * v + 4 * (-(-v // 128))
     return total
 
 
@@ -109,6 +124,18 @@ def cpu_baseline(w, scale: float, max_seconds: float = 20.0) -> dict:
                       f"per row, {dt:.1f} s single-threaded", "_outs": outs}
 
 
+def workload_config(w, kv_copies: int) -> dict:
+    lens = w.seq_lens[w.token_to_req].astype(np.int64)
+    cfg = {"workload": w.name, "rows": int(w.rows), "requests": int(len(np.unique(w.token_to_req))),
+           "cache_pages": int(w.kcache.shape[0]), "kv_tokens": int(w.kv.shape[0] * w.kv.shape[1]),
+           "top_blocks": 512, "index_width": 2051, "kv_caches_rotated": kv_copies}
+    if np.all(lens == lens[0]):
+        cfg["seq_len"] = int(lens[0])
+    else:
+        cfg["seq_len_range"] = [int(lens.min()), int(lens.max())]
+    return cfg
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +143,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", choices=["long_context", "multi_token"], default="long_context")
     ap.add_argument("--kv-copies", type=int, default=8,
                     help="distinct KV caches the steps rotate over (one per simulated layer)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -142,7 +170,7 @@ def main() -> int:
         return 0
 
     t0 = time.perf_counter()
-    w = wl.long_context(args.seed)
+    w = wl.long_context(args.seed) if args.workload == "long_context" else wl.multi_token_rows(args.seed)
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -214,7 +242,8 @@ def main() -> int:
     sel_avg_s = float(np.mean(sel_ms)) / 1e3
     att_avg_s = float(np.mean(att_ms)) / 1e3
     achieved = sel_bytes / sel_avg_s / 1e9
-    traffic = stored_traffic(sel_bytes)
+    # the committed counter summary covers the long-context launch only
+    traffic = stored_traffic(sel_bytes) if args.workload == "long_context" else None
     rows_per_s = R / (ms_per_step / 1e3)
     step_gbs = (sel_bytes + att_bytes) / (ms_per_step / 1e3) / 1e9
 
@@ -231,9 +260,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)",
-        "config": {"workload": w.name, "rows": R, "seq_len": 131072, "visible_blocks": 32768,
-                   "cache_pages": 32768, "kv_tokens": 131072, "top_blocks": 512,
-                   "index_width": 2051, "kv_caches_rotated": len(kv_sets)},
+        "config": workload_config(w, len(kv_sets)),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

@@ -164,7 +164,7 @@ def decode_rows(lengths) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
 
 
 # ---------------------------------------------------------------------------
-# the five named workloads
+# the named workloads
 
 def tiny_integer(seed: int = 0) -> Workload:
     """R=1, L=519 (a cross-page tail), integer-valued keys and queries.
@@ -299,12 +299,47 @@ def long_context(seed: int = 0, rows: int = 128) -> Workload:
     return w
 
 
+def multi_token_rows(seed: int = 0, decode_requests: int = 48, next_n: int = 4,
+                     prefill_requests: int = 4, prefill_chunk: int = 16,
+                     integer: bool = False) -> Workload:
+    """Several query rows per request: speculative-decode requests score
+    next_n draft positions each (query positions L - next_n .. L - 1) and
+    chunked-prefill requests score a chunk of prefill_chunk positions
+    (L - prefill_chunk .. L - 1); one row per position, rows of a request
+    adjacent.  L is uniform in [8192, 65536]; 8192 N(0,1) pages (or integer
+    keys in [-4,4] with integer queries in [-2,2] when ``integer``).
+
+    Draw order: lengths (decode requests, then prefill requests); per-row
+    distinct block tables; kcache; q_sel; q_attn; kv (N(0,1), sized to the
+    longest request).
+    """
+    rng = np.random.default_rng(seed)
+    N = decode_requests + prefill_requests
+    lengths = rng.integers(8192, 65536 + 1, size=N)
+    per_req = [next_n] * decode_requests + [prefill_chunk] * prefill_requests
+    P = 8192
+    bt = block_table_per_row(rng, lengths, P)
+    if integer:
+        kcache = int_f16(rng, -4, 4, (P, SLOTS, 1, SEL_DIM))
+    else:
+        kcache = normal_f16(rng, (P, SLOTS, 1, SEL_DIM))
+    t2r = np.concatenate([np.full(c, i, np.int32) for i, c in enumerate(per_req)])
+    qp = np.concatenate([int(L) - c + np.arange(c) for L, c in zip(lengths, per_req)]).astype(np.int64)
+    R = t2r.size
+    q_sel = int_f16(rng, -2, 2, (R, SEL_HEADS, SEL_DIM)) if integer else normal_f16(rng, (R, SEL_HEADS, SEL_DIM))
+    q_attn = normal_f16(rng, (R, ATT_HEADS, ATT_DIM))
+    kv = normal_f16(rng, (pages_needed(int(lengths.max())), TOKENS_PER_PAGE, KV_ROW))
+    name = f"multi_token_R{R}_next{next_n}_prefill{prefill_chunk}" + ("_int" if integer else "")
+    return Workload(name, seed, q_sel, kcache, bt, t2r, lengths.astype(np.int32), qp, q_attn, kv)
+
+
 NAMED = {
     1: tiny_integer,
     2: saturated_row,
     3: batched_shared,
     4: ties_and_edges,
     5: long_context,
+    6: multi_token_rows,
 }
 
 

@@ -65,3 +65,16 @@ def test_long_context_full_size():
     k, v = qsa.kv_views(kvd)
     alone = qsa.qsa_sparse_attn(dev(w.q_attn), k, v, dev(idx), SCALE).cpu().numpy()
     assert np.array_equal(alone, out)
+
+
+def test_multi_token_rows():
+    w = wl.multi_token_rows(0)
+    banner(f"decode {w.name}")
+    idx, out = decode_gpu(w)
+    inputs = w.select_inputs()
+    want_idx = orc().select(*inputs)
+    check_select_band(idx, want_idx, orc(), inputs, range(w.rows))
+    same = np.flatnonzero(np.all(idx == want_idx, axis=1))
+    assert same.size > w.rows // 2
+    want = orc().sparse_attn(w.q_attn[same], w.kv, want_idx[same], SCALE)
+    check_attn(out[same], want, "multi-token rows with identical selection")

@@ -186,3 +186,25 @@ def test_fail_closed_leaves_output_untouched():
         qsa.qsa_select(*d, out=torch.empty((1, 2048), dtype=torch.int32, device=d[0].device))
     torch.cuda.synchronize()
     assert torch.all(out == 12345)
+
+
+@pytest.mark.parametrize("integer", [True, False], ids=["int", "normal"])
+def test_multi_token_rows(integer):
+    """Speculative-decode (4 draft positions per request) and chunked-prefill
+    (16 positions) rows: each row's visible blocks and tail follow its own
+    query position."""
+    w = wl.multi_token_rows(0, integer=integer)
+    inputs = w.select_inputs()
+    banner(f"select {w.name}")
+    got = select_gpu(*inputs)
+    want = orc().select(*inputs)
+    if integer:
+        bad = np.flatnonzero(~np.all(got == want, axis=1))
+        assert bad.size == 0, f"rows differ: {bad[:10]}"
+    else:
+        check_select_band(got, want, orc(), inputs, range(w.rows))
+    # rows of one request differ only through their positions: tails shift
+    widths = (got >= 0).sum(axis=1)
+    for r in range(w.rows):
+        V, T = orc().row_extent(int(w.seq_lens[w.token_to_req[r]]), int(w.query_pos[r]))
+        assert widths[r] == min(2048, 4 * V) + T

@@ -69,3 +69,15 @@ def test_shared_pages_batched_table_only():
     used = bt[bt >= 0]
     assert len(np.unique(used)) == used.size
     assert [int((row >= 0).sum()) for row in bt] == [wl.pages_needed(L) for L in lengths]
+
+
+def test_multi_token_rows_structure():
+    w = wl.multi_token_rows(0, decode_requests=6, next_n=3, prefill_requests=2, prefill_chunk=5)
+    assert w.rows == 6 * 3 + 2 * 5
+    # rows of a request are adjacent and end at the request's last position
+    for req in range(8):
+        rows = np.flatnonzero(w.token_to_req == req)
+        assert np.all(np.diff(rows) == 1)
+        pos = w.query_pos[rows]
+        assert pos[-1] == w.seq_lens[req] - 1 and np.all(np.diff(pos) == 1)
+    assert w.query_pos.dtype == np.int64 and w.token_to_req.dtype == np.int32
