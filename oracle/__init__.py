@@ -16,6 +16,11 @@ Parity status of each function (the pins live in ``tests/oracle_pins.py``):
 * ``sparse_attn``  pinned: single-index/duplicate/hole closed forms, equal
   logits -> mean, two-token logistic form, torch float64 library softmax.
 * ``half_to_double`` pinned: every binary16 bit pattern against numpy.
+* ``e4m3_to_double`` pinned: every e4m3 code against torch.float8_e4m3fn.
+* ``select_fp8`` / ``row_scores_fp8`` pinned: integer keys re-encoded as
+  e4m3 codes with power-of-two scales give the fp16 selection (itself
+  pinned by brute force) exactly; one-hot queries read back scale * code for
+  every code; numpy float64 gather of the dequantized keys + lexsort.
 """
 
 from __future__ import annotations
@@ -75,6 +80,12 @@ class Oracle:
         lib.qsa_oracle_select.restype = ctypes.c_int
         lib.qsa_oracle_sparse_attn.argtypes = [i64, i64, p, p, p, ctypes.c_double, p]
         lib.qsa_oracle_sparse_attn.restype = ctypes.c_int
+        lib.qsa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        lib.qsa_oracle_e4m3_to_double.restype = ctypes.c_double
+        lib.qsa_oracle_row_scores_fp8.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p, i64, p]
+        lib.qsa_oracle_row_scores_fp8.restype = ctypes.c_int
+        lib.qsa_oracle_select_fp8.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p]
+        lib.qsa_oracle_select_fp8.restype = ctypes.c_int
         lib.qsa_oracle_mutant.argtypes = []
         lib.qsa_oracle_mutant.restype = ctypes.c_int
         self.lib = lib
@@ -97,6 +108,9 @@ class Oracle:
     # -- API ---------------------------------------------------------------
     def half_to_double(self, bits: int) -> float:
         return self.lib.qsa_oracle_half_to_double(int(bits) & 0xFFFF)
+
+    def e4m3_to_double(self, code: int) -> float:
+        return self.lib.qsa_oracle_e4m3_to_double(int(code) & 0xFF)
 
     def row_extent(self, seq_len: int, query_pos: int) -> tuple[int, int]:
         """(visible blocks V, tail length T) of one query row."""
@@ -142,6 +156,47 @@ class Oracle:
             max_blocks, ctypes.byref(v))
         self._check(rc)
         return scores[: v.value].copy()
+
+    def _fp8_cache(self, codes, scales):
+        codes = self._c(codes, np.uint8)
+        scales = self._c(scales, np.float32)
+        assert codes.shape[1:] == (128, 1, 128)
+        assert scales.shape == codes.shape[:2]
+        return codes, scales
+
+    def select_fp8(self, q, codes, scales, block_table, token_to_req, seq_lens,
+                   query_pos) -> np.ndarray:
+        """[R,2051] int32 selection over an e4m3 key cache: codes
+        [P,128,1,128] uint8, scales [P,128] float32."""
+        q, _, bt, t2r, sl, qp = self._select_args(
+            q, np.zeros((1, 128, 1, 128), np.float16), block_table, token_to_req, seq_lens,
+            query_pos)
+        codes, scales = self._fp8_cache(codes, scales)
+        R = q.shape[0]
+        out = np.empty((R, WIDTH), dtype=np.int32)
+        rc = self.lib.qsa_oracle_select_fp8(
+            R, codes.shape[0], sl.shape[0], bt.shape[1], self._ptr(q), self._ptr(codes),
+            self._ptr(scales), self._ptr(bt), self._ptr(t2r), self._ptr(sl), self._ptr(qp),
+            self._ptr(out))
+        self._check(rc)
+        return out
+
+    def row_scores_fp8(self, r, q, codes, scales, block_table, token_to_req, seq_lens,
+                       query_pos) -> np.ndarray:
+        """float32 scores of every visible block of row r over an e4m3 cache."""
+        q, _, bt, t2r, sl, qp = self._select_args(
+            q, np.zeros((1, 128, 1, 128), np.float16), block_table, token_to_req, seq_lens,
+            query_pos)
+        codes, scales = self._fp8_cache(codes, scales)
+        max_blocks = bt.shape[1] * 128
+        out = np.zeros(max_blocks, dtype=np.float32)
+        v = ctypes.c_int64()
+        rc = self.lib.qsa_oracle_row_scores_fp8(
+            int(r), codes.shape[0], sl.shape[0], bt.shape[1], self._ptr(q), self._ptr(codes),
+            self._ptr(scales), self._ptr(bt), self._ptr(t2r), self._ptr(sl), self._ptr(qp),
+            self._ptr(out), max_blocks, ctypes.byref(v))
+        self._check(rc)
+        return out[: v.value].copy()
 
     def sparse_attn(self, q, kv, indices, scale: float) -> np.ndarray:
         """[R,3,256] float64 attention output.  kv is [..., 512] fp16 with

@@ -32,6 +32,13 @@
  *     o[r][h][:] = sum_j softmax(l)_j * V[idx_j][:]      (V = kv[t][256:512])
  *     an empty J gives o = 0.
  *
+ *   fp8 key cache (the vllm qsa_cache.py page lists fp8 / fp8_e4m3 among
+ *   the compressed indexer cache's dtypes; the "[XPU] Enable multiple key
+ *   kernels for sparse attention" page's fp8 logits calls take the keys as
+ *   k_quant with a k_scale): each compressed key is 128 e4m3 codes plus one
+ *   binary32 scale, and the key used for scoring is the dequantized vector
+ *   scale * e4m3(code[d]); everything else is as above.
+ *
  * Precision: fp16 inputs are widened to double with a conversion written
  * from the IEEE 754 binary16 definition; every dot product and softmax is
  * evaluated in double.  A selection score is rounded once to binary32 at
@@ -93,6 +100,33 @@ double qsa_oracle_half_to_double(uint16_t h) {
   return sign ? -v : v;
 }
 
+/* OCP 8-bit floating point, E4M3 variant without infinities ("e4m3fn"):
+ * 1 sign bit, 4 exponent bits (bias 7), 3 fraction bits.  Exponent 0
+ * encodes subnormals (fraction * 2^-9); the all-ones pattern S.1111.111 is
+ * NaN and every other pattern is finite (largest 448). */
+double qsa_oracle_e4m3_to_double(uint8_t c) {
+  int sign = (c >> 7) & 1;
+  int expo = (c >> 3) & 15;
+  int frac = c & 7;
+  double v;
+  if (expo == 15 && frac == 7) {
+    v = NAN;
+  } else if (expo == 0) {
+#if QSA_ORACLE_MUTANT == 13
+    v = ldexp((double)(8 + frac), -9); /* planted: subnormal read as normal */
+#else
+    v = ldexp((double)frac, -9);
+#endif
+  } else {
+#if QSA_ORACLE_MUTANT == 12
+    v = ldexp((double)(8 + frac), expo - 11); /* planted: exponent bias 8 */
+#else
+    v = ldexp((double)(8 + frac), expo - 10);
+#endif
+  }
+  return sign ? -v : v;
+}
+
 /* Visible blocks and tail length of one query row. */
 void qsa_oracle_row_extent(int64_t seq_len, int64_t query_pos, int64_t* visible,
                            int64_t* tail) {
@@ -145,11 +179,33 @@ static void widen_query(const uint16_t* q_row, double* qd) {
   for (int i = 0; i < OR_SEL_HEADS * OR_SEL_DIM; ++i) qd[i] = qsa_oracle_half_to_double(q_row[i]);
 }
 
-/* Score of one compressed key against the row's four indexer heads (qd:
- * the row's query already widened to double, [4][128]). */
-static float block_score(const double* qd, const uint16_t* key) {
-  double kd[OR_SEL_DIM];
-  for (int d = 0; d < OR_SEL_DIM; ++d) kd[d] = qsa_oracle_half_to_double(key[d]);
+/* The compressed key cache: binary16 keys, or e4m3 codes with one binary32
+ * scale per key.  Both are [P,128,1,128] in elements; scales are [P,128]. */
+typedef struct {
+  const uint16_t* f16;
+  const uint8_t* codes;
+  const float* scales;
+} key_cache;
+
+/* Key number `slot_index` (= page * 128 + slot) widened to double: the
+ * binary16 values, or scale * e4m3(code) per element. */
+static void widen_key(const key_cache* kc, int64_t slot_index, double* kd) {
+  if (kc->f16) {
+    const uint16_t* key = kc->f16 + slot_index * OR_SEL_DIM;
+    for (int d = 0; d < OR_SEL_DIM; ++d) kd[d] = qsa_oracle_half_to_double(key[d]);
+    return;
+  }
+  const uint8_t* code = kc->codes + slot_index * OR_SEL_DIM;
+  double scale = (double)kc->scales[slot_index];
+#if QSA_ORACLE_MUTANT == 11
+  scale = 1.0; /* planted: per-key scale ignored */
+#endif
+  for (int d = 0; d < OR_SEL_DIM; ++d) kd[d] = scale * qsa_oracle_e4m3_to_double(code[d]);
+}
+
+/* Score of one compressed key (kd, widened) against the row's four indexer
+ * heads (qd: the row's query widened to double, [4][128]). */
+static float block_score(const double* qd, const double* kd) {
   double total = 0.0;
   int heads = OR_SEL_HEADS;
 #if QSA_ORACLE_MUTANT == 5
@@ -169,11 +225,10 @@ static float block_score(const double* qd, const uint16_t* key) {
   return (float)total;
 }
 
-/* Address of compressed key b of a request.  Returns NULL when the block
- * table or the page id cannot serve it. */
-static const uint16_t* key_address(const uint16_t* kcache, int64_t num_pages,
-                                   const int32_t* table_row, int64_t table_width,
-                                   int64_t b, int* err) {
+/* Cache slot (page * 128 + slot) of compressed key b of a request, or -1
+ * with *err set when the block table or the page id cannot serve it. */
+static int64_t key_slot(int64_t num_pages, const int32_t* table_row, int64_t table_width,
+                        int64_t b, int* err) {
   int64_t logical_page = b / OR_PAGE_SLOTS;
   int64_t slot = b % OR_PAGE_SLOTS;
 #if QSA_ORACLE_MUTANT == 3
@@ -183,14 +238,39 @@ static const uint16_t* key_address(const uint16_t* kcache, int64_t num_pages,
 #endif
   if (logical_page >= table_width) {
     *err = OR_ERR_TABLE;
-    return NULL;
+    return -1;
   }
   int64_t page = table_row[logical_page];
   if (page < 0 || page >= num_pages) {
     *err = OR_ERR_PAGE;
-    return NULL;
+    return -1;
   }
-  return kcache + (page * OR_PAGE_SLOTS + slot) * OR_SEL_DIM;
+  return page * OR_PAGE_SLOTS + slot;
+}
+
+static int row_scores(int64_t r, int64_t num_pages, int64_t num_reqs, int64_t table_width,
+                      const uint16_t* q, const key_cache* kc, const int32_t* block_table,
+                      const int32_t* token_to_req, const int32_t* seq_lens,
+                      const int64_t* query_pos, float* scores, int64_t max_blocks,
+                      int64_t* visible) {
+  int64_t req = token_to_req[r];
+  if (req < 0 || req >= num_reqs) return OR_ERR_REQ;
+  int64_t v, t;
+  qsa_oracle_row_extent(seq_lens[req], query_pos[r], &v, &t);
+  *visible = v;
+  if (v > max_blocks) return OR_ERR_ARG;
+  double qd[OR_SEL_HEADS * OR_SEL_DIM];
+  widen_query(q + r * OR_SEL_HEADS * OR_SEL_DIM, qd);
+  const int32_t* table_row = block_table + req * table_width;
+  double kd[OR_SEL_DIM];
+  for (int64_t b = 0; b < v; ++b) {
+    int err = OR_OK;
+    int64_t at = key_slot(num_pages, table_row, table_width, b, &err);
+    if (at < 0) return err;
+    widen_key(kc, at, kd);
+    scores[b] = block_score(qd, kd);
+  }
+  return OR_OK;
 }
 
 /*
@@ -203,35 +283,28 @@ int qsa_oracle_row_scores(int64_t r, int64_t num_pages, int64_t num_reqs,
                           const int32_t* token_to_req, const int32_t* seq_lens,
                           const int64_t* query_pos, float* scores,
                           int64_t max_blocks, int64_t* visible) {
-  int64_t req = token_to_req[r];
-  if (req < 0 || req >= num_reqs) return OR_ERR_REQ;
-  int64_t v, t;
-  qsa_oracle_row_extent(seq_lens[req], query_pos[r], &v, &t);
-  *visible = v;
-  if (v > max_blocks) return OR_ERR_ARG;
-  double qd[OR_SEL_HEADS * OR_SEL_DIM];
-  widen_query(q + r * OR_SEL_HEADS * OR_SEL_DIM, qd);
-  const int32_t* table_row = block_table + req * table_width;
-  for (int64_t b = 0; b < v; ++b) {
-    int err = OR_OK;
-    const uint16_t* key = key_address(kcache, num_pages, table_row, table_width, b, &err);
-    if (!key) return err;
-    scores[b] = block_score(qd, key);
-  }
-  return OR_OK;
+  key_cache kc = {kcache, NULL, NULL};
+  return row_scores(r, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
+                    seq_lens, query_pos, scores, max_blocks, visible);
 }
 
-/*
- * Selection for rows [0, R).  Shapes: q [R,4,128] fp16 bits,
- * kcache [P,128,1,128] fp16 bits, block_table [N,W] int32,
- * token_to_req [R] int32, seq_lens [N] int32, query_pos [R] int64,
- * out [R,2051] int32 (written).  Returns OR_OK or the first error.
- */
-int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
-                      int64_t table_width, const uint16_t* q, const uint16_t* kcache,
-                      const int32_t* block_table, const int32_t* token_to_req,
-                      const int32_t* seq_lens, const int64_t* query_pos,
-                      int32_t* out) {
+/* As qsa_oracle_row_scores, for an e4m3 cache: codes [P,128,1,128] bytes,
+ * scales [P,128] binary32. */
+int qsa_oracle_row_scores_fp8(int64_t r, int64_t num_pages, int64_t num_reqs,
+                              int64_t table_width, const uint16_t* q, const uint8_t* codes,
+                              const float* scales, const int32_t* block_table,
+                              const int32_t* token_to_req, const int32_t* seq_lens,
+                              const int64_t* query_pos, float* scores, int64_t max_blocks,
+                              int64_t* visible) {
+  key_cache kc = {NULL, codes, scales};
+  return row_scores(r, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
+                    seq_lens, query_pos, scores, max_blocks, visible);
+}
+
+static int select_rows(int64_t R, int64_t num_pages, int64_t num_reqs, int64_t table_width,
+                       const uint16_t* q, const key_cache* kc, const int32_t* block_table,
+                       const int32_t* token_to_req, const int32_t* seq_lens,
+                       const int64_t* query_pos, int32_t* out) {
   for (int64_t r = 0; r < R; ++r) {
     int32_t* out_row = out + r * OR_WIDTH;
     for (int i = 0; i < OR_WIDTH; ++i) out_row[i] = -1;
@@ -247,14 +320,16 @@ int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
     double qd[OR_SEL_HEADS * OR_SEL_DIM];
     widen_query(q + r * OR_SEL_HEADS * OR_SEL_DIM, qd);
     const int32_t* table_row = block_table + req * table_width;
+    double kd[OR_SEL_DIM];
     for (int64_t b = 0; b < v; ++b) {
       int err = OR_OK;
-      const uint16_t* key = key_address(kcache, num_pages, table_row, table_width, b, &err);
-      if (!key) {
+      int64_t at = key_slot(num_pages, table_row, table_width, b, &err);
+      if (at < 0) {
         free(all);
         return err;
       }
-      all[b].score = block_score(qd, key);
+      widen_key(kc, at, kd);
+      all[b].score = block_score(qd, kd);
       all[b].block = b;
     }
     if (v > 1) qsort(all, (size_t)v, sizeof(scored_block), by_score_then_index);
@@ -270,6 +345,34 @@ int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
     free(all);
   }
   return OR_OK;
+}
+
+/*
+ * Selection for rows [0, R).  Shapes: q [R,4,128] fp16 bits,
+ * kcache [P,128,1,128] fp16 bits, block_table [N,W] int32,
+ * token_to_req [R] int32, seq_lens [N] int32, query_pos [R] int64,
+ * out [R,2051] int32 (written).  Returns OR_OK or the first error.
+ */
+int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
+                      int64_t table_width, const uint16_t* q, const uint16_t* kcache,
+                      const int32_t* block_table, const int32_t* token_to_req,
+                      const int32_t* seq_lens, const int64_t* query_pos,
+                      int32_t* out) {
+  key_cache kc = {kcache, NULL, NULL};
+  return select_rows(R, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
+                     seq_lens, query_pos, out);
+}
+
+/* As qsa_oracle_select, for an e4m3 cache: codes [P,128,1,128] bytes,
+ * scales [P,128] binary32. */
+int qsa_oracle_select_fp8(int64_t R, int64_t num_pages, int64_t num_reqs,
+                          int64_t table_width, const uint16_t* q, const uint8_t* codes,
+                          const float* scales, const int32_t* block_table,
+                          const int32_t* token_to_req, const int32_t* seq_lens,
+                          const int64_t* query_pos, int32_t* out) {
+  key_cache kc = {NULL, codes, scales};
+  return select_rows(R, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
+                     seq_lens, query_pos, out);
 }
 
 /*

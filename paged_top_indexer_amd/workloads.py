@@ -16,6 +16,9 @@ Layouts (fp16 unless stated):
 * ``kv``           [NP, 512, 512]     packed token rows: K = [..., :256],
                                       V = [..., 256:]; token t is flat row t
 * ``indices``      [R, 2051] int32    attention index rows, -1 = hole
+* ``kcodes``       [P, 128, 1, 128] uint8, ``kscale`` [P, 128] float32: the
+                   same keys as an e4m3 cache (codes plus one scale per key),
+                   for the workloads that carry one
 
 A page of the compressed cache covers 128 compressed keys, i.e. 512 tokens
 at four tokens per key, so a request of L tokens holds ceil(L / 512) pages.
@@ -56,6 +59,9 @@ class Workload:
     attn_indices: np.ndarray | None = None
     attn_q: np.ndarray | None = None
     notes: dict = field(default_factory=dict)
+    # e4m3 form of the compressed-key cache (with_fp8_keys)
+    kcodes: np.ndarray | None = None
+    kscale: np.ndarray | None = None
 
     @property
     def rows(self) -> int:
@@ -63,6 +69,11 @@ class Workload:
 
     def select_inputs(self) -> tuple:
         return (self.q_sel, self.kcache, self.block_table, self.token_to_req,
+                self.seq_lens, self.query_pos)
+
+    def select_inputs_fp8(self) -> tuple:
+        assert self.kcodes is not None, "workload has no e4m3 key cache"
+        return (self.q_sel, self.kcodes, self.kscale, self.block_table, self.token_to_req,
                 self.seq_lens, self.query_pos)
 
 
@@ -83,6 +94,57 @@ def normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
 def int_f16(rng: np.random.Generator, lo: int, hi: int, shape) -> np.ndarray:
     """Integer values uniform in [lo, hi] as fp16."""
     return rng.integers(lo, hi + 1, size=shape).astype(np.float16)
+
+
+E4M3_MAX = 448.0
+
+
+def e4m3_codes(values: np.ndarray) -> np.ndarray:
+    """uint8 e4m3 ("e4m3fn") codes of float32 values, rounded to nearest even
+    by torch's float8 cast after clipping to the format's range."""
+    import torch
+
+    v = np.clip(np.ascontiguousarray(values, dtype=np.float32), -E4M3_MAX, E4M3_MAX)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def fp8_integer_keys(rng: np.random.Generator, kcache: np.ndarray):
+    """An e4m3 cache holding exactly the same integer-valued keys: each key
+    gets a scale 2^j, j uniform in {-2..2}, and codes key / 2^j (integers in
+    [-4, 4] scaled by 2^-j have at most two significant bits, so every code
+    is exact and scale * code == key)."""
+    P = kcache.shape[0]
+    scales = np.ldexp(np.float32(1.0), rng.integers(-2, 3, size=(P, SLOTS))).astype(np.float32)
+    vals = kcache.astype(np.float32) / scales[:, :, None, None]
+    codes = e4m3_codes(vals)
+    return codes, scales
+
+
+def fp8_normal_keys(kcache: np.ndarray, slab: int = 1024):
+    """Per-key absmax quantization of fp16 keys: scale = max|k| / 448 (1 for
+    an all-zero key), codes = e4m3(k / scale).  Done in slabs of pages."""
+    P = kcache.shape[0]
+    codes = np.empty(kcache.shape, dtype=np.uint8)
+    scales = np.empty((P, SLOTS), dtype=np.float32)
+    for s0 in range(0, P, slab):
+        k = kcache[s0:s0 + slab].astype(np.float32)
+        amax = np.abs(k).max(axis=(2, 3))
+        sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        scales[s0:s0 + slab] = sc
+        codes[s0:s0 + slab] = e4m3_codes(k / sc[:, :, None, None])
+    return codes, scales
+
+
+def with_fp8_keys(w: "Workload", integer: bool) -> "Workload":
+    """The workload with an e4m3 copy of its compressed-key cache attached:
+    the same integer keys exactly (``integer``; scale exponents drawn from
+    default_rng(seed + 7777)), or the absmax quantization of its keys."""
+    if integer:
+        w.kcodes, w.kscale = fp8_integer_keys(np.random.default_rng(w.seed + 7777), w.kcache)
+    else:
+        w.kcodes, w.kscale = fp8_normal_keys(w.kcache)
+    w.name = w.name + "_fp8"
+    return w
 
 
 def pages_needed(seq_len: int) -> int:

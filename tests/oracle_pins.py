@@ -10,7 +10,10 @@ when the oracle disagrees with:
 * numpy's float64 gather and library sort on N(0,1) inputs,
 * closed-form special cases of selection and of attention,
 * torch's float64 softmax on gathered rows,
-* numpy's binary16 decoder, for every bit pattern.
+* numpy's binary16 decoder, for every bit pattern,
+* torch's float8_e4m3fn decoder, for every code; the fp16 selection
+  (pinned above) on integer keys re-encoded as e4m3 codes with power-of-two
+  scales, which dequantize to exactly the same keys.
 
 The same functions run against the trusted oracle (they must all pass) and
 against builds with one planted mistake (at least one must fail).
@@ -288,8 +291,99 @@ def pin_half_to_double(orc):
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
 
 
+# ---------------------------------------------------------------------------
+# e4m3 key cache
+
+def torch_e4m3_table() -> np.ndarray:
+    """float64 value of every e4m3fn code, decoded by torch."""
+    import torch
+
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def pin_e4m3_to_double(orc):
+    """Every e4m3 code against torch's float8_e4m3fn decoder."""
+    want = torch_e4m3_table()
+    got = np.array([orc.e4m3_to_double(c) for c in range(256)])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_select_fp8_integer_equivalence(orc):
+    """Integer keys re-encoded as e4m3 codes with per-key power-of-two
+    scales dequantize to the same keys: the fp8 selection equals the brute
+    force on the integer keys, ties included."""
+    for seed, palette, qr in [(0, None, 4), (1, 8, 2), (2, 3, 1)]:
+        args = integer_problem(seed, PIN_LENGTHS, palette, qr)
+        q, kcache, bt, t2r, sl, qp = args
+        codes, scales = wl.fp8_integer_keys(np.random.default_rng(100 + seed), kcache)
+        assert len(np.unique(scales)) == 5
+        got = orc.select_fp8(q, codes, scales, bt, t2r, sl, qp)
+        want = brute_select_integer(*args)
+        assert np.array_equal(got, want), f"fp8 integer mismatch (seed {seed})"
+
+
+def pin_row_scores_fp8_one_hot(orc):
+    """One-hot queries read a single code back: with head 0 = +1 and head
+    1 = -1 on dimension 7, block i scores exactly float32(s_i * |e4m3(c_i)|)
+    (one of the two ReLUs passes it), for every finite code and arbitrary
+    float32 scales."""
+    table = torch_e4m3_table()
+    finite = np.flatnonzero(~np.isnan(table))
+    n = finite.size                       # 254 codes -> 254 blocks
+    pages = -(-n // 128)
+    rng = np.random.default_rng(17)
+    codes = np.zeros((pages, 128, 1, 128), np.uint8)
+    scales = rng.uniform(0.01, 3.0, size=(pages, 128)).astype(np.float32)
+    b = np.arange(n)
+    codes[b // 128, b % 128, 0, 7] = finite
+    q = np.zeros((1, 4, 128), np.float16)
+    q[0, 0, 7], q[0, 1, 7] = 1.0, -1.0
+    bt = np.arange(pages, dtype=np.int32).reshape(1, pages)
+    t2r, sl, qp = wl.decode_rows([4 * n])
+    got = orc.row_scores_fp8(0, q, codes, scales, bt, t2r, sl, qp)
+    want = (scales[b // 128, b % 128].astype(np.float64) * np.abs(table[finite])).astype(np.float32)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+def pin_select_fp8_gather_and_sort_normal(orc):
+    """Absmax-quantized N(0,1) keys: scores against a numpy float64 gather of
+    the dequantized keys (torch's decoder x scale), selection against
+    lexsort of the float32-rounded scores."""
+    rng = np.random.default_rng(23)
+    lengths = [2900, 517]
+    P = 48
+    kcache = wl.normal_f16(rng, (P, 128, 1, 128))
+    codes, scales = wl.fp8_normal_keys(kcache)
+    bt = wl.block_table_per_row(rng, lengths, P)
+    q = wl.normal_f16(rng, (2, 4, 128))
+    t2r, sl, qp = wl.decode_rows(lengths)
+    table = torch_e4m3_table()
+    out = orc.select_fp8(q, codes, scales, bt, t2r, sl, qp)
+    for r, L in enumerate(lengths):
+        V = L // 4
+        b = np.arange(V)
+        pg, sl_ = bt[r, b // 128], b % 128
+        keys = table[codes[pg, sl_, 0, :]] * scales[pg, sl_][:, None].astype(np.float64)
+        s64 = np.maximum(keys @ q[r].astype(np.float64).T, 0.0).sum(axis=1)
+        got_scores = orc.row_scores_fp8(r, q, codes, scales, bt, t2r, sl, qp)
+        assert np.allclose(got_scores, s64, rtol=1e-6, atol=1e-6)
+        order = np.lexsort((b, -s64.astype(np.float32).astype(np.float64)))
+        n = min(TOPK, V)
+        want = (4 * order[:n, None] + np.arange(4)).reshape(-1)
+        assert np.array_equal(out[r, :4 * n], want)
+        assert np.array_equal(out[r, 4 * n:4 * n + L % 4], 4 * V + np.arange(L % 4))
+
+
 ALL_PINS = [
     pin_half_to_double,
+    pin_e4m3_to_double,
+    pin_select_fp8_integer_equivalence,
+    pin_row_scores_fp8_one_hot,
+    pin_select_fp8_gather_and_sort_normal,
     pin_select_worked_examples,
     pin_select_brute_force_integer,
     pin_select_multirow_requests,

@@ -1,6 +1,6 @@
 """Each planted mistake in the oracle must be caught by at least one pin.
 
-The oracle source carries ten compile-time mutants (a dropped term, a wrong
+The oracle source carries thirteen compile-time mutants (a dropped term, a wrong
 sign, an off-by-one, a transposed operand, ...).  Building each one and
 running the pins shows that the pins constrain every step of the oracle.
 """
@@ -21,6 +21,9 @@ MUTANTS = {
     8: "visible-block rule off by one",
     9: "a hole read as token 0",
     10: "scores ordered ascending",
+    11: "fp8 key scale ignored",
+    12: "e4m3 exponent bias 8",
+    13: "e4m3 subnormal read as normal",
 }
 
 

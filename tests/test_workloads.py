@@ -81,3 +81,27 @@ def test_multi_token_rows_structure():
         pos = w.query_pos[rows]
         assert pos[-1] == w.seq_lens[req] - 1 and np.all(np.diff(pos) == 1)
     assert w.query_pos.dtype == np.int64 and w.token_to_req.dtype == np.int32
+
+
+def test_fp8_key_caches():
+    """e4m3 caches: no NaN codes; the integer re-encoding dequantizes to the
+    same keys exactly; absmax scaling puts each key's largest code at 448."""
+    import torch
+
+    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    w = wl.with_fp8_keys(wl.ties_and_edges(0), integer=True)
+    assert w.name.endswith("_fp8") and w.kcodes.dtype == np.uint8 and w.kscale.dtype == np.float32
+    assert not np.isnan(table[w.kcodes]).any()
+    deq = table[w.kcodes] * w.kscale[:, :, None, None]
+    assert np.array_equal(deq, w.kcache.astype(np.float64))
+    rng = np.random.default_rng(1)
+    k = wl.normal_f16(rng, (4, 128, 1, 128))
+    codes, scales = wl.fp8_normal_keys(k)
+    vals = np.abs(table[codes])
+    assert not np.isnan(vals).any()
+    assert np.all(vals.max(axis=(2, 3)) == 448.0)
+    # round to nearest: within half a step, 2^-4 relative for normals and
+    # 2^-10 x scale absolute in the subnormal range
+    err = np.abs(table[codes] * scales[:, :, None, None] - k.astype(np.float64))
+    bound = np.maximum(np.abs(k.astype(np.float64)) * 2.0 ** -4, scales[:, :, None, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
