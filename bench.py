@@ -8,6 +8,9 @@ Workloads (``--workload``):
   fp16 N(0,1) compressed-key cache (1 GiB) behind random permuted block
   tables, and full-width [128,2051] sparse attention over a 131072-token
   packed fp16 KV cache (128 MiB).
+* long_context_fp8: the long-context batch with its compressed keys
+  absmax-quantized to an e4m3 cache (128 B of codes + one fp32 scale per
+  key, 528 MiB), timed through qsa_decode_step_fp8.
 * multi_token: several query rows per request -- 48 speculative-decode
   requests with 4 draft positions each and 4 chunked-prefill requests with
   16 positions each (R=256), lengths uniform in [8192, 65536], an 8192-page
@@ -42,7 +45,6 @@ if ROOT not in sys.path:
 
 METRIC = "select+sparse-attn decode rows/sec and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-COUNTERS = os.path.join(ROOT, "profiles", "select_long_context_R128_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
                   for f in ("qsa_select.hip", "qsa_launch.h", "qsa_capi.cpp")]
 
@@ -51,12 +53,12 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def select_algorithmic_bytes(seq_lens, query_pos, token_to_req) -> int:
+def select_algorithmic_bytes(seq_lens, query_pos, token_to_req, key_bytes: int = 256) -> int:
     """Bytes the selection must move per launch.  Per request, its compressed
-    keys once (256 B per block visible to its furthest row) and the 4 B
-    block-table entries that map them: rows of one request read the same
-    pages.  Per row, the 1 KiB query, 16 B of row metadata and the 8204 B
-    output row."""
+    keys once (key_bytes per block visible to its furthest row: 256 for fp16
+    keys, 132 for e4m3 codes + scale) and the 4 B block-table entries that
+    map them: rows of one request read the same pages.  Per row, the 1 KiB
+    query, 16 B of row metadata and the 8204 B output row."""
     furthest = {}
     total = 0
     for r in range(len(token_to_req)):
@@ -67,7 +69,7 @@ def select_algorithmic_bytes(seq_lens, query_pos, token_to_req) -> int:
         furthest[req] = max(furthest.get(req, 0), v)
         total += 1024 + 16 + 8204
     for v in furthest.values():
-        total += 256 * v + 4 * (-(-v // 128))
+        total += key_bytes * v + 4 * (-(-v // 128))
     return total
 
 
@@ -88,19 +90,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(launch_bytes: int):
-    """HBM bytes per select launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTERS):
+def stored_traffic(workload: str):
+    """HBM bytes per select launch from the committed counter summary of this
+    workload (profiles/select_<workload>_counters.json), if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"select_{workload}_counters.json")
+    if not os.path.exists(path):
         return None
-    with open(COUNTERS) as f:
+    with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, scale: float, max_seconds: float = 20.0) -> dict:
+def cpu_baseline(w, scale: float, fp8: bool = False, max_seconds: float = 20.0) -> dict:
     """The CPU oracle (single-threaded C, unmodified) on the host cores: the
     whole decode step of the first rows of the same workload, until all rows
     are done or max_seconds of work have been spent."""
@@ -114,7 +118,10 @@ def cpu_baseline(w, scale: float, max_seconds: float = 20.0) -> dict:
     while done < w.rows and time.perf_counter() - t0 < max_seconds:
         r = np.array([done])
         q, kc, bt, t2r, sl, qp = inputs
-        sel = orc.select(q[r], kc, bt, t2r[r], sl, qp[r])
+        if fp8:
+            sel = orc.select_fp8(q[r], w.kcodes, w.kscale, bt, t2r[r], sl, qp[r])
+        else:
+            sel = orc.select(q[r], kc, bt, t2r[r], sl, qp[r])
         att = orc.sparse_attn(w.q_attn[r], w.kv, sel, scale)
         outs.append((sel, att))
         done += 1
@@ -143,7 +150,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=["long_context", "multi_token"], default="long_context")
+    ap.add_argument("--workload", choices=["long_context", "long_context_fp8", "multi_token"],
+                    default="long_context")
     ap.add_argument("--kv-copies", type=int, default=8,
                     help="distinct KV caches the steps rotate over (one per simulated layer)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -170,11 +178,23 @@ def main() -> int:
         return 0
 
     t0 = time.perf_counter()
-    w = wl.long_context(args.seed) if args.workload == "long_context" else wl.multi_token_rows(args.seed)
+    fp8 = args.workload == "long_context_fp8"
+    if args.workload == "multi_token":
+        w = wl.multi_token_rows(args.seed)
+    else:
+        w = wl.long_context(args.seed)
+        if fp8:
+            w = wl.with_fp8_keys(w, integer=False)
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    sel_in = [d(a) for a in w.select_inputs()]
+    if fp8:
+        sel_in = [d(a) for a in w.select_inputs_fp8()]
+        sel_in[1] = sel_in[1].view(torch.float8_e4m3fn)
+        select_fn, decode_fn = qsa.qsa_select_fp8, qsa.qsa_decode_step_fp8
+    else:
+        sel_in = [d(a) for a in w.select_inputs()]
+        select_fn, decode_fn = qsa.qsa_select, qsa.qsa_decode_step
     # Consecutive decode steps of a model read different layers' caches.  The
     # steps here rotate over distinct KV caches (8 x 128 MiB by default, four
     # times the 256 MB Infinity Cache) so that no step finds its KV in the
@@ -199,7 +219,7 @@ def main() -> int:
 
     def step(i):
         k, v = kv_views[i % len(kv_views)]
-        qsa.qsa_decode_step(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
+        decode_fn(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
 
     # warm-up, then exactly K timed decode steps (events only at the ends)
     for i in range(args.warmup):
@@ -221,7 +241,7 @@ def main() -> int:
     for i in range(args.steps):
         k, v = kv_views[i % len(kv_views)]
         events[i][0].record(stream)
-        qsa.qsa_select(*sel_in, out=idx, workspace=sel_ws)
+        select_fn(*sel_in, out=idx, workspace=sel_ws)
         events[i][1].record(stream)
         qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
         events[i][2].record(stream)
@@ -237,13 +257,13 @@ def main() -> int:
 
     got_idx = idx.cpu().numpy()
     got_out = out.cpu().numpy()
-    sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req)
+    sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
+                                         key_bytes=132 if fp8 else 256)
     att_bytes = attn_algorithmic_bytes(got_idx)
     sel_avg_s = float(np.mean(sel_ms)) / 1e3
     att_avg_s = float(np.mean(att_ms)) / 1e3
     achieved = sel_bytes / sel_avg_s / 1e9
-    # the committed counter summary covers the long-context launch only
-    traffic = stored_traffic(sel_bytes) if args.workload == "long_context" else None
+    traffic = stored_traffic(w.name)
     rows_per_s = R / (ms_per_step / 1e3)
     step_gbs = (sel_bytes + att_bytes) / (ms_per_step / 1e3) / 1e9
 
@@ -258,25 +278,28 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)",
+        "dtype": "e4m3 keys x f16 queries, f16 attention" if fp8 else "f16",
+        "data": ("synthetic (seeded N(0,1) keys absmax-quantized to e4m3 with one fp32 scale per "
+                 "key; N(0,1) fp16 queries/KV; random permuted block tables)" if fp8 else
+                 "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)"),
         "config": workload_config(w, len(kv_sets)),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "qsa_select (qsa_select_chunk_kernel + qsa_select_merge_kernel)",
+                     "kernel": ("qsa_select_fp8" if fp8 else "qsa_select") +
+                               " (qsa_select_chunk_kernel + qsa_select_merge_kernel)",
                      "bytes_per_launch": sel_bytes, "avg_launch_ms": round(sel_avg_s * 1e3, 4)},
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
                    "attention_bytes": att_bytes,
                    "attention_gbs": round(att_bytes / att_avg_s / 1e9, 1),
                    "step_gbs": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
-                   "timed_entry_point": "qsa_decode_step",
+                   "timed_entry_point": "qsa_decode_step_fp8" if fp8 else "qsa_decode_step",
                    "stage_timing": "separate pass: qsa_select and qsa_sparse_attn with events "
                                    "between them"},
     }
     if not args.no_cpu_baseline:
-        base = cpu_baseline(w, scale)
+        base = cpu_baseline(w, scale, fp8=fp8)
         outs = base.pop("_outs")
         # the timed configuration's output on the rows the oracle finished
         same = sum(np.array_equal(sel[0], got_idx[i]) for i, (sel, _) in enumerate(outs))

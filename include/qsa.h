@@ -9,6 +9,9 @@
  *   qsa_sparse_attn  fp16 attention over exactly those indices
  *   qsa_decode_step  both, back to back on one stream, indices stay on device
  *
+ * and the same selection over an fp8 e4m3 compressed-key cache
+ * (qsa_select_fp8, qsa_decode_step_fp8).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Tensors are passed as qsa_tensor descriptors: a DEVICE pointer to the
@@ -74,7 +77,9 @@ extern "C" {
 typedef enum {
   QSA_DTYPE_F16 = 1,
   QSA_DTYPE_I32 = 2,
-  QSA_DTYPE_I64 = 3
+  QSA_DTYPE_I64 = 3,
+  QSA_DTYPE_F32 = 4,
+  QSA_DTYPE_E4M3 = 5 /* one byte per element: OCP e4m3 without infinities ("e4m3fn") */
 } qsa_dtype;
 
 typedef enum {
@@ -155,6 +160,30 @@ QSA_API int qsa_select(const qsa_tensor* q, const qsa_tensor* kcache,
                        qsa_stream stream);
 
 /*
+ * qsa_select_fp8 -- qsa_select over an fp8 e4m3 compressed-key cache.  The
+ * page "qsa_cache.py" (vllm qwen4_exp, QSAStateBackend) lists fp8 / fp8_e4m3
+ * among the compressed indexer cache's dtypes, and the fp8 logits calls on
+ * the page "[XPU] Enable multiple key kernels for sparse attention" take the
+ * keys as k_quant with a k_scale; neither fixes the scale layout.  Here
+ * every compressed key carries one fp32 scale:
+ *
+ *   kcache   E4M3 [P,128,1,128] contiguous, 16-byte aligned: the codes.
+ *   kscale   F32 [P,128] contiguous (same P): the scale of each key.
+ *
+ * The key scored for block b is the dequantized vector
+ * kscale[page][slot] * e4m3(kcache[page][slot][0][d]); everything else --
+ * the other arguments, V and T, the order, the output, the workspace
+ * (qsa_select_workspace_bytes) and the error behaviour -- is as for
+ * qsa_select.  Device-side preconditions in addition: scales finite and
+ * >= 0, codes not NaN (0x7F, 0xFF).
+ */
+QSA_API int qsa_select_fp8(const qsa_tensor* q, const qsa_tensor* kcache,
+                           const qsa_tensor* kscale, const qsa_tensor* block_table,
+                           const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                           const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
+                           size_t workspace_bytes, qsa_stream stream);
+
+/*
  * qsa_sparse_attn -- fp16 sparse decode attention over logical indices with
  * holes and duplicates ("Exact contracts", attention).
  *
@@ -197,6 +226,19 @@ QSA_API int qsa_decode_step(const qsa_tensor* q_sel, const qsa_tensor* kcache,
                             const qsa_tensor* v, float softmax_scale,
                             const qsa_tensor* indices, const qsa_tensor* out,
                             void* workspace, size_t workspace_bytes, qsa_stream stream);
+
+/*
+ * qsa_decode_step_fp8 -- qsa_decode_step with the selection of
+ * qsa_select_fp8 (kcache E4M3 codes plus kscale F32 [P,128]).  Workspace:
+ * qsa_decode_step_workspace_bytes.
+ */
+QSA_API int qsa_decode_step_fp8(const qsa_tensor* q_sel, const qsa_tensor* kcache,
+                                const qsa_tensor* kscale, const qsa_tensor* block_table,
+                                const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                                const qsa_tensor* query_pos, const qsa_tensor* q_attn,
+                                const qsa_tensor* k, const qsa_tensor* v, float softmax_scale,
+                                const qsa_tensor* indices, const qsa_tensor* out, void* workspace,
+                                size_t workspace_bytes, qsa_stream stream);
 
 #ifdef __cplusplus
 }

@@ -2,7 +2,7 @@
 and sparse attention over the selected tokens, as hand-written HIP kernels
 for gfx950 behind a small C ABI (``include/qsa.h``).
 
-The three entry points carry the C names; the library is loaded on first
+The entry points carry the C names; the library is loaded on first
 use and there is no fallback path.
 """
 
@@ -16,7 +16,9 @@ from ._binding import (  # noqa: F401
     kv_views,
     library,
     qsa_decode_step,
+    qsa_decode_step_fp8,
     qsa_select,
+    qsa_select_fp8,
     qsa_sparse_attn,
     select_workspace_bytes,
     sparse_attn_workspace_bytes,

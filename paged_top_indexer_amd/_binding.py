@@ -16,7 +16,7 @@ import threading
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libqsa_amd.so")
 
-F16, I32, I64 = 1, 2, 3
+F16, I32, I64, F32, E4M3 = 1, 2, 3, 4, 5
 TOKEN_TOPK, COMPRESS_RATIO, OUT_WIDTH, TOPK_BLOCKS = 2048, 4, 2051, 512
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_DTYPE", 3: "QSA_ERR_SHAPE",
           4: "QSA_ERR_LAYOUT", 5: "QSA_ERR_ALIAS", 6: "QSA_ERR_WORKSPACE",
@@ -74,6 +74,10 @@ def library() -> ctypes.CDLL:
             lib.qsa_sparse_attn.restype = ctypes.c_int
             lib.qsa_decode_step.argtypes = [_P] * 9 + [f32, _P, _P, vp, sz, vp]
             lib.qsa_decode_step.restype = ctypes.c_int
+            lib.qsa_select_fp8.argtypes = [_P] * 8 + [vp, sz, vp]
+            lib.qsa_select_fp8.restype = ctypes.c_int
+            lib.qsa_decode_step_fp8.argtypes = [_P] * 10 + [f32, _P, _P, vp, sz, vp]
+            lib.qsa_decode_step_fp8.restype = ctypes.c_int
             _lib = lib
         return _lib
 
@@ -112,7 +116,8 @@ def _torch():
 
 def _dtype_code(t) -> int:
     torch = _torch()
-    codes = {torch.float16: F16, torch.int32: I32, torch.int64: I64}
+    codes = {torch.float16: F16, torch.int32: I32, torch.int64: I64, torch.float32: F32,
+             torch.float8_e4m3fn: E4M3}
     return codes.get(t.dtype, 0)
 
 
@@ -178,6 +183,24 @@ def qsa_select(q, kcache, block_table, token_to_req, seq_lens, query_pos, out=No
     return out
 
 
+def qsa_select_fp8(q, kcache, kscale, block_table, token_to_req, seq_lens, query_pos, out=None,
+                   workspace=None, stream=None):
+    """Selection over an e4m3 key cache (kcache torch.float8_e4m3fn
+    [P,128,1,128], kscale float32 [P,128]); returns out ([R,2051] int32)."""
+    torch = _torch()
+    lib = library()
+    R = q.shape[0]
+    if out is None:
+        out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
+    sh = _stream(stream, q.device)
+    need = select_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
+    ws, ws_bytes = _ws_args(need, q.device, sh, workspace, "select")
+    descs = [tensor_desc(t) for t in (q, kcache, kscale, block_table, token_to_req, seq_lens,
+                                      query_pos, out)]
+    check(lib.qsa_select_fp8(*[ctypes.byref(d) for d in descs], ws, ws_bytes, ctypes.c_void_p(sh)))
+    return out
+
+
 def qsa_sparse_attn(q, k, v, indices, softmax_scale: float, out=None, workspace=None, stream=None):
     """Sparse attention over index rows; returns out ([R,3,256] fp16)."""
     torch = _torch()
@@ -213,4 +236,28 @@ def qsa_decode_step(q_sel, kcache, block_table, token_to_req, seq_lens, query_po
     check(lib.qsa_decode_step(*[ctypes.byref(d) for d in first], ctypes.c_float(softmax_scale),
                               ctypes.byref(idd), ctypes.byref(od), ws, ws_bytes,
                               ctypes.c_void_p(sh)))
+    return indices, out
+
+
+def qsa_decode_step_fp8(q_sel, kcache, kscale, block_table, token_to_req, seq_lens, query_pos,
+                        q_attn, k, v, softmax_scale: float, indices=None, out=None,
+                        workspace=None, stream=None):
+    """qsa_decode_step with the e4m3 key cache of qsa_select_fp8; returns
+    (indices, out)."""
+    torch = _torch()
+    lib = library()
+    R = q_sel.shape[0]
+    if indices is None:
+        indices = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q_sel.device)
+    if out is None:
+        out = torch.empty((R, 3, 256), dtype=torch.float16, device=q_sel.device)
+    sh = _stream(stream, q_sel.device)
+    need = decode_step_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
+    ws, ws_bytes = _ws_args(need, q_sel.device, sh, workspace, "decode")
+    first = [tensor_desc(t) for t in (q_sel, kcache, kscale, block_table, token_to_req, seq_lens,
+                                      query_pos, q_attn, k, v)]
+    idd, od = tensor_desc(indices), tensor_desc(out)
+    check(lib.qsa_decode_step_fp8(*[ctypes.byref(d) for d in first], ctypes.c_float(softmax_scale),
+                                  ctypes.byref(idd), ctypes.byref(od), ws, ws_bytes,
+                                  ctypes.c_void_p(sh)))
     return indices, out

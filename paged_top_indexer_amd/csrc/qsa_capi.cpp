@@ -33,6 +33,8 @@ int64_t elem_size(int32_t dtype) {
     case QSA_DTYPE_F16: return 2;
     case QSA_DTYPE_I32: return 4;
     case QSA_DTYPE_I64: return 8;
+    case QSA_DTYPE_F32: return 4;
+    case QSA_DTYPE_E4M3: return 1;
     default: return 0;
   }
 }
@@ -42,6 +44,8 @@ const char* dtype_name(int32_t dtype) {
     case QSA_DTYPE_F16: return "f16";
     case QSA_DTYPE_I32: return "i32";
     case QSA_DTYPE_I64: return "i64";
+    case QSA_DTYPE_F32: return "f32";
+    case QSA_DTYPE_E4M3: return "e4m3";
     default: return "unknown";
   }
 }
@@ -116,19 +120,27 @@ struct SelectView {
   int64_t rows = 0, pages = 0, reqs = 0, width = 0, bt_stride = 0;
 };
 
-int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* bt,
-                    const qsa_tensor* t2r, const qsa_tensor* sl, const qsa_tensor* qp,
-                    const qsa_tensor* out, SelectView* v) {
+// kscale == NULL: an fp16 key cache; else an e4m3 cache with per-key scales.
+int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* kscale,
+                    bool e4m3, const qsa_tensor* bt, const qsa_tensor* t2r,
+                    const qsa_tensor* sl, const qsa_tensor* qp, const qsa_tensor* out,
+                    SelectView* v) {
   const int64_t any3[3] = {-1, QSA_SEL_HEADS, QSA_SEL_DIM};
   QSA_TRY(check_tensor("q", q, QSA_DTYPE_F16, 3, any3));
   QSA_TRY(check_contiguous("q", q));
   QSA_TRY(check_aligned("q", q, 16));
   const int64_t R = q->shape[0];
   const int64_t kshape[4] = {-1, QSA_PAGE_SLOTS, 1, QSA_SEL_DIM};
-  QSA_TRY(check_tensor("kcache", kcache, QSA_DTYPE_F16, 4, kshape));
+  QSA_TRY(check_tensor("kcache", kcache, e4m3 ? QSA_DTYPE_E4M3 : QSA_DTYPE_F16, 4, kshape));
   QSA_TRY(check_contiguous("kcache", kcache));
   QSA_TRY(check_aligned("kcache", kcache, 16));
   if (kcache->shape[0] < 1) return fail(QSA_ERR_SHAPE, "kcache: needs at least one page");
+  if (e4m3) {
+    const int64_t sshape[2] = {kcache->shape[0], QSA_PAGE_SLOTS};
+    QSA_TRY(check_tensor("kscale", kscale, QSA_DTYPE_F32, 2, sshape));
+    QSA_TRY(check_contiguous("kscale", kscale));
+    QSA_TRY(check_aligned("kscale", kscale, 4));
+  }
   const int64_t bshape[2] = {-1, -1};
   QSA_TRY(check_tensor("block_table", bt, QSA_DTYPE_I32, 2, bshape));
   const int64_t N = bt->shape[0], W = bt->shape[1];
@@ -149,9 +161,10 @@ int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_ten
   if (R > (int64_t)1 << 30) return fail(QSA_ERR_SHAPE, "q: too many rows");
   if (W > ((int64_t)1 << 22)) return fail(QSA_ERR_SHAPE, "block_table: too wide");
   const Span so = span_of(out);
-  const qsa_tensor* ins[6] = {q, kcache, bt, t2r, sl, qp};
-  const char* names[6] = {"q", "kcache", "block_table", "token_to_req", "seq_lens", "query_pos"};
-  for (int i = 0; i < 6; ++i) {
+  const qsa_tensor* ins[7] = {q, kcache, bt, t2r, sl, qp, kscale};
+  const char* names[7] = {"q", "kcache", "block_table", "token_to_req", "seq_lens", "query_pos",
+                          "kscale"};
+  for (int i = 0; i < (e4m3 ? 7 : 6); ++i) {
     if (overlaps(so, span_of(ins[i]))) return fail(QSA_ERR_ALIAS, "out overlaps %s", names[i]);
   }
   v->rows = R;
@@ -293,6 +306,110 @@ AttnPlan plan_attn(int64_t rows) {
 
 }  // namespace qsa
 
+namespace {
+
+void fill_select_args(qsa::SelectArgs& a, const qsa_tensor* q, const qsa_tensor* kcache,
+                      const qsa_tensor* kscale, bool e4m3, const qsa_tensor* block_table,
+                      const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                      const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
+                      const SelectView& v) {
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.kcache = e4m3 ? nullptr : static_cast<const uint16_t*>(kcache->data);
+  a.kcodes = e4m3 ? static_cast<const uint8_t*>(kcache->data) : nullptr;
+  a.kscale = e4m3 ? static_cast<const float*>(kscale->data) : nullptr;
+  a.block_table = static_cast<const int32_t*>(block_table->data);
+  a.token_to_req = static_cast<const int32_t*>(token_to_req->data);
+  a.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  a.query_pos = static_cast<const int64_t*>(query_pos->data);
+  a.out = static_cast<int32_t*>(out->data);
+  a.workspace = workspace;
+  a.rows = v.rows;
+  a.num_pages = v.pages;
+  a.num_reqs = v.reqs;
+  a.table_width = v.width;
+  a.bt_stride = v.bt_stride;
+}
+
+int select_impl(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* kscale,
+                bool e4m3, const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                const qsa_tensor* seq_lens, const qsa_tensor* query_pos, const qsa_tensor* out,
+                void* workspace, size_t workspace_bytes, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  SelectView v;
+  QSA_TRY(validate_select(q, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
+                          query_pos, out, &v));
+  if (v.rows == 0) return QSA_OK;
+  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
+  Span guarded[8] = {span_of(q),        span_of(kcache),   span_of(block_table),
+                     span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
+                     span_of(out),      e4m3 ? span_of(kscale) : Span()};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 8));
+  qsa::SelectArgs a;
+  fill_select_args(a, q, kcache, kscale, e4m3, block_table, token_to_req, seq_lens, query_pos,
+                   out, workspace, v);
+  const int err = qsa::launch_select(a, plan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_tensor* kscale,
+                bool e4m3, const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                const qsa_tensor* seq_lens, const qsa_tensor* query_pos, const qsa_tensor* q_attn,
+                const qsa_tensor* k, const qsa_tensor* v, float softmax_scale,
+                const qsa_tensor* indices, const qsa_tensor* out, void* workspace,
+                size_t workspace_bytes, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  SelectView sv;
+  QSA_TRY(validate_select(q_sel, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
+                          query_pos, indices, &sv));
+  AttnView av;
+  QSA_TRY(validate_attn(q_attn, k, v, indices, softmax_scale, out, true, &av));
+  if (av.rows != sv.rows) return fail(QSA_ERR_SHAPE, "q_attn rows differ from q_sel rows");
+  // the attention output must not overlap any selection input either
+  const qsa_tensor* sel_in[7] = {q_sel, kcache, block_table, token_to_req, seq_lens, query_pos,
+                                 kscale};
+  for (int i = 0; i < (e4m3 ? 7 : 6); ++i) {
+    if (overlaps(span_of(out), span_of(sel_in[i]))) {
+      return fail(QSA_ERR_ALIAS, "out overlaps a selection input");
+    }
+  }
+  if (sv.rows == 0) return QSA_OK;
+  const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width);
+  const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
+  const size_t sel_bytes = align256(splan.bytes);
+  const size_t need = sel_bytes + aplan.bytes;
+  qsa_tensor whole = *k;
+  whole.ndim = 1;
+  whole.shape[0] = av.tokens * 2 * QSA_ATT_DIM;
+  whole.stride[0] = 1;
+  Span guarded[11] = {span_of(q_sel),        span_of(kcache),   span_of(block_table),
+                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
+                      span_of(q_attn),       span_of(&whole),   span_of(indices),
+                      span_of(out),          e4m3 ? span_of(kscale) : Span()};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, need, guarded, 11));
+
+  qsa::SelectArgs s;
+  fill_select_args(s, q_sel, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
+                   query_pos, indices, workspace, sv);
+  int err = qsa::launch_select(s, splan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
+
+  qsa::AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q_attn->data);
+  a.kv = static_cast<const uint16_t*>(k->data);
+  a.indices = static_cast<const int32_t*>(indices->data);
+  a.out = static_cast<uint16_t*>(out->data);
+  a.workspace = aplan.bytes ? static_cast<char*>(workspace) + sel_bytes : nullptr;
+  a.rows = av.rows;
+  a.num_tokens = av.tokens;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  err = qsa::launch_attn(a, aplan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "attention launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 QSA_API const char* qsa_status_string(int status) {
@@ -340,31 +457,17 @@ QSA_API int qsa_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_
                        const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
                        const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
                        size_t workspace_bytes, qsa_stream stream) {
-  g_last_error[0] = '\0';
-  SelectView v;
-  QSA_TRY(validate_select(q, kcache, block_table, token_to_req, seq_lens, query_pos, out, &v));
-  if (v.rows == 0) return QSA_OK;
-  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
-  Span guarded[7] = {span_of(q), span_of(kcache), span_of(block_table), span_of(token_to_req),
-                     span_of(seq_lens), span_of(query_pos), span_of(out)};
-  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 7));
-  qsa::SelectArgs a;
-  a.q = static_cast<const uint16_t*>(q->data);
-  a.kcache = static_cast<const uint16_t*>(kcache->data);
-  a.block_table = static_cast<const int32_t*>(block_table->data);
-  a.token_to_req = static_cast<const int32_t*>(token_to_req->data);
-  a.seq_lens = static_cast<const int32_t*>(seq_lens->data);
-  a.query_pos = static_cast<const int64_t*>(query_pos->data);
-  a.out = static_cast<int32_t*>(out->data);
-  a.workspace = workspace;
-  a.rows = v.rows;
-  a.num_pages = v.pages;
-  a.num_reqs = v.reqs;
-  a.table_width = v.width;
-  a.bt_stride = v.bt_stride;
-  const int err = qsa::launch_select(a, plan, stream);
-  if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
-  return QSA_OK;
+  return select_impl(q, kcache, nullptr, false, block_table, token_to_req, seq_lens, query_pos,
+                     out, workspace, workspace_bytes, stream);
+}
+
+QSA_API int qsa_select_fp8(const qsa_tensor* q, const qsa_tensor* kcache,
+                           const qsa_tensor* kscale, const qsa_tensor* block_table,
+                           const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                           const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
+                           size_t workspace_bytes, qsa_stream stream) {
+  return select_impl(q, kcache, kscale, true, block_table, token_to_req, seq_lens, query_pos, out,
+                     workspace, workspace_bytes, stream);
 }
 
 QSA_API int qsa_sparse_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_tensor* v,
@@ -401,63 +504,20 @@ QSA_API int qsa_decode_step(const qsa_tensor* q_sel, const qsa_tensor* kcache,
                             const qsa_tensor* q_attn, const qsa_tensor* k, const qsa_tensor* v,
                             float softmax_scale, const qsa_tensor* indices, const qsa_tensor* out,
                             void* workspace, size_t workspace_bytes, qsa_stream stream) {
-  g_last_error[0] = '\0';
-  SelectView sv;
-  QSA_TRY(validate_select(q_sel, kcache, block_table, token_to_req, seq_lens, query_pos, indices, &sv));
-  AttnView av;
-  QSA_TRY(validate_attn(q_attn, k, v, indices, softmax_scale, out, true, &av));
-  if (av.rows != sv.rows) return fail(QSA_ERR_SHAPE, "q_attn rows differ from q_sel rows");
-  // the attention output must not overlap any selection input either
-  const qsa_tensor* sel_in[6] = {q_sel, kcache, block_table, token_to_req, seq_lens, query_pos};
-  for (int i = 0; i < 6; ++i) {
-    if (overlaps(span_of(out), span_of(sel_in[i]))) {
-      return fail(QSA_ERR_ALIAS, "out overlaps a selection input");
-    }
-  }
-  if (sv.rows == 0) return QSA_OK;
-  const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width);
-  const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
-  const size_t sel_bytes = align256(splan.bytes);
-  const size_t need = sel_bytes + aplan.bytes;
-  qsa_tensor whole = *k;
-  whole.ndim = 1;
-  whole.shape[0] = av.tokens * 2 * QSA_ATT_DIM;
-  whole.stride[0] = 1;
-  Span guarded[10] = {span_of(q_sel),     span_of(kcache),       span_of(block_table),
-                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
-                      span_of(q_attn),    span_of(&whole),       span_of(indices),
-                      span_of(out)};
-  QSA_TRY(check_workspace(workspace, workspace_bytes, need, guarded, 10));
+  return decode_impl(q_sel, kcache, nullptr, false, block_table, token_to_req, seq_lens,
+                     query_pos, q_attn, k, v, softmax_scale, indices, out, workspace,
+                     workspace_bytes, stream);
+}
 
-  qsa::SelectArgs s;
-  s.q = static_cast<const uint16_t*>(q_sel->data);
-  s.kcache = static_cast<const uint16_t*>(kcache->data);
-  s.block_table = static_cast<const int32_t*>(block_table->data);
-  s.token_to_req = static_cast<const int32_t*>(token_to_req->data);
-  s.seq_lens = static_cast<const int32_t*>(seq_lens->data);
-  s.query_pos = static_cast<const int64_t*>(query_pos->data);
-  s.out = static_cast<int32_t*>(indices->data);
-  s.workspace = workspace;
-  s.rows = sv.rows;
-  s.num_pages = sv.pages;
-  s.num_reqs = sv.reqs;
-  s.table_width = sv.width;
-  s.bt_stride = sv.bt_stride;
-  int err = qsa::launch_select(s, splan, stream);
-  if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
-
-  qsa::AttnArgs a;
-  a.q = static_cast<const uint16_t*>(q_attn->data);
-  a.kv = static_cast<const uint16_t*>(k->data);
-  a.indices = static_cast<const int32_t*>(indices->data);
-  a.out = static_cast<uint16_t*>(out->data);
-  a.workspace = aplan.bytes ? static_cast<char*>(workspace) + sel_bytes : nullptr;
-  a.rows = av.rows;
-  a.num_tokens = av.tokens;
-  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
-  err = qsa::launch_attn(a, aplan, stream);
-  if (err) return fail(QSA_ERR_LAUNCH, "attention launch failed (hipError %d)", err);
-  return QSA_OK;
+QSA_API int qsa_decode_step_fp8(const qsa_tensor* q_sel, const qsa_tensor* kcache,
+                                const qsa_tensor* kscale, const qsa_tensor* block_table,
+                                const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                                const qsa_tensor* query_pos, const qsa_tensor* q_attn,
+                                const qsa_tensor* k, const qsa_tensor* v, float softmax_scale,
+                                const qsa_tensor* indices, const qsa_tensor* out, void* workspace,
+                                size_t workspace_bytes, qsa_stream stream) {
+  return decode_impl(q_sel, kcache, kscale, true, block_table, token_to_req, seq_lens, query_pos,
+                     q_attn, k, v, softmax_scale, indices, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

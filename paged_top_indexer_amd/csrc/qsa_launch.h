@@ -50,7 +50,9 @@ AttnPlan plan_attn(int64_t rows);
 
 struct SelectArgs {
   const uint16_t* q;          // [R,4,128] fp16
-  const uint16_t* kcache;     // [P,128,1,128] fp16
+  const uint16_t* kcache;     // [P,128,1,128] fp16 keys (NULL for an e4m3 cache)
+  const uint8_t* kcodes = nullptr;  // [P,128,1,128] e4m3 codes, with
+  const float* kscale = nullptr;    // [P,128] per-key scales (non-NULL selects e4m3)
   const int32_t* block_table; // [N, >=W], row stride bt_stride
   const int32_t* token_to_req;
   const int32_t* seq_lens;

@@ -13,6 +13,13 @@
 //    pages (128 compressed keys of 256 B each per page, one contiguous
 //    32 KiB run).  Workgroups whose chunk lies past the row's visible blocks
 //    exit at once.
+//  * Key caches: fp16 keys (256 B each), or e4m3 codes (128 B each) with one
+//    fp32 scale per key.  An e4m3 code becomes the binary16 pattern of
+//    code * 2^-8 by moving its sign to bit 15 and its 7 exponent+fraction
+//    bits to bits 7..13 (the biases 7 and 15 differ by 8; subnormals map
+//    onto subnormals), so the same fp16 MFMA scores both; the factor 2^8 is
+//    folded into the key's scale, which multiplies the head sum (a scale is
+//    >= 0, so scale * sum ReLU(q.k) = sum ReLU(q.(scale k))).
 //  * Scoring: each wave scores tiles of 16 keys with
 //    v_mfma_f32_16x16x32_f16: A = the 4 query heads (rows 4..15 zero),
 //    B = 16 keys.  Lane l loads key (l % 16), bytes [64c + 16(l/16), +16)
@@ -49,7 +56,6 @@ constexpr int kChunkThreads = 256;
 constexpr int kMergeThreads = 256;
 constexpr int kMaxChunkPages = 32;
 constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
-constexpr int kUnroll = 4;        // tiles in flight per wave
 constexpr int kBins = 2048;       // radix digit of up to 11 bits
 constexpr int kMergeList = 8192 + kTopKBlocks;  // LDS list of the merge
 
@@ -59,7 +65,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct SelectParams {
   const uint16_t* q;
-  const uint16_t* kcache;
+  const uint16_t* kcache;  // fp16 keys, or
+  const uint8_t* kcodes;   // e4m3 codes [P,128,1,128] with
+  const float* kscale;     // one scale per key [P,128]
   const int32_t* block_table;
   const int32_t* token_to_req;
   const int32_t* seq_lens;
@@ -426,9 +434,11 @@ struct ChunkSmem {
   alignas(16) uint32_t hist0[kBins];  // counted while scoring
   union {
     // scoring: one 16-key tile per wave, 16-byte chunk j of key n stored at
-    // [n][j ^ n] so that both the coalesced write and the MFMA-layout read
-    // touch 16 distinct bank groups
+    // [n][j ^ n] (fp16: 16 chunks per key) or [n][j ^ (n & 7)] (e4m3: 8
+    // chunks per key), so that both the coalesced write and the
+    // MFMA-layout read touch distinct bank groups
     u32x4 stage[kChunkWaves][16][16];
+    u32x4 stage8[kChunkWaves][16][8];
     // selection (after scoring)
     struct {
       alignas(16) uint32_t hist1[kBins];
@@ -438,25 +448,65 @@ struct ChunkSmem {
   } u;
 };
 
-__global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectParams p) {
-  __shared__ ChunkSmem sm;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t r = blockIdx.x / p.chunks_per_row;
-  const int64_t chunk = blockIdx.x % p.chunks_per_row;
-  if (r >= p.rows) return;
-  const Row row = row_setup(p, r);
-  if (chunk >= row.nchunks) return;
-  const int64_t chunk_base = chunk * p.chunk_blocks;
-  const int nblk = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
-  const bool select = nblk > kTopKBlocks;
-  if (select) {
-    for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
-    __syncthreads();
-  }
+// Where a chunk's scores go: order-preserving keys in LDS (a score is >= 0:
+// its bit pattern with the sign cleared orders like the value and maps -0
+// onto +0), plus the first radix histogram when the chunk needs a select.
+__device__ __forceinline__ void store_score(ChunkSmem& sm, int i, float sc, bool select) {
+  const uint32_t key = __float_as_uint(sc) & 0x7FFFFFFFu;
+  sm.keys[i] = key;
+  if (select) atomicAdd(&sm.hist0[digit0(key)], 1u);
+}
 
-  // ---- scoring (MFMA) ----------------------------------------------------
+// The physical pages of a chunk (at most 32): lane i holds the page of the
+// chunk's i-th logical page, or 0 when the table names a page outside
+// [0, P) (an unmet precondition: such a page reads as an all-zero key, see
+// the valid mask).  A tile's page is then a readlane away, so no load in
+// the scoring loop waits on another load.
+__device__ __forceinline__ int32_t chunk_pages(const SelectParams& p, int64_t req,
+                                               int64_t chunk_base, int nblk, int lane,
+                                               bool* valid) {
+  const int npages = (nblk + kPageSlots - 1) / kPageSlots;
+  int32_t page = 0;
+  *valid = false;
+  if (lane < npages) {
+    const int64_t pg = p.block_table[req * p.bt_stride + (chunk_base / kPageSlots) + lane];
+    *valid = pg >= 0 && pg < p.num_pages;
+    page = *valid ? (int32_t)pg : 0;
+  }
+  return page;
+}
+
+// Key loads go through a buffer resource spanning one cache page: an offset
+// at or past the page's size returns zeros without touching memory.  Keys
+// past the chunk's end, tiles past the wave's last one and pages outside
+// [0, P) all use such an offset, so every load is unconditional
+// (straight-line code: each tile waits only for its own loads) and costs no
+// traffic when it is not needed.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+constexpr int kNontemporal = 2;           // cache policy: nt
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferWord3);
+}
+
+// Keys of tile t (16 blocks from 16t) that exist: 0 when t is past the
+// chunk's last tile (tt = the clamped tile) or its page is invalid.
+__device__ __forceinline__ int tile_keys(int t, int tt, int ntiles, int nblk, uint64_t valid_mask) {
+  const int on_page = (int)((valid_mask >> (tt >> 3)) & 1);
+  const int in_chunk = t < ntiles ? min(16, nblk - 16 * tt) : 0;
+  return in_chunk * on_page;
+}
+
+// fp16 keys.  MFMA k step c covers dims [32c, 32c + 32): lane (n + 16g)
+// holds dims [32c + 8g, +8) of key n (B) or of head n (A).
+__device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem& sm, int64_t r,
+                                                int64_t req, int64_t chunk_base, int nblk,
+                                                bool select) {
+  constexpr int kUnroll = 4;  // tiles in flight per wave (4 KiB each)
+  constexpr int kPageBytes = kPageSlots * kSelDim * 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // key column of B / head row of A
   const int g = lane >> 4;  // 8-element slice of each 32-wide k step
   half8 qa[4];
@@ -467,45 +517,61 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
       qa[c] = *reinterpret_cast<const half8*>(p.q + (r * kSelHeads + n) * kSelDim + 32 * c + 8 * g);
     }
   }
-  const int32_t* bt_row = p.block_table + row.req * p.bt_stride;
+  bool page_valid;
+  const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
+  const uint64_t valid_mask = __ballot(page_valid);
   const int ntiles = (nblk + 15) >> 4;
+  if (wave >= ntiles) return;
   u32x4(*stage)[16] = sm.u.stage[wave];
   const int s16 = lane & 15;  // 16-byte chunk of a key this lane loads
+
+  // Coalesced nontemporal loads: instruction c reads keys 4c..4c+3 of a
+  // tile (1 KiB contiguous), lane l taking chunk l % 16 of key 4c + l / 16.
+  // Keys are read exactly once; nontemporal loads stream page-permuted
+  // reads at the linear-read rate.
+  u32x4 raw[kUnroll][4];
+  auto issue = [&](int u, int t) {
+    // keys of tile t that exist (0 past the wave's last tile or on an
+    // invalid page); an integer, so that the compiler keeps one code path
+    const int tt = min(t, ntiles - 1);
+    const int live = tile_keys(t, tt, ntiles, nblk, valid_mask);
+    const int32_t page = __builtin_amdgcn_readlane(pages, tt >> 3);  // 8 tiles per page
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kcache + (int64_t)page * kPageSlots * kSelDim,
+                                                kPageBytes);
+    const uint32_t off = (uint32_t)((16 * tt) & (kPageSlots - 1)) * (kSelDim * 2) + lane * 16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool ok = 4 * c + g < live;
+      raw[u][c] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, ok ? off + 1024 * c : kOutOfRange, 0,
+                                                       kNontemporal));
+    }
+  };
+  // Rolling pipeline: slot u holds tile t0 + 4u; once it is scored, the slot
+  // is refilled with the tile kUnroll slots ahead, so kUnroll tiles stay in
+  // flight while the wave computes.  Every slot is scored on every pass (a
+  // slot past the last tile holds zeros and stores nothing): a loop without
+  // side exits, so each tile waits only for its own loads.
+  // (the scheduling barriers keep the slots' loads in slot order, which the
+  // per-tile waits rely on)
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    issue(u, wave + u * kChunkWaves);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll 1
   for (int t0 = wave; t0 < ntiles; t0 += kChunkWaves * kUnroll) {
-    // Coalesced nontemporal loads: instruction c reads keys 4c..4c+3 of the
-    // tile (1 KiB contiguous), lane l taking chunk l % 16 of key 4c + l / 16.
-    // Keys are read exactly once; nontemporal loads stream page-permuted
-    // reads at the linear-read rate.
-    u32x4 raw[kUnroll][4];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = t0 + u * kChunkWaves;
-      bool page_ok = false;
-      const u32x4* kp = nullptr;
-      if (t < ntiles) {
-        const int64_t b0 = chunk_base + 16 * t;  // 16-aligned: one page per tile
-        const int64_t page = bt_row[b0 >> 7];
-        page_ok = page >= 0 && page < p.num_pages;
-        kp = reinterpret_cast<const u32x4*>(p.kcache + (page * kPageSlots + (b0 & (kPageSlots - 1))) *
-                                                           kSelDim) + lane;
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool ok = page_ok && 16 * t + 4 * c + g < nblk;
-        raw[u][c] = ok ? __builtin_nontemporal_load(kp + 64 * c) : u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kChunkWaves;
-      if (t >= ntiles) break;
       // transpose through the wave's LDS tile
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int key = 4 * c + g;
         stage[key][s16 ^ key] = raw[u][c];
       }
+      issue(u, t + kChunkWaves * kUnroll);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_wave_barrier();
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -518,12 +584,149 @@ __global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectP
       // lanes 0..15 hold heads 0..3 of key n
       const float sc = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) +
                        fmaxf(acc[3], 0.f);
-      if (g == 0 && 16 * t + n < nblk) {
-        const uint32_t key = __float_as_uint(sc) & 0x7FFFFFFFu;
-        sm.keys[16 * t + n] = key;
-        if (select) atomicAdd(&sm.hist0[digit0(key)], 1u);
-      }
+      if (g == 0 && 16 * t + n < nblk) store_score(sm, 16 * t + n, sc, select);
     }
+  }
+}
+
+// Two e4m3 codes (bytes 0,1 of w when hi is false, bytes 2,3 when true) as
+// two binary16 patterns of code * 2^-8.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w, bool hi) {
+  // z: first code in byte 1, second code in byte 3
+  const uint32_t z = hi ? (((w >> 8) & 0x0000FF00u) | (w & 0xFF000000u))
+                        : (((w & 0x000000FFu) << 8) | ((w & 0x0000FF00u) << 16));
+  return (z & 0x80008000u) | ((z >> 1) & 0x3F803F80u);
+}
+
+__device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
+  u32x4 h = {e4m3x2_to_f16x2(w0, false), e4m3x2_to_f16x2(w0, true), e4m3x2_to_f16x2(w1, false),
+             e4m3x2_to_f16x2(w1, true)};
+  return __builtin_bit_cast(half8, h);
+}
+
+// e4m3 keys.  The dot product does not care in which order the k steps
+// visit the 128 dims, so each lane takes 32 contiguous bytes of its key:
+// MFMA k step c gives lane (n + 16g) dims [32g + 8c, +8) of key n (B) or of
+// head n (A).
+__device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm, int64_t r,
+                                                 int64_t req, int64_t chunk_base, int nblk,
+                                                 bool select) {
+  constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each)
+  constexpr int kPageBytes = kPageSlots * kSelDim;
+  constexpr int kScaleBytes = kPageSlots * 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  half8 qa[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qa[c] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (n < kSelHeads) {
+      qa[c] = *reinterpret_cast<const half8*>(p.q + (r * kSelHeads + n) * kSelDim + 32 * g + 8 * c);
+    }
+  }
+  bool page_valid;
+  const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
+  const uint64_t valid_mask = __ballot(page_valid);
+  const int ntiles = (nblk + 15) >> 4;
+  if (wave >= ntiles) return;
+  u32x4(*stage)[8] = sm.u.stage8[wave];
+  const int s8 = lane & 7;     // 16-byte chunk of a key this lane loads
+  const int k8 = lane >> 3;    // key of the 8-key half tile this lane loads
+
+  // Coalesced nontemporal loads: instruction c reads keys 8c..8c+7 of a
+  // tile (1 KiB contiguous), lane l taking chunk l % 8 of key 8c + l / 8;
+  // every lane also reads the scale of key l % 16 (64 bytes per tile).
+  u32x4 raw[kUnroll][2];
+  float scale[kUnroll];
+  auto issue_keys = [&](int u, int t) {
+    const int tt = min(t, ntiles - 1);
+    const int live = tile_keys(t, tt, ntiles, nblk, valid_mask);
+    const int32_t page = __builtin_amdgcn_readlane(pages, tt >> 3);
+    const __amdgpu_buffer_rsrc_t rk = page_rsrc(p.kcodes + (int64_t)page * kPageSlots * kSelDim,
+                                                kPageBytes);
+    const uint32_t off = (uint32_t)((16 * tt) & (kPageSlots - 1)) * kSelDim + lane * 16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool ok = 8 * c + k8 < live;
+      raw[u][c] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ok ? off + 1024 * c : kOutOfRange, 0,
+                                                       kNontemporal));
+    }
+  };
+  auto issue_scale = [&](int u, int t) {
+    const int tt = min(t, ntiles - 1);
+    const int live = tile_keys(t, tt, ntiles, nblk, valid_mask);
+    const int32_t page = __builtin_amdgcn_readlane(pages, tt >> 3);
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kscale + (int64_t)page * kPageSlots, kScaleBytes);
+    const uint32_t off = (uint32_t)(((16 * tt) & (kPageSlots - 1)) + n) * 4;
+    scale[u] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rs, n < live ? off : kOutOfRange, 0,
+                                                    kNontemporal));
+  };
+  // Rolling pipeline, as in the fp16 scorer; a slot's scale is refilled
+  // only once its score is stored, so the old and new scale never need two
+  // registers (the scheduling barriers keep the loads in the order the
+  // per-tile waits rely on).
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    issue_keys(u, wave + u * kChunkWaves);
+    issue_scale(u, wave + u * kChunkWaves);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll 1
+  for (int t0 = wave; t0 < ntiles; t0 += kChunkWaves * kUnroll) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = t0 + u * kChunkWaves;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int key = 8 * c + k8;
+        stage[key][s8 ^ (key & 7)] = raw[u][c];
+      }
+      issue_keys(u, t + kChunkWaves * kUnroll);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_wave_barrier();
+      const u32x4 lo = stage[n][(2 * g) ^ (n & 7)];      // dims [32g, 32g + 16)
+      const u32x4 hi = stage[n][(2 * g + 1) ^ (n & 7)];  // dims [32g + 16, 32g + 32)
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[0], e4m3x8_to_half8(lo[0], lo[1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[1], e4m3x8_to_half8(lo[2], lo[3]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[2], e4m3x8_to_half8(hi[0], hi[1]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[3], e4m3x8_to_half8(hi[2], hi[3]), acc, 0, 0, 0);
+      __builtin_amdgcn_wave_barrier();
+      const float sum = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) +
+                        fmaxf(acc[3], 0.f);
+      // scale * 2^8 is exact, so this is one rounding of scale * code-sum
+      const float sc = sum * (scale[u] * 256.f);
+      if (g == 0 && 16 * t + n < nblk) store_score(sm, 16 * t + n, sc, select);
+      issue_scale(u, t + kChunkWaves * kUnroll);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <bool kE4M3>
+__global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectParams p) {
+  __shared__ ChunkSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x / p.chunks_per_row;
+  const int64_t chunk = blockIdx.x % p.chunks_per_row;
+  if (r >= p.rows) return;
+  const Row row = row_setup(p, r);
+  if (chunk >= row.nchunks) return;
+  const int64_t chunk_base = chunk * p.chunk_blocks;
+  const int nblk = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
+  const bool select = nblk > kTopKBlocks;
+  if (select) {
+    for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
+    __syncthreads();
+  }
+  if (kE4M3) {
+    score_chunk_e4m3(p, sm, r, row.req, chunk_base, nblk, select);
+  } else {
+    score_chunk_f16(p, sm, r, row.req, chunk_base, nblk, select);
   }
   __syncthreads();
 
@@ -669,6 +872,8 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
   SelectParams p;
   p.q = a.q;
   p.kcache = a.kcache;
+  p.kcodes = a.kcodes;
+  p.kscale = a.kscale;
   p.block_table = a.block_table;
   p.token_to_req = a.token_to_req;
   p.seq_lens = a.seq_lens;
@@ -686,8 +891,13 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
   p.chunk_blocks = plan.chunk_pages * kPageSlots;
   p.cand_cap = (int)plan.cand_cap;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(qsa_select_chunk_kernel, dim3((unsigned)(a.rows * plan.chunks_per_row)),
-                     dim3(kChunkThreads), 0, s, p);
+  if (a.kscale) {
+    hipLaunchKernelGGL(qsa_select_chunk_kernel<true>, dim3((unsigned)(a.rows * plan.chunks_per_row)),
+                       dim3(kChunkThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(qsa_select_chunk_kernel<false>, dim3((unsigned)(a.rows * plan.chunks_per_row)),
+                       dim3(kChunkThreads), 0, s, p);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.chunks_per_row == 1) return (int)err;
   hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, p);

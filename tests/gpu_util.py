@@ -39,6 +39,18 @@ def select_gpu(q, kcache, bt, t2r, sl, qp) -> np.ndarray:
     return out.cpu().numpy()
 
 
+def dev_e4m3(codes: np.ndarray) -> torch.Tensor:
+    """uint8 e4m3 codes as a float8_e4m3fn device tensor (same bytes)."""
+    return dev(codes.astype(np.uint8)).view(torch.float8_e4m3fn)
+
+
+def select_gpu_fp8(q, codes, scales, bt, t2r, sl, qp) -> np.ndarray:
+    out = qsa.qsa_select_fp8(dev(q), dev_e4m3(codes), dev(scales), dev(bt), dev(t2r), dev(sl),
+                             dev(qp))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
 def attn_gpu(q, kv, idx, scale) -> np.ndarray:
     kvd = dev(kv.reshape(-1, 512, 512))
     k, v = qsa.kv_views(kvd)
@@ -60,8 +72,14 @@ def check_attn(got16: np.ndarray, want64: np.ndarray, what: str = "") -> float:
 
 def check_select_band(gpu: np.ndarray, ref: np.ndarray, orc, inputs, rows) -> None:
     """The N(0,1) acceptance rule on the listed rows (inputs as passed to the
-    oracle, rows as indices into them)."""
-    q, kcache, bt, t2r, sl, qp = inputs
+    oracle -- six for an fp16 cache, seven with codes and scales for an e4m3
+    cache -- and rows as indices into them)."""
+    if len(inputs) == 7:
+        q, codes, scales, bt, t2r, sl, qp = inputs
+        row_scores = lambda r: orc.row_scores_fp8(r, *inputs)  # noqa: E731
+    else:
+        q, kcache, bt, t2r, sl, qp = inputs
+        row_scores = lambda r: orc.row_scores(r, *inputs)  # noqa: E731
     for r in rows:
         g, o = gpu[r], ref[r]
         V, T = orc.row_extent(int(sl[t2r[r]]), int(qp[r]))
@@ -77,7 +95,7 @@ def check_select_band(gpu: np.ndarray, ref: np.ndarray, orc, inputs, rows) -> No
         assert len(np.unique(bg)) == n and np.all(bg < V) and np.all(bg >= 0), f"row {r}: blocks"
         if n == 0:
             continue
-        scores = orc.row_scores(r, q, kcache, bt, t2r, sl, qp).astype(np.float64)
+        scores = row_scores(r).astype(np.float64)
         s_n = scores[bo[-1]]
         band = BAND * max(abs(s_n), 1.0)
         diff = np.setxor1d(bg, bo)
@@ -89,10 +107,11 @@ def check_select_band(gpu: np.ndarray, ref: np.ndarray, orc, inputs, rows) -> No
 
 
 def subset_rows(inputs, rows):
-    """Selection inputs restricted to some query rows (requests unchanged)."""
-    q, kcache, bt, t2r, sl, qp = inputs
+    """Selection inputs restricted to some query rows (requests unchanged);
+    six (fp16 cache) or seven (e4m3 codes + scales) inputs."""
     rows = np.asarray(rows)
-    return (q[rows], kcache, bt, t2r[rows], sl, qp[rows])
+    q, *cache, bt, t2r, sl, qp = inputs
+    return (q[rows], *cache, bt, t2r[rows], sl, qp[rows])
 
 
 def orc():

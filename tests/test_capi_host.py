@@ -227,11 +227,87 @@ def test_decode_step_checks():
 
 
 def test_torch_descriptor_dtype_refused():
-    """A float32 tensor gets dtype code 0 from the binding and the library
-    refuses it; the binding turns the status into RuntimeError."""
+    """A float32 query is refused by the library; the binding turns the
+    status into RuntimeError."""
     import torch
     q = torch.zeros((1, 4, 128), dtype=torch.float32)
     f, a, ws, wsb = select_args(R=1)
     a["q"] = B.tensor_desc(q)
     with pytest.raises(RuntimeError, match="QSA_ERR_DTYPE"):
         B.check(call_select(a, ws, wsb))
+
+
+# ---------------------------------------------------------------------------
+# e4m3 key cache entry points
+
+def fp8_args(R=4, P=8, N=4, W=40):
+    f, a, ws, wsb = select_args(R=R, P=P, N=N, W=W)
+    a["kcache"] = mk(f, B.E4M3, (P, 128, 1, 128), 1)
+    a["kscale"] = mk(f, B.F32, (P, 128), 4)
+    return f, a, ws, wsb
+
+
+def call_select_fp8(a, ws, ws_bytes):
+    lib = B.library()
+    order = ["q", "kcache", "kscale", "bt", "t2r", "sl", "qp", "out"]
+    ptrs = [ctypes.byref(a[k]) if a[k] is not None else None for k in order]
+    return lib.qsa_select_fp8(*ptrs, ctypes.c_void_p(ws), ws_bytes, None)
+
+
+FP8_CASES = {
+    "kcache_f16": (lambda f, a: a.__setitem__("kcache", mk(f, B.F16, (8, 128, 1, 128), 2)), DTYPE),
+    "kcache_misaligned": (lambda f, a: a.__setitem__("kcache", mk(f, B.E4M3, (8, 128, 1, 128), 1, ptr=f.alloc(1 << 17) + 8)), LAYOUT),
+    "kcache_strided": (lambda f, a: a.__setitem__("kcache", mk(f, B.E4M3, (8, 128, 1, 128), 1, stride=(32768, 256, 128, 1))), LAYOUT),
+    "kscale_f16": (lambda f, a: a.__setitem__("kscale", mk(f, B.F16, (8, 128), 2)), DTYPE),
+    "kscale_pages": (lambda f, a: a.__setitem__("kscale", mk(f, B.F32, (7, 128), 4)), SHAPE),
+    "kscale_slots": (lambda f, a: a.__setitem__("kscale", mk(f, B.F32, (8, 64), 4)), SHAPE),
+    "kscale_rank": (lambda f, a: a.__setitem__("kscale", mk(f, B.F32, (8 * 128,), 4)), SHAPE),
+    "kscale_strided": (lambda f, a: a.__setitem__("kscale", mk(f, B.F32, (8, 128), 4, stride=(256, 1))), LAYOUT),
+    "kscale_misaligned": (lambda f, a: a.__setitem__("kscale", mk(f, B.F32, (8, 128), 4, ptr=f.alloc(8192) + 2)), LAYOUT),
+    "kscale_null": (lambda f, a: a.__setitem__("kscale", None), NULL),
+    "out_aliases_kscale": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2051), 4, ptr=a["kscale"].data)), ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FP8_CASES))
+def test_select_fp8_fail_closed(case):
+    mutate, want = FP8_CASES[case]
+    f, a, ws, wsb = fp8_args()
+    mutate(f, a)
+    rc = call_select_fp8(a, ws, wsb)
+    assert rc == want, (rc, B.library().qsa_last_error())
+    assert B.library().qsa_last_error() != b""
+
+
+def test_select_fp8_zero_rows_and_workspace():
+    f, a, ws, wsb = fp8_args(R=0)
+    assert call_select_fp8(a, 0, 0) == OK
+    f, a, ws, wsb = fp8_args()
+    assert wsb > 0
+    assert call_select_fp8(a, ws, wsb - 1) == WORKSPACE
+    assert call_select_fp8(a, a["kscale"].data, wsb) == ALIAS
+
+
+def test_fp16_entry_refuses_e4m3_cache():
+    f, a, ws, wsb = fp8_args()
+    assert call_select(a, ws, wsb) == DTYPE
+
+
+def test_decode_step_fp8_checks():
+    lib = B.library()
+    f, s, sws, swsb = fp8_args(R=2)
+    g, a, aws, awsb, base = attn_args(R=2)
+    wsb = B.decode_step_workspace_bytes(2, 40)
+    ws = f.alloc(wsb)
+
+    def call(out=None, ws_bytes=wsb, kscale=None):
+        return lib.qsa_decode_step_fp8(
+            ctypes.byref(s["q"]), ctypes.byref(s["kcache"]), ctypes.byref(kscale or s["kscale"]),
+            ctypes.byref(s["bt"]), ctypes.byref(s["t2r"]), ctypes.byref(s["sl"]),
+            ctypes.byref(s["qp"]), ctypes.byref(a["q"]), ctypes.byref(a["k"]),
+            ctypes.byref(a["v"]), ctypes.c_float(0.0625), ctypes.byref(s["out"]),
+            ctypes.byref(out or a["out"]), ctypes.c_void_p(ws), ws_bytes, None)
+
+    assert call(out=mk(g, B.F16, (2, 3, 256), 2, ptr=s["kscale"].data)) == ALIAS
+    assert call(ws_bytes=wsb - 256) == WORKSPACE
+    assert call(kscale=mk(g, B.F32, (8, 127), 4)) == SHAPE
