@@ -21,6 +21,11 @@ Parity status of each function (the pins live in ``tests/oracle_pins.py``):
   e4m3 codes with power-of-two scales give the fp16 selection (itself
   pinned by brute force) exactly; one-hot queries read back scale * code for
   every code; numpy float64 gather of the dequantized keys + lexsort.
+* ``select_weighted`` / ``paged_logits`` / ``topk_per_row`` pinned: integer
+  brute force with integer (also negative) head weights; weights of one give
+  the unweighted selection; numpy float64 gather + weights; top-k per row
+  against numpy's lexsort on arbitrary logits (negative values, signed zeros,
+  repeats, junk past the visible blocks).
 """
 
 from __future__ import annotations
@@ -86,6 +91,12 @@ class Oracle:
         lib.qsa_oracle_row_scores_fp8.restype = ctypes.c_int
         lib.qsa_oracle_select_fp8.argtypes = [i64, i64, i64, i64, p, p, p, p, p, p, p, p]
         lib.qsa_oracle_select_fp8.restype = ctypes.c_int
+        lib.qsa_oracle_select_weighted.argtypes = [i64, i64, i64, i64] + [p] * 10
+        lib.qsa_oracle_select_weighted.restype = ctypes.c_int
+        lib.qsa_oracle_paged_logits.argtypes = [i64, i64, i64, i64] + [p] * 10 + [i64, i64]
+        lib.qsa_oracle_paged_logits.restype = ctypes.c_int
+        lib.qsa_oracle_topk_per_row.argtypes = [i64, i64, p, i64, i64, p, p, p, p]
+        lib.qsa_oracle_topk_per_row.restype = ctypes.c_int
         lib.qsa_oracle_mutant.argtypes = []
         lib.qsa_oracle_mutant.restype = ctypes.c_int
         self.lib = lib
@@ -197,6 +208,70 @@ class Oracle:
             self._ptr(out), max_blocks, ctypes.byref(v))
         self._check(rc)
         return out[: v.value].copy()
+
+    def _cache_ptrs(self, kcache, codes, scales):
+        """(kcache, codes, scales) arrays and pointers for the entry points
+        that take either an fp16 cache or e4m3 codes + scales."""
+        if codes is not None:
+            codes, scales = self._fp8_cache(codes, scales)
+            return codes.shape[0], None, self._ptr(codes), self._ptr(scales), (codes, scales)
+        kcache = self._c(kcache, np.float16)
+        assert kcache.shape[1:] == (128, 1, 128)
+        return kcache.shape[0], self._ptr(kcache), None, None, (kcache,)
+
+    def _weights(self, weights, R):
+        if weights is None:
+            return None, None
+        w = self._c(weights, np.float32)
+        assert w.shape == (R, 4)
+        return w, self._ptr(w)
+
+    def select_weighted(self, q, weights, block_table, token_to_req, seq_lens, query_pos,
+                        kcache=None, codes=None, scales=None) -> np.ndarray:
+        """[R,2051] selection with per-head weights [R,4] (fp16 cache, or
+        e4m3 codes + scales)."""
+        q, _, bt, t2r, sl, qp = self._select_args(
+            q, np.zeros((1, 128, 1, 128), np.float16), block_table, token_to_req, seq_lens,
+            query_pos)
+        R = q.shape[0]
+        P, kp, cp, sp, keep = self._cache_ptrs(kcache, codes, scales)
+        w, wp = self._weights(weights, R)
+        out = np.empty((R, WIDTH), dtype=np.int32)
+        rc = self.lib.qsa_oracle_select_weighted(
+            R, P, sl.shape[0], bt.shape[1], self._ptr(q), wp, kp, cp, sp, self._ptr(bt),
+            self._ptr(t2r), self._ptr(sl), self._ptr(qp), self._ptr(out))
+        self._check(rc)
+        return out
+
+    def paged_logits(self, q, weights, block_table, token_to_req, seq_lens, query_pos, width,
+                     kcache=None, codes=None, scales=None) -> np.ndarray:
+        """[R,width] float32: block scores for b < V, -inf past V."""
+        q, _, bt, t2r, sl, qp = self._select_args(
+            q, np.zeros((1, 128, 1, 128), np.float16), block_table, token_to_req, seq_lens,
+            query_pos)
+        R = q.shape[0]
+        P, kp, cp, sp, keep = self._cache_ptrs(kcache, codes, scales)
+        w, wp = self._weights(weights, R)
+        out = np.empty((R, int(width)), dtype=np.float32)
+        rc = self.lib.qsa_oracle_paged_logits(
+            R, P, sl.shape[0], bt.shape[1], self._ptr(q), wp, kp, cp, sp, self._ptr(bt),
+            self._ptr(t2r), self._ptr(sl), self._ptr(qp), self._ptr(out), int(width), int(width))
+        self._check(rc)
+        return out
+
+    def topk_per_row(self, logits, token_to_req, seq_lens, query_pos) -> np.ndarray:
+        """[R,2051] selection from a given [R, width] float32 logits matrix."""
+        lg = self._c(logits, np.float32)
+        t2r = self._c(token_to_req, np.int32)
+        sl = self._c(seq_lens, np.int32)
+        qp = self._c(query_pos, np.int64)
+        R = lg.shape[0]
+        out = np.empty((R, WIDTH), dtype=np.int32)
+        rc = self.lib.qsa_oracle_topk_per_row(
+            R, sl.shape[0], self._ptr(lg), lg.shape[1], lg.shape[1], self._ptr(t2r),
+            self._ptr(sl), self._ptr(qp), self._ptr(out))
+        self._check(rc)
+        return out
 
     def sparse_attn(self, q, kv, indices, scale: float) -> np.ndarray:
         """[R,3,256] float64 attention output.  kv is [..., 512] fp16 with

@@ -39,6 +39,15 @@
  *   binary32 scale, and the key used for scoring is the dequantized vector
  *   scale * e4m3(code[d]); everything else is as above.
  *
+ *   per-head weights and the two-pass form (the "[XPU] Enable multiple key
+ *   kernels for sparse attention" page: the paged MQA logits call takes
+ *   per-head weights and returns a logits matrix, which top_k_per_row_decode
+ *   then reduces): score s_b = sum_h w[r][h] * ReLU(q[r][h] . key_b) with
+ *   fp32 weights (w = 1 is the unweighted score above); paged logits =
+ *   the matrix of s_b for b < V and -inf for V <= b < width; top-k per row
+ *   = the selection above applied to a given logits row, reading its first V
+ *   entries only.
+ *
  * Precision: fp16 inputs are widened to double with a conversion written
  * from the IEEE 754 binary16 definition; every dot product and softmax is
  * evaluated in double.  A selection score is rounded once to binary32 at
@@ -204,8 +213,9 @@ static void widen_key(const key_cache* kc, int64_t slot_index, double* kd) {
 }
 
 /* Score of one compressed key (kd, widened) against the row's four indexer
- * heads (qd: the row's query widened to double, [4][128]). */
-static float block_score(const double* qd, const double* kd) {
+ * heads (qd: the row's query widened to double, [4][128]), each head's ReLU
+ * term weighted by w[h] (w NULL: every weight 1). */
+static float block_score(const double* qd, const double* kd, const float* w) {
   double total = 0.0;
   int heads = OR_SEL_HEADS;
 #if QSA_ORACLE_MUTANT == 5
@@ -216,10 +226,16 @@ static float block_score(const double* qd, const double* kd) {
     for (int d = 0; d < OR_SEL_DIM; ++d) {
       dot += qd[h * OR_SEL_DIM + d] * kd[d];
     }
+    double wh = w ? (double)w[h] : 1.0;
+#if QSA_ORACLE_MUTANT == 14
+    wh = 1.0; /* planted: head weights ignored */
+#endif
 #if QSA_ORACLE_MUTANT == 2
-    total += dot; /* planted: ReLU dropped */
+    total += wh * dot; /* planted: ReLU dropped */
+#elif QSA_ORACLE_MUTANT == 15
+    total += wh * dot > 0.0 ? wh * dot : 0.0; /* planted: ReLU after the weight */
 #else
-    total += dot > 0.0 ? dot : 0.0;
+    total += wh * (dot > 0.0 ? dot : 0.0);
 #endif
   }
   return (float)total;
@@ -249,10 +265,10 @@ static int64_t key_slot(int64_t num_pages, const int32_t* table_row, int64_t tab
 }
 
 static int row_scores(int64_t r, int64_t num_pages, int64_t num_reqs, int64_t table_width,
-                      const uint16_t* q, const key_cache* kc, const int32_t* block_table,
-                      const int32_t* token_to_req, const int32_t* seq_lens,
-                      const int64_t* query_pos, float* scores, int64_t max_blocks,
-                      int64_t* visible) {
+                      const uint16_t* q, const float* weights, const key_cache* kc,
+                      const int32_t* block_table, const int32_t* token_to_req,
+                      const int32_t* seq_lens, const int64_t* query_pos, float* scores,
+                      int64_t max_blocks, int64_t* visible) {
   int64_t req = token_to_req[r];
   if (req < 0 || req >= num_reqs) return OR_ERR_REQ;
   int64_t v, t;
@@ -268,7 +284,7 @@ static int row_scores(int64_t r, int64_t num_pages, int64_t num_reqs, int64_t ta
     int64_t at = key_slot(num_pages, table_row, table_width, b, &err);
     if (at < 0) return err;
     widen_key(kc, at, kd);
-    scores[b] = block_score(qd, kd);
+    scores[b] = block_score(qd, kd, weights ? weights + r * OR_SEL_HEADS : NULL);
   }
   return OR_OK;
 }
@@ -284,7 +300,7 @@ int qsa_oracle_row_scores(int64_t r, int64_t num_pages, int64_t num_reqs,
                           const int64_t* query_pos, float* scores,
                           int64_t max_blocks, int64_t* visible) {
   key_cache kc = {kcache, NULL, NULL};
-  return row_scores(r, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
+  return row_scores(r, num_pages, num_reqs, table_width, q, NULL, &kc, block_table, token_to_req,
                     seq_lens, query_pos, scores, max_blocks, visible);
 }
 
@@ -297,14 +313,28 @@ int qsa_oracle_row_scores_fp8(int64_t r, int64_t num_pages, int64_t num_reqs,
                               const int64_t* query_pos, float* scores, int64_t max_blocks,
                               int64_t* visible) {
   key_cache kc = {NULL, codes, scales};
-  return row_scores(r, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
+  return row_scores(r, num_pages, num_reqs, table_width, q, NULL, &kc, block_table, token_to_req,
                     seq_lens, query_pos, scores, max_blocks, visible);
 }
 
+/* Fill one output row from its V blocks already sorted by (score desc,
+ * block asc): the first min(512, V) blocks expanded to 4 tokens each, then
+ * the T tail tokens, then -1. */
+static void write_row(int32_t* out_row, const scored_block* sorted, int64_t v, int64_t t) {
+  for (int i = 0; i < OR_WIDTH; ++i) out_row[i] = -1;
+  int64_t n = v < OR_TOPK_BLOCKS ? v : OR_TOPK_BLOCKS;
+  for (int64_t i = 0; i < n; ++i) {
+    for (int j = 0; j < OR_RATIO; ++j) {
+      out_row[OR_RATIO * i + j] = (int32_t)(OR_RATIO * sorted[i].block + j);
+    }
+  }
+  for (int64_t k = 0; k < t; ++k) out_row[OR_RATIO * n + k] = (int32_t)(OR_RATIO * v + k);
+}
+
 static int select_rows(int64_t R, int64_t num_pages, int64_t num_reqs, int64_t table_width,
-                       const uint16_t* q, const key_cache* kc, const int32_t* block_table,
-                       const int32_t* token_to_req, const int32_t* seq_lens,
-                       const int64_t* query_pos, int32_t* out) {
+                       const uint16_t* q, const float* weights, const key_cache* kc,
+                       const int32_t* block_table, const int32_t* token_to_req,
+                       const int32_t* seq_lens, const int64_t* query_pos, int32_t* out) {
   for (int64_t r = 0; r < R; ++r) {
     int32_t* out_row = out + r * OR_WIDTH;
     for (int i = 0; i < OR_WIDTH; ++i) out_row[i] = -1;
@@ -329,19 +359,11 @@ static int select_rows(int64_t R, int64_t num_pages, int64_t num_reqs, int64_t t
         return err;
       }
       widen_key(kc, at, kd);
-      all[b].score = block_score(qd, kd);
+      all[b].score = block_score(qd, kd, weights ? weights + r * OR_SEL_HEADS : NULL);
       all[b].block = b;
     }
     if (v > 1) qsort(all, (size_t)v, sizeof(scored_block), by_score_then_index);
-    int64_t n = v < OR_TOPK_BLOCKS ? v : OR_TOPK_BLOCKS;
-    for (int64_t i = 0; i < n; ++i) {
-      for (int j = 0; j < OR_RATIO; ++j) {
-        out_row[OR_RATIO * i + j] = (int32_t)(OR_RATIO * all[i].block + j);
-      }
-    }
-    for (int64_t k = 0; k < t; ++k) {
-      out_row[OR_RATIO * n + k] = (int32_t)(OR_RATIO * v + k);
-    }
+    write_row(out_row, all, v, t);
     free(all);
   }
   return OR_OK;
@@ -359,8 +381,8 @@ int qsa_oracle_select(int64_t R, int64_t num_pages, int64_t num_reqs,
                       const int32_t* seq_lens, const int64_t* query_pos,
                       int32_t* out) {
   key_cache kc = {kcache, NULL, NULL};
-  return select_rows(R, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
-                     seq_lens, query_pos, out);
+  return select_rows(R, num_pages, num_reqs, table_width, q, NULL, &kc, block_table,
+                     token_to_req, seq_lens, query_pos, out);
 }
 
 /* As qsa_oracle_select, for an e4m3 cache: codes [P,128,1,128] bytes,
@@ -371,8 +393,79 @@ int qsa_oracle_select_fp8(int64_t R, int64_t num_pages, int64_t num_reqs,
                           const int32_t* token_to_req, const int32_t* seq_lens,
                           const int64_t* query_pos, int32_t* out) {
   key_cache kc = {NULL, codes, scales};
-  return select_rows(R, num_pages, num_reqs, table_width, q, &kc, block_table, token_to_req,
-                     seq_lens, query_pos, out);
+  return select_rows(R, num_pages, num_reqs, table_width, q, NULL, &kc, block_table,
+                     token_to_req, seq_lens, query_pos, out);
+}
+
+/* Weighted selection: weights [R,4] binary32; the key cache is binary16
+ * (kcache) when codes is NULL, else e4m3 codes with scales. */
+int qsa_oracle_select_weighted(int64_t R, int64_t num_pages, int64_t num_reqs,
+                               int64_t table_width, const uint16_t* q, const float* weights,
+                               const uint16_t* kcache, const uint8_t* codes,
+                               const float* scales, const int32_t* block_table,
+                               const int32_t* token_to_req, const int32_t* seq_lens,
+                               const int64_t* query_pos, int32_t* out) {
+  key_cache kc = {codes ? NULL : kcache, codes, scales};
+  return select_rows(R, num_pages, num_reqs, table_width, q, weights, &kc, block_table,
+                     token_to_req, seq_lens, query_pos, out);
+}
+
+/*
+ * Paged logits: logits[r][b] (row stride `stride` floats) = the score of
+ * block b for b < V, -inf for V <= b < width.  weights may be NULL (all 1);
+ * key cache as for qsa_oracle_select_weighted.  V > width is an error.
+ */
+int qsa_oracle_paged_logits(int64_t R, int64_t num_pages, int64_t num_reqs, int64_t table_width,
+                            const uint16_t* q, const float* weights, const uint16_t* kcache,
+                            const uint8_t* codes, const float* scales,
+                            const int32_t* block_table, const int32_t* token_to_req,
+                            const int32_t* seq_lens, const int64_t* query_pos, float* logits,
+                            int64_t width, int64_t stride) {
+  key_cache kc = {codes ? NULL : kcache, codes, scales};
+  for (int64_t r = 0; r < R; ++r) {
+    float* row = logits + r * stride;
+    int64_t v = 0;
+    int rc = row_scores(r, num_pages, num_reqs, table_width, q, weights, &kc, block_table,
+                        token_to_req, seq_lens, query_pos, row, width, &v);
+    if (rc != OR_OK) return rc;
+    for (int64_t b = v; b < width; ++b) row[b] = -INFINITY;
+  }
+  return OR_OK;
+}
+
+/*
+ * Top-k per row over given logits (row stride `stride` floats, `width`
+ * columns): for each query row, V and T from its request and position as in
+ * the selection; the first V logits are the block scores; they are ordered
+ * by (score descending, block ascending) and written exactly as the
+ * selection writes its output.  Entries at or past V are never read.
+ */
+int qsa_oracle_topk_per_row(int64_t R, int64_t num_reqs, const float* logits, int64_t width,
+                            int64_t stride, const int32_t* token_to_req,
+                            const int32_t* seq_lens, const int64_t* query_pos, int32_t* out) {
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t req = token_to_req[r];
+    if (req < 0 || req >= num_reqs) return OR_ERR_REQ;
+    int64_t v, t;
+    qsa_oracle_row_extent(seq_lens[req], query_pos[r], &v, &t);
+#if QSA_ORACLE_MUTANT == 16
+    v = width; /* planted: the whole logits row read */
+#endif
+    if (v > width) return OR_ERR_ARG;
+    scored_block* all = NULL;
+    if (v > 0) {
+      all = (scored_block*)malloc((size_t)v * sizeof(scored_block));
+      if (!all) return OR_ERR_NOMEM;
+    }
+    for (int64_t b = 0; b < v; ++b) {
+      all[b].score = logits[r * stride + b];
+      all[b].block = b;
+    }
+    if (v > 1) qsort(all, (size_t)v, sizeof(scored_block), by_score_then_index);
+    write_row(out + r * OR_WIDTH, all, v, t);
+    free(all);
+  }
+  return OR_OK;
 }
 
 /*

@@ -56,9 +56,9 @@ def brute_visible(seq_len: int, query_pos: int) -> tuple[int, int]:
     return len(blocks), len(tail)
 
 
-def brute_select_integer(q, kcache, bt, t2r, sl, qp) -> np.ndarray:
+def brute_select_integer(q, kcache, bt, t2r, sl, qp, weights=None) -> np.ndarray:
     """Selection from exact integer scores and rank counting (inputs must be
-    integer-valued fp16)."""
+    integer-valued fp16; weights, when given, integer-valued [R,4])."""
     R = q.shape[0]
     out = np.full((R, WIDTH), -1, dtype=np.int32)
     qi = q.astype(np.int64)
@@ -68,7 +68,8 @@ def brute_select_integer(q, kcache, bt, t2r, sl, qp) -> np.ndarray:
         b = np.arange(V)
         keys = kcache[bt[req, b // 128], b % 128, 0, :].astype(np.int64)  # [V,128]
         dots = keys @ qi[r].T                                               # [V,4]
-        s = np.maximum(dots, 0).sum(axis=1)                                 # [V]
+        wr = np.ones(4, np.int64) if weights is None else weights[r].astype(np.int64)
+        s = (np.maximum(dots, 0) * wr).sum(axis=1)                          # [V]
         # rank = blocks with a larger score + earlier blocks with an equal score
         better = (s[None, :] > s[:, None]) | ((s[None, :] == s[:, None]) & (b[None, :] < b[:, None]))
         rank = better.sum(axis=1)
@@ -378,12 +379,113 @@ def pin_select_fp8_gather_and_sort_normal(orc):
         assert np.array_equal(out[r, 4 * n:4 * n + L % 4], 4 * V + np.arange(L % 4))
 
 
+# ---------------------------------------------------------------------------
+# per-head weights and the two-pass form
+
+def pin_select_weighted_brute_force(orc):
+    """Integer head weights in [-3, 3] (zero and negative included): exact
+    int64 scores and rank counting, fp16 and e4m3 caches."""
+    for seed, palette, qr in [(4, None, 3), (5, 6, 2)]:
+        args = integer_problem(seed, PIN_LENGTHS, palette, qr)
+        q, kcache, bt, t2r, sl, qp = args
+        rng = np.random.default_rng(50 + seed)
+        w = rng.integers(-3, 4, size=(q.shape[0], 4)).astype(np.float32)
+        w[0] = [0, 0, 0, 0]                       # every score 0: ascending blocks
+        w[1] = [-1, -2, -1, -3]                   # every score <= 0
+        want = brute_select_integer(*args, weights=w)
+        got = orc.select_weighted(q, w, bt, t2r, sl, qp, kcache=kcache)
+        assert np.array_equal(got, want), f"weighted brute force (seed {seed})"
+        codes, scales = wl.fp8_integer_keys(np.random.default_rng(60 + seed), kcache)
+        got8 = orc.select_weighted(q, w, bt, t2r, sl, qp, codes=codes, scales=scales)
+        assert np.array_equal(got8, want), f"weighted e4m3 brute force (seed {seed})"
+
+
+def pin_weights_of_one(orc):
+    """Weights of one give the unweighted selection; the paged logits with no
+    weights are the exact row scores followed by -inf; top-k per row over
+    them is the brute-force selection."""
+    args = integer_problem(6, PIN_LENGTHS[:10], 5, 2)
+    q, kcache, bt, t2r, sl, qp = args
+    ones = np.ones((q.shape[0], 4), np.float32)
+    assert np.array_equal(orc.select_weighted(q, ones, bt, t2r, sl, qp, kcache=kcache),
+                          brute_select_integer(*args))
+    width = bt.shape[1] * 128 + 7
+    lg = orc.paged_logits(q, None, bt, t2r, sl, qp, width, kcache=kcache)
+    for r in range(q.shape[0]):
+        V, _ = brute_visible(int(sl[t2r[r]]), int(qp[r]))
+        b = np.arange(V)
+        keys = kcache[bt[t2r[r], b // 128], b % 128, 0, :].astype(np.int64)
+        want = np.maximum(keys @ q[r].astype(np.int64).T, 0).sum(axis=1)
+        assert np.array_equal(lg[r, :V], want.astype(np.float32))
+        assert np.all(np.isneginf(lg[r, V:]))
+    # the two passes compose to the brute-force selection (rows with V < 512
+    # would pick up -inf entries if the top-k read past V)
+    assert np.array_equal(orc.topk_per_row(lg, t2r, sl, qp), brute_select_integer(*args))
+
+
+def pin_paged_logits_gather_normal(orc):
+    """N(0,1) keys and real weights of both signs: the logits against a numpy
+    float64 gather, -inf past the visible blocks."""
+    rng = np.random.default_rng(31)
+    lengths = [2900, 517, 0]
+    P = 40
+    kcache = wl.normal_f16(rng, (P, 128, 1, 128))
+    bt = wl.block_table_per_row(rng, lengths, P)
+    q = wl.normal_f16(rng, (3, 4, 128))
+    t2r, sl, qp = wl.decode_rows(lengths)
+    w = rng.normal(size=(3, 4)).astype(np.float32)
+    width = bt.shape[1] * 128
+    lg = orc.paged_logits(q, w, bt, t2r, sl, qp, width, kcache=kcache)
+    for r, L in enumerate(lengths):
+        V = L // 4
+        b = np.arange(V)
+        keys = kcache[bt[r, b // 128], b % 128, 0, :].astype(np.float64)
+        dots = keys @ q[r].astype(np.float64).T
+        want = (np.maximum(dots, 0.0) * w[r].astype(np.float64)).sum(axis=1)
+        assert np.allclose(lg[r, :V], want, rtol=1e-6, atol=1e-6)
+        assert np.all(np.isneginf(lg[r, V:]))
+
+
+def pin_topk_per_row_lexsort(orc):
+    """Top-k per row over arbitrary logits -- negative values, +0 and -0
+    (equal), many exact repeats, huge junk past each row's visible blocks --
+    against numpy's lexsort of the first V entries."""
+    rng = np.random.default_rng(41)
+    lengths = [2900, 1337, 519, 4, 0, 6001]
+    qpos = [2899, 1000, 518, 3, -1, 6000]
+    width = 1600
+    lg = np.round(rng.normal(size=(len(lengths), width)) * 4) / 4   # coarse grid: ties
+    lg = lg.astype(np.float32)
+    zeros = rng.random(lg.shape) < 0.1
+    lg[zeros] = np.where(rng.random(zeros.sum()) < 0.5, 0.0, -0.0)
+    t2r = np.arange(len(lengths), dtype=np.int32)
+    sl = np.array(lengths, np.int32)
+    qp = np.array(qpos, np.int64)
+    for r in range(len(lengths)):
+        V, _ = brute_visible(lengths[r], qpos[r])
+        lg[r, V:] = 1e30                                             # never read
+    got = orc.topk_per_row(lg, t2r, sl, qp)
+    for r in range(len(lengths)):
+        V, T = brute_visible(lengths[r], qpos[r])
+        b = np.arange(V)
+        order = np.lexsort((b, -lg[r, :V].astype(np.float64)))
+        n = min(TOPK, V)
+        want = np.full(WIDTH, -1, np.int32)
+        want[:4 * n] = (4 * order[:n, None] + np.arange(4)).reshape(-1)
+        want[4 * n:4 * n + T] = 4 * V + np.arange(T)
+        assert np.array_equal(got[r], want), f"row {r}"
+
+
 ALL_PINS = [
     pin_half_to_double,
     pin_e4m3_to_double,
     pin_select_fp8_integer_equivalence,
     pin_row_scores_fp8_one_hot,
     pin_select_fp8_gather_and_sort_normal,
+    pin_select_weighted_brute_force,
+    pin_weights_of_one,
+    pin_paged_logits_gather_normal,
+    pin_topk_per_row_lexsort,
     pin_select_worked_examples,
     pin_select_brute_force_integer,
     pin_select_multirow_requests,

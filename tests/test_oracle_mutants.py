@@ -1,6 +1,6 @@
 """Each planted mistake in the oracle must be caught by at least one pin.
 
-The oracle source carries thirteen compile-time mutants (a dropped term, a wrong
+The oracle source carries sixteen compile-time mutants (a dropped term, a wrong
 sign, an off-by-one, a transposed operand, ...).  Building each one and
 running the pins shows that the pins constrain every step of the oracle.
 """
@@ -24,6 +24,9 @@ MUTANTS = {
     11: "fp8 key scale ignored",
     12: "e4m3 exponent bias 8",
     13: "e4m3 subnormal read as normal",
+    14: "head weights ignored",
+    15: "ReLU after the head weight",
+    16: "top-k per row reads past the visible blocks",
 }
 
 
