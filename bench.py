@@ -11,6 +11,11 @@ Workloads (``--workload``):
 * long_context_fp8: the long-context batch with its compressed keys
   absmax-quantized to an e4m3 cache (128 B of codes + one fp32 scale per
   key, 528 MiB), timed through qsa_decode_step_fp8.
+* long_context_two_pass: the long-context batch with per-head weights
+  (uniform in [-0.5, 1.5]), selected in two passes -- qsa_paged_logits
+  writes the [128, 32768] fp32 logits matrix, qsa_topk_per_row reduces it --
+  then attention; the fused weighted selection (qsa_select_weighted) is
+  timed on the same inputs for comparison.
 * multi_token: several query rows per request -- 48 speculative-decode
   requests with 4 draft positions each and 4 chunked-prefill requests with
   16 positions each (R=256), lengths uniform in [8192, 65536], an 8192-page
@@ -73,6 +78,24 @@ def select_algorithmic_bytes(seq_lens, query_pos, token_to_req, key_bytes: int =
     return total
 
 
+def logits_algorithmic_bytes(seq_lens, query_pos, token_to_req, width: int) -> int:
+    """Bytes the paged-logits pass must move per launch: the keys and
+    table entries as for the selection, per row the 1 KiB query, 16 B of
+    weights, 16 B of row metadata and its 4 B x width logits row."""
+    furthest = {}
+    total = 0
+    for r in range(len(token_to_req)):
+        req = int(token_to_req[r])
+        L = int(seq_lens[req])
+        qp = int(query_pos[r])
+        v = max(0, min((qp + 1) // 4, L // 4))
+        furthest[req] = max(furthest.get(req, 0), v)
+        total += 1024 + 16 + 16 + 4 * width
+    for v in furthest.values():
+        total += 256 * v + 4 * (-(-v // 128))
+    return total
+
+
 def attn_algorithmic_bytes(indices: np.ndarray) -> int:
     """Per row: 1 KiB per distinct valid token (K and V halves), the 8204 B
     index row, the 1.5 KiB query and the 1.5 KiB output."""
@@ -104,7 +127,8 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, scale: float, fp8: bool = False, max_seconds: float = 20.0) -> dict:
+def cpu_baseline(w, scale: float, fp8: bool = False, weights=None,
+                 max_seconds: float = 20.0) -> dict:
     """The CPU oracle (single-threaded C, unmodified) on the host cores: the
     whole decode step of the first rows of the same workload, until all rows
     are done or max_seconds of work have been spent."""
@@ -120,6 +144,10 @@ def cpu_baseline(w, scale: float, fp8: bool = False, max_seconds: float = 20.0) 
         q, kc, bt, t2r, sl, qp = inputs
         if fp8:
             sel = orc.select_fp8(q[r], w.kcodes, w.kscale, bt, t2r[r], sl, qp[r])
+        elif weights is not None:
+            lg = orc.paged_logits(q[r], weights[r], bt, t2r[r], sl, qp[r], bt.shape[1] * 128,
+                                  kcache=kc)
+            sel = orc.topk_per_row(lg, t2r[r], sl, qp[r])
         else:
             sel = orc.select(q[r], kc, bt, t2r[r], sl, qp[r])
         att = orc.sparse_attn(w.q_attn[r], w.kv, sel, scale)
@@ -150,7 +178,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=["long_context", "long_context_fp8", "multi_token"],
+    ap.add_argument("--workload", choices=["long_context", "long_context_fp8",
+                                           "long_context_two_pass", "multi_token"],
                     default="long_context")
     ap.add_argument("--kv-copies", type=int, default=8,
                     help="distinct KV caches the steps rotate over (one per simulated layer)")
@@ -179,12 +208,17 @@ def main() -> int:
 
     t0 = time.perf_counter()
     fp8 = args.workload == "long_context_fp8"
+    two_pass = args.workload == "long_context_two_pass"
+    head_w = None
     if args.workload == "multi_token":
         w = wl.multi_token_rows(args.seed)
     else:
         w = wl.long_context(args.seed)
         if fp8:
             w = wl.with_fp8_keys(w, integer=False)
+        if two_pass:
+            head_w = wl.head_weights(np.random.default_rng(args.seed + 555), w.rows)
+            w.name = w.name + "_two_pass"
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -217,9 +251,31 @@ def main() -> int:
     ws_all = torch.zeros(max(1, qsa.decode_step_workspace_bytes(R, w.block_table.shape[1])),
                          dtype=torch.uint8, device=dev)
 
-    def step(i):
-        k, v = kv_views[i % len(kv_views)]
-        decode_fn(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
+    if two_pass:
+        wt = d(head_w)
+        logits_width = w.block_table.shape[1] * 128
+        logits = torch.empty((R, logits_width), dtype=torch.float32, device=dev)
+        topk_ws = torch.zeros(max(1, qsa.topk_per_row_workspace_bytes(R, logits_width)),
+                              dtype=torch.uint8, device=dev)
+
+        def select_stage(mark=None):
+            qsa.qsa_paged_logits(*sel_in, weights=wt, logits=logits)
+            if mark is not None:
+                mark.record(stream)
+            qsa.qsa_topk_per_row(logits, sel_in[3], sel_in[4], sel_in[5], out=idx,
+                                 workspace=topk_ws)
+
+        def step(i):
+            k, v = kv_views[i % len(kv_views)]
+            select_stage()
+            qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
+    else:
+        def select_stage(mark=None):
+            select_fn(*sel_in, out=idx, workspace=sel_ws)
+
+        def step(i):
+            k, v = kv_views[i % len(kv_views)]
+            decode_fn(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
 
     # warm-up, then exactly K timed decode steps (events only at the ends)
     for i in range(args.warmup):
@@ -237,17 +293,35 @@ def main() -> int:
 
     # Per-stage times for the roofline: the same two stages through their own
     # entry points, with events recorded on the launch stream around each.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         k, v = kv_views[i % len(kv_views)]
         events[i][0].record(stream)
-        select_fn(*sel_in, out=idx, workspace=sel_ws)
+        select_stage(mark=events[i][3] if two_pass else None)
         events[i][1].record(stream)
         qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
         events[i][2].record(stream)
     torch.cuda.synchronize()
     sel_ms = [e[0].elapsed_time(e[1]) for e in events]
     att_ms = [e[1].elapsed_time(e[2]) for e in events]
+    extra = {}
+    if two_pass:
+        logits_ms = [e[0].elapsed_time(e[3]) for e in events]
+        topk_ms = [e[3].elapsed_time(e[1]) for e in events]
+        # the fused weighted selection on the same inputs, for comparison
+        fused_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fused_idx = torch.empty_like(idx)
+        qsa.qsa_select_weighted(sel_in[0], wt, *sel_in[1:], out=fused_idx, workspace=sel_ws)
+        fused_ev[0].record(stream)
+        for _ in range(args.steps):
+            qsa.qsa_select_weighted(sel_in[0], wt, *sel_in[1:], out=fused_idx, workspace=sel_ws)
+        fused_ev[1].record(stream)
+        torch.cuda.synchronize()
+        extra = {"logits_ms": round(float(np.mean(logits_ms)), 4),
+                 "topk_ms": round(float(np.mean(topk_ms)), 4),
+                 "fused_weighted_select_ms": round(fused_ev[0].elapsed_time(fused_ev[1]) / args.steps, 4)}
+        log(f"two-pass: logits {extra['logits_ms']:.4f} ms + top-k {extra['topk_ms']:.4f} ms; "
+            f"fused weighted select {extra['fused_weighted_select_ms']:.4f} ms")
     log(f"step {ms_per_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms); stages: select "
         f"{np.mean(sel_ms):.4f} ms (min {np.min(sel_ms):.4f}), attention {np.mean(att_ms):.4f} ms")
 
@@ -262,10 +336,21 @@ def main() -> int:
     att_bytes = attn_algorithmic_bytes(got_idx)
     sel_avg_s = float(np.mean(sel_ms)) / 1e3
     att_avg_s = float(np.mean(att_ms)) / 1e3
-    achieved = sel_bytes / sel_avg_s / 1e9
+    if two_pass:
+        # the dominant kernel of the two-pass step is the paged-logits pass
+        roof_bytes = logits_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
+                                              logits_width)
+        roof_s = extra["logits_ms"] / 1e3
+        roof_kernel = "qsa_paged_logits (qsa_select_chunk_kernel, logits out)"
+    else:
+        roof_bytes, roof_s = sel_bytes, sel_avg_s
+        roof_kernel = (("qsa_select_fp8" if fp8 else "qsa_select") +
+                       " (qsa_select_chunk_kernel + qsa_select_merge_kernel)")
+    achieved = roof_bytes / roof_s / 1e9
     traffic = stored_traffic(w.name)
     rows_per_s = R / (ms_per_step / 1e3)
-    step_gbs = (sel_bytes + att_bytes) / (ms_per_step / 1e3) / 1e9
+    step_bytes = sel_bytes + att_bytes + (R * logits_width * 8 if two_pass else 0)
+    step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -281,25 +366,28 @@ def main() -> int:
         "dtype": "e4m3 keys x f16 queries, f16 attention" if fp8 else "f16",
         "data": ("synthetic (seeded N(0,1) keys absmax-quantized to e4m3 with one fp32 scale per "
                  "key; N(0,1) fp16 queries/KV; random permuted block tables)" if fp8 else
+                 "synthetic (seeded N(0,1) fp16 keys/queries/KV, per-head weights U[-0.5, 1.5], "
+                 "random permuted block tables)" if two_pass else
                  "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)"),
         "config": workload_config(w, len(kv_sets)),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": ("qsa_select_fp8" if fp8 else "qsa_select") +
-                               " (qsa_select_chunk_kernel + qsa_select_merge_kernel)",
-                     "bytes_per_launch": sel_bytes, "avg_launch_ms": round(sel_avg_s * 1e3, 4)},
+                     "traffic": traffic, "kernel": roof_kernel,
+                     "bytes_per_launch": roof_bytes, "avg_launch_ms": round(roof_s * 1e3, 4)},
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
                    "attention_bytes": att_bytes,
                    "attention_gbs": round(att_bytes / att_avg_s / 1e9, 1),
                    "step_gbs": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
-                   "timed_entry_point": "qsa_decode_step_fp8" if fp8 else "qsa_decode_step",
+                   "timed_entry_point": ("qsa_paged_logits + qsa_topk_per_row + qsa_sparse_attn"
+                                         if two_pass else
+                                         "qsa_decode_step_fp8" if fp8 else "qsa_decode_step"),
+                   **extra,
                    "stage_timing": "separate pass: qsa_select and qsa_sparse_attn with events "
                                    "between them"},
     }
     if not args.no_cpu_baseline:
-        base = cpu_baseline(w, scale, fp8=fp8)
+        base = cpu_baseline(w, scale, fp8=fp8, weights=head_w)
         outs = base.pop("_outs")
         # the timed configuration's output on the rows the oracle finished
         same = sum(np.array_equal(sel[0], got_idx[i]) for i, (sel, _) in enumerate(outs))

@@ -10,7 +10,10 @@
  *   qsa_decode_step  both, back to back on one stream, indices stay on device
  *
  * and the same selection over an fp8 e4m3 compressed-key cache
- * (qsa_select_fp8, qsa_decode_step_fp8).
+ * (qsa_select_fp8, qsa_decode_step_fp8), with per-head weights
+ * (qsa_select_weighted), and in two passes: scores materialised as a logits
+ * matrix (qsa_paged_logits), then a top-k per row over it
+ * (qsa_topk_per_row).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -182,6 +185,76 @@ QSA_API int qsa_select_fp8(const qsa_tensor* q, const qsa_tensor* kcache,
                            const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
                            const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
                            size_t workspace_bytes, qsa_stream stream);
+
+/*
+ * qsa_select_weighted -- qsa_select with per-head weights.  The page "[XPU]
+ * Enable multiple key kernels for sparse attention" shows the paged MQA
+ * logits call taking per-head `weights`; here block b scores
+ *
+ *   s_b = sum_h weights[r][h] * ReLU(q[r][h] . key_b)
+ *
+ * (weights of 1 give qsa_select's score).  Weighted scores may be negative;
+ * the order is still (score descending, block ascending) with -0 == +0.
+ *
+ *   weights  F32 [R,4] contiguous, 16-byte aligned, finite.
+ *   kscale   NULL: kcache is an F16 cache as for qsa_select; otherwise
+ *            kcache is an E4M3 cache and kscale its F32 [P,128] scales, as
+ *            for qsa_select_fp8.
+ *
+ * Everything else (arguments, output, workspace = qsa_select_workspace_bytes,
+ * errors) as for qsa_select.
+ */
+QSA_API int qsa_select_weighted(const qsa_tensor* q, const qsa_tensor* weights,
+                                const qsa_tensor* kcache, const qsa_tensor* kscale,
+                                const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                                const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                                const qsa_tensor* out, void* workspace, size_t workspace_bytes,
+                                qsa_stream stream);
+
+/*
+ * qsa_paged_logits -- the first of the two passes of the same page (paged
+ * MQA logits with per-head weights, returned as a logits matrix): the score
+ * of every visible block, written as fp32 logits.
+ *
+ *   q, kcache, block_table, token_to_req, seq_lens, query_pos  as for
+ *            qsa_select; weights F32 [R,4] or NULL (all 1); kscale NULL (F16
+ *            cache) or the scales of an E4M3 cache, as for
+ *            qsa_select_weighted.
+ *   logits   F32 [R, Wl], stride[1] == 1, stride[0] >= Wl, 4-byte aligned,
+ *            written: logits[r][b] = s_b for b < V, -inf for V <= b < Wl.
+ *            Wl >= W * 128 (W = block_table columns), so every visible block
+ *            has its column.  Must not overlap any input.
+ *
+ * No workspace.  Errors as for qsa_select.
+ */
+QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
+                             const qsa_tensor* kcache, const qsa_tensor* kscale,
+                             const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                             const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                             const qsa_tensor* logits, qsa_stream stream);
+
+/* Workspace bytes qsa_topk_per_row needs for `rows` rows of `logits_width`
+ * columns.  0 when rows == 0. */
+QSA_API size_t qsa_topk_per_row_workspace_bytes(int64_t rows, int64_t logits_width);
+
+/*
+ * qsa_topk_per_row -- the second pass (the page's top_k_per_row_decode
+ * step): the selection of qsa_select applied to given block scores.
+ *
+ *   logits       F32 [R, Wl], stride[1] == 1, stride[0] >= Wl, 4-byte
+ *                aligned: logits[r][b] is the score of block b of row r.
+ *   token_to_req I32 [R], seq_lens I32 [N], query_pos I64 [R]: as for
+ *                qsa_select; they give each row's V and T.
+ *   out          I32 [R,2051] contiguous, written as by qsa_select.
+ *
+ * Only the first V logits of a row are read (V <= Wl is a precondition; the
+ * kernel reads at most Wl); values must not be NaN.  Workspace:
+ * qsa_topk_per_row_workspace_bytes(R, Wl).  Errors as for qsa_select.
+ */
+QSA_API int qsa_topk_per_row(const qsa_tensor* logits, const qsa_tensor* token_to_req,
+                             const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                             const qsa_tensor* out, void* workspace, size_t workspace_bytes,
+                             qsa_stream stream);
 
 /*
  * qsa_sparse_attn -- fp16 sparse decode attention over logical indices with

@@ -17,9 +17,13 @@ from ._binding import (  # noqa: F401
     library,
     qsa_decode_step,
     qsa_decode_step_fp8,
+    qsa_paged_logits,
     qsa_select,
     qsa_select_fp8,
+    qsa_select_weighted,
+    qsa_topk_per_row,
     qsa_sparse_attn,
     select_workspace_bytes,
     sparse_attn_workspace_bytes,
+    topk_per_row_workspace_bytes,
 )

@@ -78,6 +78,14 @@ def library() -> ctypes.CDLL:
             lib.qsa_select_fp8.restype = ctypes.c_int
             lib.qsa_decode_step_fp8.argtypes = [_P] * 10 + [f32, _P, _P, vp, sz, vp]
             lib.qsa_decode_step_fp8.restype = ctypes.c_int
+            lib.qsa_select_weighted.argtypes = [_P] * 9 + [vp, sz, vp]
+            lib.qsa_select_weighted.restype = ctypes.c_int
+            lib.qsa_paged_logits.argtypes = [_P] * 9 + [vp]
+            lib.qsa_paged_logits.restype = ctypes.c_int
+            lib.qsa_topk_per_row_workspace_bytes.argtypes = [i64, i64]
+            lib.qsa_topk_per_row_workspace_bytes.restype = sz
+            lib.qsa_topk_per_row.argtypes = [_P] * 5 + [vp, sz, vp]
+            lib.qsa_topk_per_row.restype = ctypes.c_int
             _lib = lib
         return _lib
 
@@ -198,6 +206,70 @@ def qsa_select_fp8(q, kcache, kscale, block_table, token_to_req, seq_lens, query
     descs = [tensor_desc(t) for t in (q, kcache, kscale, block_table, token_to_req, seq_lens,
                                       query_pos, out)]
     check(lib.qsa_select_fp8(*[ctypes.byref(d) for d in descs], ws, ws_bytes, ctypes.c_void_p(sh)))
+    return out
+
+
+def _opt(t):
+    """Descriptor pointer of an optional tensor (None -> NULL)."""
+    return None if t is None else ctypes.byref(tensor_desc(t))
+
+
+def qsa_select_weighted(q, weights, kcache, block_table, token_to_req, seq_lens, query_pos,
+                        kscale=None, out=None, workspace=None, stream=None):
+    """Selection with per-head weights [R,4] float32 (fp16 cache, or e4m3
+    codes with kscale); returns out ([R,2051] int32)."""
+    torch = _torch()
+    lib = library()
+    R = q.shape[0]
+    if out is None:
+        out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
+    sh = _stream(stream, q.device)
+    need = select_workspace_bytes(R, block_table.shape[1]) if block_table.dim() == 2 else 0
+    ws, ws_bytes = _ws_args(need, q.device, sh, workspace, "select")
+    d = [tensor_desc(t) for t in (q, weights, kcache)]
+    rest = [tensor_desc(t) for t in (block_table, token_to_req, seq_lens, query_pos, out)]
+    check(lib.qsa_select_weighted(*[ctypes.byref(x) for x in d], _opt(kscale),
+                                  *[ctypes.byref(x) for x in rest], ws, ws_bytes,
+                                  ctypes.c_void_p(sh)))
+    return out
+
+
+def qsa_paged_logits(q, kcache, block_table, token_to_req, seq_lens, query_pos, weights=None,
+                     kscale=None, logits=None, width=None, stream=None):
+    """Block scores as an fp32 logits matrix [R, width] (width defaults to
+    the block table's width x 128; -inf past each row's visible blocks)."""
+    torch = _torch()
+    lib = library()
+    R = q.shape[0]
+    if logits is None:
+        W = block_table.shape[1] * 128 if width is None else int(width)
+        logits = torch.empty((R, W), dtype=torch.float32, device=q.device)
+    sh = _stream(stream, q.device)
+    rest = [tensor_desc(t) for t in (block_table, token_to_req, seq_lens, query_pos, logits)]
+    check(lib.qsa_paged_logits(ctypes.byref(tensor_desc(q)), _opt(weights),
+                               ctypes.byref(tensor_desc(kcache)), _opt(kscale),
+                               *[ctypes.byref(x) for x in rest], ctypes.c_void_p(sh)))
+    return logits
+
+
+def topk_per_row_workspace_bytes(rows: int, logits_width: int) -> int:
+    return int(library().qsa_topk_per_row_workspace_bytes(int(rows), int(logits_width)))
+
+
+def qsa_topk_per_row(logits, token_to_req, seq_lens, query_pos, out=None, workspace=None,
+                     stream=None):
+    """Top-512 blocks per row of a logits matrix, expanded as by qsa_select;
+    returns out ([R,2051] int32)."""
+    torch = _torch()
+    lib = library()
+    R = logits.shape[0]
+    if out is None:
+        out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=logits.device)
+    sh = _stream(stream, logits.device)
+    need = topk_per_row_workspace_bytes(R, logits.shape[1]) if logits.dim() == 2 else 0
+    ws, ws_bytes = _ws_args(need, logits.device, sh, workspace, "topk")
+    d = [tensor_desc(t) for t in (logits, token_to_req, seq_lens, query_pos, out)]
+    check(lib.qsa_topk_per_row(*[ctypes.byref(x) for x in d], ws, ws_bytes, ctypes.c_void_p(sh)))
     return out
 
 

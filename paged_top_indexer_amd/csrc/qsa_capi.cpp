@@ -120,11 +120,12 @@ struct SelectView {
   int64_t rows = 0, pages = 0, reqs = 0, width = 0, bt_stride = 0;
 };
 
-// kscale == NULL: an fp16 key cache; else an e4m3 cache with per-key scales.
-int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* kscale,
-                    bool e4m3, const qsa_tensor* bt, const qsa_tensor* t2r,
-                    const qsa_tensor* sl, const qsa_tensor* qp, const qsa_tensor* out,
-                    SelectView* v) {
+// The selection family's inputs.  e4m3 false: an fp16 key cache (kscale
+// unused); true: e4m3 codes with per-key scales.  weights may be NULL.
+int validate_select_inputs(const qsa_tensor* q, const qsa_tensor* weights,
+                           const qsa_tensor* kcache, const qsa_tensor* kscale, bool e4m3,
+                           const qsa_tensor* bt, const qsa_tensor* t2r, const qsa_tensor* sl,
+                           const qsa_tensor* qp, SelectView* v) {
   const int64_t any3[3] = {-1, QSA_SEL_HEADS, QSA_SEL_DIM};
   QSA_TRY(check_tensor("q", q, QSA_DTYPE_F16, 3, any3));
   QSA_TRY(check_contiguous("q", q));
@@ -154,19 +155,15 @@ int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_ten
   QSA_TRY(check_contiguous("seq_lens", sl));
   QSA_TRY(check_tensor("query_pos", qp, QSA_DTYPE_I64, 1, rshape));
   QSA_TRY(check_contiguous("query_pos", qp));
-  const int64_t oshape[2] = {R, QSA_OUT_WIDTH};
-  QSA_TRY(check_tensor("out", out, QSA_DTYPE_I32, 2, oshape));
-  QSA_TRY(check_contiguous("out", out));
+  if (weights) {
+    const int64_t wshape[2] = {R, QSA_SEL_HEADS};
+    QSA_TRY(check_tensor("weights", weights, QSA_DTYPE_F32, 2, wshape));
+    QSA_TRY(check_contiguous("weights", weights));
+    QSA_TRY(check_aligned("weights", weights, 16));
+  }
   if (R > 0 && N < 1) return fail(QSA_ERR_SHAPE, "seq_lens/block_table: no requests for %lld rows", (long long)R);
   if (R > (int64_t)1 << 30) return fail(QSA_ERR_SHAPE, "q: too many rows");
   if (W > ((int64_t)1 << 22)) return fail(QSA_ERR_SHAPE, "block_table: too wide");
-  const Span so = span_of(out);
-  const qsa_tensor* ins[7] = {q, kcache, bt, t2r, sl, qp, kscale};
-  const char* names[7] = {"q", "kcache", "block_table", "token_to_req", "seq_lens", "query_pos",
-                          "kscale"};
-  for (int i = 0; i < (e4m3 ? 7 : 6); ++i) {
-    if (overlaps(so, span_of(ins[i]))) return fail(QSA_ERR_ALIAS, "out overlaps %s", names[i]);
-  }
   v->rows = R;
   v->pages = kcache->shape[0];
   v->reqs = N;
@@ -174,6 +171,43 @@ int validate_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_ten
   v->bt_stride = N > 1 ? bt->stride[0] : W;
   return QSA_OK;
 }
+
+// An output of the selection family must not overlap any of its inputs.
+int check_select_output(const char* what, const qsa_tensor* out, const qsa_tensor* q,
+                        const qsa_tensor* weights, const qsa_tensor* kcache,
+                        const qsa_tensor* kscale, bool e4m3, const qsa_tensor* bt,
+                        const qsa_tensor* t2r, const qsa_tensor* sl, const qsa_tensor* qp) {
+  const Span so = span_of(out);
+  const qsa_tensor* ins[8] = {q, kcache, bt, t2r, sl, qp, e4m3 ? kscale : nullptr, weights};
+  const char* names[8] = {"q", "kcache", "block_table", "token_to_req", "seq_lens", "query_pos",
+                          "kscale", "weights"};
+  for (int i = 0; i < 8; ++i) {
+    if (ins[i] && overlaps(so, span_of(ins[i]))) {
+      return fail(QSA_ERR_ALIAS, "%s overlaps %s", what, names[i]);
+    }
+  }
+  return QSA_OK;
+}
+
+int check_index_rows(const char* name, const qsa_tensor* out, int64_t rows) {
+  const int64_t oshape[2] = {rows, QSA_OUT_WIDTH};
+  QSA_TRY(check_tensor(name, out, QSA_DTYPE_I32, 2, oshape));
+  return check_contiguous(name, out);
+}
+
+// A logits matrix: F32 [R, width], unit column stride, row stride >= width.
+int check_logits(const char* name, const qsa_tensor* t, int64_t rows) {
+  const int64_t shape[2] = {rows, -1};
+  QSA_TRY(check_tensor(name, t, QSA_DTYPE_F32, 2, shape));
+  const int64_t width = t->shape[1];
+  if (width < 1) return fail(QSA_ERR_SHAPE, "%s: width must be >= 1", name);
+  if (width > ((int64_t)1 << 29)) return fail(QSA_ERR_SHAPE, "%s: too wide", name);
+  if (width > 1 && t->stride[1] != 1) return fail(QSA_ERR_LAYOUT, "%s: stride[1] must be 1", name);
+  if (rows > 1 && t->stride[0] < width) return fail(QSA_ERR_LAYOUT, "%s: stride[0] < width", name);
+  return check_aligned(name, t, 4);
+}
+
+int64_t logits_stride(const qsa_tensor* t) { return t->shape[0] > 1 ? t->stride[0] : t->shape[1]; }
 
 struct AttnView {
   int64_t rows = 0, tokens = 0;
@@ -308,12 +342,13 @@ AttnPlan plan_attn(int64_t rows) {
 
 namespace {
 
-void fill_select_args(qsa::SelectArgs& a, const qsa_tensor* q, const qsa_tensor* kcache,
-                      const qsa_tensor* kscale, bool e4m3, const qsa_tensor* block_table,
-                      const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
-                      const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
-                      const SelectView& v) {
+void fill_select_args(qsa::SelectArgs& a, const qsa_tensor* q, const qsa_tensor* weights,
+                      const qsa_tensor* kcache, const qsa_tensor* kscale, bool e4m3,
+                      const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                      const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                      const qsa_tensor* out, void* workspace, const SelectView& v) {
   a.q = static_cast<const uint16_t*>(q->data);
+  a.weights = weights ? static_cast<const float*>(weights->data) : nullptr;
   a.kcache = e4m3 ? nullptr : static_cast<const uint16_t*>(kcache->data);
   a.kcodes = e4m3 ? static_cast<const uint8_t*>(kcache->data) : nullptr;
   a.kscale = e4m3 ? static_cast<const float*>(kscale->data) : nullptr;
@@ -321,32 +356,38 @@ void fill_select_args(qsa::SelectArgs& a, const qsa_tensor* q, const qsa_tensor*
   a.token_to_req = static_cast<const int32_t*>(token_to_req->data);
   a.seq_lens = static_cast<const int32_t*>(seq_lens->data);
   a.query_pos = static_cast<const int64_t*>(query_pos->data);
-  a.out = static_cast<int32_t*>(out->data);
+  a.out = out ? static_cast<int32_t*>(out->data) : nullptr;  // NULL: paged logits
   a.workspace = workspace;
   a.rows = v.rows;
   a.num_pages = v.pages;
   a.num_reqs = v.reqs;
   a.table_width = v.width;
   a.bt_stride = v.bt_stride;
+  a.max_visible = v.width * QSA_PAGE_SLOTS;
 }
 
-int select_impl(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* kscale,
-                bool e4m3, const qsa_tensor* block_table, const qsa_tensor* token_to_req,
-                const qsa_tensor* seq_lens, const qsa_tensor* query_pos, const qsa_tensor* out,
-                void* workspace, size_t workspace_bytes, qsa_stream stream) {
+int select_impl(const qsa_tensor* q, const qsa_tensor* weights, const qsa_tensor* kcache,
+                const qsa_tensor* kscale, bool e4m3, const qsa_tensor* block_table,
+                const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
+                const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
+                size_t workspace_bytes, qsa_stream stream) {
   g_last_error[0] = '\0';
   SelectView v;
-  QSA_TRY(validate_select(q, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
-                          query_pos, out, &v));
+  QSA_TRY(validate_select_inputs(q, weights, kcache, kscale, e4m3, block_table, token_to_req,
+                                 seq_lens, query_pos, &v));
+  QSA_TRY(check_index_rows("out", out, v.rows));
+  QSA_TRY(check_select_output("out", out, q, weights, kcache, kscale, e4m3, block_table,
+                              token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
   const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
-  Span guarded[8] = {span_of(q),        span_of(kcache),   span_of(block_table),
+  Span guarded[9] = {span_of(q),        span_of(kcache),   span_of(block_table),
                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
-                     span_of(out),      e4m3 ? span_of(kscale) : Span()};
-  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 8));
+                     span_of(out),      e4m3 ? span_of(kscale) : Span(),
+                     weights ? span_of(weights) : Span()};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 9));
   qsa::SelectArgs a;
-  fill_select_args(a, q, kcache, kscale, e4m3, block_table, token_to_req, seq_lens, query_pos,
-                   out, workspace, v);
+  fill_select_args(a, q, weights, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
+                   query_pos, out, workspace, v);
   const int err = qsa::launch_select(a, plan, stream);
   if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
   return QSA_OK;
@@ -360,8 +401,11 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
                 size_t workspace_bytes, qsa_stream stream) {
   g_last_error[0] = '\0';
   SelectView sv;
-  QSA_TRY(validate_select(q_sel, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
-                          query_pos, indices, &sv));
+  QSA_TRY(validate_select_inputs(q_sel, nullptr, kcache, kscale, e4m3, block_table,
+                                 token_to_req, seq_lens, query_pos, &sv));
+  QSA_TRY(check_index_rows("indices", indices, sv.rows));
+  QSA_TRY(check_select_output("indices", indices, q_sel, nullptr, kcache, kscale, e4m3,
+                              block_table, token_to_req, seq_lens, query_pos));
   AttnView av;
   QSA_TRY(validate_attn(q_attn, k, v, indices, softmax_scale, out, true, &av));
   if (av.rows != sv.rows) return fail(QSA_ERR_SHAPE, "q_attn rows differ from q_sel rows");
@@ -389,7 +433,7 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   QSA_TRY(check_workspace(workspace, workspace_bytes, need, guarded, 11));
 
   qsa::SelectArgs s;
-  fill_select_args(s, q_sel, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
+  fill_select_args(s, q_sel, nullptr, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
                    query_pos, indices, workspace, sv);
   int err = qsa::launch_select(s, splan, stream);
   if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
@@ -457,8 +501,8 @@ QSA_API int qsa_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_
                        const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
                        const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
                        size_t workspace_bytes, qsa_stream stream) {
-  return select_impl(q, kcache, nullptr, false, block_table, token_to_req, seq_lens, query_pos,
-                     out, workspace, workspace_bytes, stream);
+  return select_impl(q, nullptr, kcache, nullptr, false, block_table, token_to_req, seq_lens,
+                     query_pos, out, workspace, workspace_bytes, stream);
 }
 
 QSA_API int qsa_select_fp8(const qsa_tensor* q, const qsa_tensor* kcache,
@@ -466,8 +510,105 @@ QSA_API int qsa_select_fp8(const qsa_tensor* q, const qsa_tensor* kcache,
                            const qsa_tensor* token_to_req, const qsa_tensor* seq_lens,
                            const qsa_tensor* query_pos, const qsa_tensor* out, void* workspace,
                            size_t workspace_bytes, qsa_stream stream) {
-  return select_impl(q, kcache, kscale, true, block_table, token_to_req, seq_lens, query_pos, out,
-                     workspace, workspace_bytes, stream);
+  return select_impl(q, nullptr, kcache, kscale, true, block_table, token_to_req, seq_lens,
+                     query_pos, out, workspace, workspace_bytes, stream);
+}
+
+QSA_API int qsa_select_weighted(const qsa_tensor* q, const qsa_tensor* weights,
+                                const qsa_tensor* kcache, const qsa_tensor* kscale,
+                                const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                                const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                                const qsa_tensor* out, void* workspace, size_t workspace_bytes,
+                                qsa_stream stream) {
+  g_last_error[0] = '\0';
+  if (!weights) return fail(QSA_ERR_NULL, "weights: descriptor is NULL");
+  return select_impl(q, weights, kcache, kscale, kscale != nullptr, block_table, token_to_req,
+                     seq_lens, query_pos, out, workspace, workspace_bytes, stream);
+}
+
+QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
+                             const qsa_tensor* kcache, const qsa_tensor* kscale,
+                             const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                             const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                             const qsa_tensor* logits, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  const bool e4m3 = kscale != nullptr;
+  SelectView v;
+  QSA_TRY(validate_select_inputs(q, weights, kcache, kscale, e4m3, block_table, token_to_req,
+                                 seq_lens, query_pos, &v));
+  QSA_TRY(check_logits("logits", logits, v.rows));
+  if (logits->shape[1] < v.width * QSA_PAGE_SLOTS) {
+    return fail(QSA_ERR_SHAPE, "logits: width %lld < block_table width x 128 = %lld",
+                (long long)logits->shape[1], (long long)(v.width * QSA_PAGE_SLOTS));
+  }
+  QSA_TRY(check_select_output("logits", logits, q, weights, kcache, kscale, e4m3, block_table,
+                              token_to_req, seq_lens, query_pos));
+  if (v.rows == 0) return QSA_OK;
+  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
+  qsa::SelectArgs a;
+  fill_select_args(a, q, weights, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
+                   query_pos, nullptr, nullptr, v);
+  a.logits_out = static_cast<float*>(logits->data);
+  a.logits_stride = logits_stride(logits);
+  a.logits_width = logits->shape[1];
+  const int err = qsa::launch_paged_logits(a, plan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "paged logits launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+QSA_API size_t qsa_topk_per_row_workspace_bytes(int64_t rows, int64_t logits_width) {
+  if (rows <= 0) return 0;
+  return qsa::plan_select(rows, (logits_width + QSA_PAGE_SLOTS - 1) / QSA_PAGE_SLOTS).bytes;
+}
+
+QSA_API int qsa_topk_per_row(const qsa_tensor* logits, const qsa_tensor* token_to_req,
+                             const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                             const qsa_tensor* out, void* workspace, size_t workspace_bytes,
+                             qsa_stream stream) {
+  g_last_error[0] = '\0';
+  if (!logits) return fail(QSA_ERR_NULL, "logits: descriptor is NULL");
+  const int64_t R = logits->shape[0];
+  QSA_TRY(check_logits("logits", logits, logits->ndim == 2 ? R : -1));
+  const int64_t rshape[1] = {R};
+  QSA_TRY(check_tensor("token_to_req", token_to_req, QSA_DTYPE_I32, 1, rshape));
+  QSA_TRY(check_contiguous("token_to_req", token_to_req));
+  const int64_t any1[1] = {-1};
+  QSA_TRY(check_tensor("seq_lens", seq_lens, QSA_DTYPE_I32, 1, any1));
+  QSA_TRY(check_contiguous("seq_lens", seq_lens));
+  QSA_TRY(check_tensor("query_pos", query_pos, QSA_DTYPE_I64, 1, rshape));
+  QSA_TRY(check_contiguous("query_pos", query_pos));
+  QSA_TRY(check_index_rows("out", out, R));
+  const int64_t N = seq_lens->shape[0];
+  if (R > 0 && N < 1) return fail(QSA_ERR_SHAPE, "seq_lens: no requests for %lld rows", (long long)R);
+  if (R > (int64_t)1 << 30) return fail(QSA_ERR_SHAPE, "logits: too many rows");
+  const qsa_tensor* ins[4] = {logits, token_to_req, seq_lens, query_pos};
+  const char* names[4] = {"logits", "token_to_req", "seq_lens", "query_pos"};
+  for (int i = 0; i < 4; ++i) {
+    if (overlaps(span_of(out), span_of(ins[i]))) return fail(QSA_ERR_ALIAS, "out overlaps %s", names[i]);
+  }
+  if (R == 0) return QSA_OK;
+  const int64_t width = logits->shape[1];
+  const int64_t pages = (width + QSA_PAGE_SLOTS - 1) / QSA_PAGE_SLOTS;
+  const qsa::SelectPlan plan = qsa::plan_select(R, pages);
+  Span guarded[5] = {span_of(logits), span_of(token_to_req), span_of(seq_lens),
+                     span_of(query_pos), span_of(out)};
+  QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 5));
+  qsa::SelectArgs a;
+  a.logits_in = static_cast<const float*>(logits->data);
+  a.logits_stride = logits_stride(logits);
+  a.logits_width = width;
+  a.max_visible = width;
+  a.token_to_req = static_cast<const int32_t*>(token_to_req->data);
+  a.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  a.query_pos = static_cast<const int64_t*>(query_pos->data);
+  a.out = static_cast<int32_t*>(out->data);
+  a.workspace = workspace;
+  a.rows = R;
+  a.num_reqs = N;
+  a.table_width = pages;
+  const int err = qsa::launch_select(a, plan, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "top-k launch failed (hipError %d)", err);
+  return QSA_OK;
 }
 
 QSA_API int qsa_sparse_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_tensor* v,

@@ -48,18 +48,26 @@ struct AttnPlan {
 
 AttnPlan plan_attn(int64_t rows);
 
+// Arguments of the selection family.  Scores come from fp16 keys (kcache),
+// e4m3 keys (kcodes + kscale) or a logits matrix (logits_in); they are
+// selected (launch_select) or written out as logits (launch_paged_logits).
 struct SelectArgs {
-  const uint16_t* q;          // [R,4,128] fp16
-  const uint16_t* kcache;     // [P,128,1,128] fp16 keys (NULL for an e4m3 cache)
-  const uint8_t* kcodes = nullptr;  // [P,128,1,128] e4m3 codes, with
-  const float* kscale = nullptr;    // [P,128] per-key scales (non-NULL selects e4m3)
-  const int32_t* block_table; // [N, >=W], row stride bt_stride
-  const int32_t* token_to_req;
-  const int32_t* seq_lens;
-  const int64_t* query_pos;
-  int32_t* out;               // [R,2051]
-  void* workspace;
-  int64_t rows, num_pages, num_reqs, table_width, bt_stride;
+  const uint16_t* q = nullptr;        // [R,4,128] fp16
+  const float* weights = nullptr;     // [R,4] per-head weights, or NULL (all 1)
+  const uint16_t* kcache = nullptr;   // [P,128,1,128] fp16 keys, or
+  const uint8_t* kcodes = nullptr;    // [P,128,1,128] e4m3 codes, with
+  const float* kscale = nullptr;      // [P,128] per-key scales (non-NULL selects e4m3)
+  const float* logits_in = nullptr;   // [R, >=logits_width] scores (top-k per row)
+  float* logits_out = nullptr;        // [R, logits_width] scores written (paged logits)
+  int64_t logits_stride = 0, logits_width = 0;
+  int64_t max_visible = 0;            // visible blocks are clamped to this
+  const int32_t* block_table = nullptr;  // [N, >=W], row stride bt_stride
+  const int32_t* token_to_req = nullptr;
+  const int32_t* seq_lens = nullptr;
+  const int64_t* query_pos = nullptr;
+  int32_t* out = nullptr;             // [R,2051]
+  void* workspace = nullptr;
+  int64_t rows = 0, num_pages = 0, num_reqs = 0, table_width = 0, bt_stride = 0;
 };
 
 struct AttnArgs {
@@ -74,6 +82,7 @@ struct AttnArgs {
 
 // Enqueue the kernels; return the hipError_t of the launch (0 = success).
 int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream);
+int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
 
 }  // namespace qsa

@@ -6,7 +6,10 @@
 // descending, block index ascending), expansion of each block to its 4
 // tokens, the tail, -1 padding -- no host sync anywhere.  The visible-block
 // rule and the page/slot addressing are those of the vllm qsa_cache.py page
-// (_build_qsa_metadata_kernel, compressed_qsa_slot_mapping).
+// (_build_qsa_metadata_kernel, compressed_qsa_slot_mapping).  The same
+// kernels serve the two-pass form of the "[XPU] Enable multiple key kernels
+// for sparse attention" page (paged logits with per-head weights, then a
+// top-k per row over the logits matrix).
 //
 // Design (MI355X / CDNA4):
 //  * Chunk kernel, grid = rows x chunks.  A chunk is `chunk_pages` cache
@@ -20,16 +23,21 @@
 //    onto subnormals), so the same fp16 MFMA scores both; the factor 2^8 is
 //    folded into the key's scale, which multiplies the head sum (a scale is
 //    >= 0, so scale * sum ReLU(q.k) = sum ReLU(q.(scale k))).
+//  * Per-head weights (optional, fp32 per row and head) multiply each
+//    head's ReLU term; weighted scores may be negative.
+//  * Sources and outputs: the chunk kernel scores keys (fp16 or e4m3) or
+//    reads scores from a logits matrix, and either selects (top-k) or
+//    writes the scores out as logits (-inf past the visible blocks).
 //  * Scoring: each wave scores tiles of 16 keys with
 //    v_mfma_f32_16x16x32_f16: A = the 4 query heads (rows 4..15 zero),
 //    B = 16 keys.  Lane l loads key (l % 16), bytes [64c + 16(l/16), +16)
 //    for c = 0..3, so every load instruction reads 16 keys x 64 contiguous
 //    bytes.  The 4 head dots of key n land in lane n, so ReLU + head sum is
-//    lane-local.  Scores go to LDS as order-preserving uint32 keys (a score
-//    is >= 0, so its IEEE bit pattern with the sign bit cleared orders like
-//    the value and maps -0 onto +0), and the first radix histogram is
-//    counted as the scores arrive, under the memory latency.
-//  * Chunk top-k: an MSB-first radix select (digits of 11, 11 and 9 bits)
+//    lane-local.  Scores go to LDS as order-preserving uint32 keys (the
+//    sign-magnitude bit pattern turned into an unsigned order, -0 mapped
+//    onto +0), and the first radix histogram is counted as the scores
+//    arrive, under the memory latency.
+//  * Chunk top-k: an MSB-first radix select (digits of 11, 11 and 10 bits)
 //    finds the k-th largest key; it stops early once the bin holding the
 //    k-th key is taken whole.  When keys equal to that threshold are only
 //    partly in, a second radix select over the complemented block index of
@@ -65,9 +73,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct SelectParams {
   const uint16_t* q;
+  const float* weights;    // [R,4] per-head weights, or NULL (all 1)
   const uint16_t* kcache;  // fp16 keys, or
   const uint8_t* kcodes;   // e4m3 codes [P,128,1,128] with
   const float* kscale;     // one scale per key [P,128]
+  const float* logits_in;  // scores given as a logits matrix (top-k per row)
+  float* logits_out;       // scores written out (paged logits)
+  int64_t logits_stride, logits_width;
+  int64_t max_visible;     // visible blocks are clamped to this
   const int32_t* block_table;
   const int32_t* token_to_req;
   const int32_t* seq_lens;
@@ -98,7 +111,8 @@ struct Row {
 
 // Visible blocks V = max(0, min(floor((qp+1)/4), floor(L/4))) and tail
 // T = min(qp+1, L) - 4V of query row r.  A request id outside [0, N) makes
-// the row empty; V never exceeds what the block table can map.
+// the row empty; V never exceeds what the block table can map (or, for a
+// logits source, the logits width).
 __device__ Row row_setup(const SelectParams& p, int64_t r) {
   Row row;
   const int64_t req = p.token_to_req[r];
@@ -112,13 +126,21 @@ __device__ Row row_setup(const SelectParams& p, int64_t r) {
     int64_t v = max((int64_t)0, min(a, b));
     const int64_t end = min(upto, seq_len);
     row.tail = (int)max((int64_t)0, min((int64_t)(kRatio - 1), end - kRatio * v));
-    row.visible = min(v, p.table_width * kPageSlots);
+    row.visible = min(v, p.max_visible);
   }
   row.nchunks = max((int64_t)1, (row.visible + p.chunk_blocks - 1) / p.chunk_blocks);
   return row;
 }
 
-__device__ __forceinline__ uint32_t digit0(uint32_t key) { return (key >> 20) & (kBins - 1); }
+// Radix digits of a 32-bit key, most significant first: 11, 11 and 10 bits.
+__device__ __forceinline__ uint32_t digit0(uint32_t key) { return key >> 21; }
+
+// Order-preserving 32-bit key of a score (any finite value or -inf): larger
+// key <=> larger score, and -0 maps onto +0, so equal scores give equal keys.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Count the keys that match `prefix` under `mask` into h by the digit
 // (key >> SHIFT) & (NB - 1).
@@ -193,7 +215,7 @@ __device__ void radix_pick(const uint32_t* h, uint32_t krem, Scratch& s) {
 }
 
 // Radix select of the k-th largest (1 <= k <= n) of the keys key_at(i),
-// i < n (bit 31 clear).  On entry hist0 holds the histogram of digit0 over
+// i < n.  On entry hist0 holds the histogram of digit0 over
 // all n keys and every thread has passed a barrier since; hist1 is a second
 // histogram; both have kBins entries, are 16-byte aligned and may be
 // overwritten.  Returns T and need_eq such that the top-k are the keys > T
@@ -207,24 +229,24 @@ __device__ void radix_select(KeyAt key_at, int n, int k, Scratch& s, uint32_t* h
   for (int i = tid; i < kBins; i += NT) hist1[i] = 0;
   if (tid < 64) radix_pick<kBins>(hist0, (uint32_t)k, s);
   __syncthreads();
-  uint32_t prefix = s.pick[0] << 20;
-  uint32_t mask = (uint32_t)(kBins - 1) << 20;
+  uint32_t prefix = s.pick[0] << 21;
+  uint32_t mask = (uint32_t)(kBins - 1) << 21;
   uint32_t krem = s.pick[1];
   bool whole = s.pick[2] == krem;  // the boundary bin is taken entirely
   if (!whole) {
-    radix_count<NT, 9, kBins>(key_at, n, mask, prefix, hist1);
-    for (int i = tid; i < 512; i += NT) hist0[i] = 0;
+    radix_count<NT, 10, kBins>(key_at, n, mask, prefix, hist1);
+    for (int i = tid; i < 1024; i += NT) hist0[i] = 0;
     __syncthreads();
     if (tid < 64) radix_pick<kBins>(hist1, krem, s);
     __syncthreads();
-    prefix |= s.pick[0] << 9;
-    mask |= (uint32_t)(kBins - 1) << 9;
+    prefix |= s.pick[0] << 10;
+    mask |= (uint32_t)(kBins - 1) << 10;
     krem = s.pick[1];
     whole = s.pick[2] == krem;
     if (!whole) {
-      radix_count<NT, 0, 512>(key_at, n, mask, prefix, hist0);
+      radix_count<NT, 0, 1024>(key_at, n, mask, prefix, hist0);
       __syncthreads();
-      if (tid < 64) radix_pick<512>(hist0, krem, s);
+      if (tid < 64) radix_pick<1024>(hist0, krem, s);
       __syncthreads();
       T = prefix | s.pick[0];
       need_eq = (int)s.pick[1];
@@ -448,13 +470,54 @@ struct ChunkSmem {
   } u;
 };
 
-// Where a chunk's scores go: order-preserving keys in LDS (a score is >= 0:
-// its bit pattern with the sign cleared orders like the value and maps -0
-// onto +0), plus the first radix histogram when the chunk needs a select.
-__device__ __forceinline__ void store_score(ChunkSmem& sm, int i, float sc, bool select) {
-  const uint32_t key = __float_as_uint(sc) & 0x7FFFFFFFu;
-  sm.keys[i] = key;
-  if (select) atomicAdd(&sm.hist0[digit0(key)], 1u);
+// Where a chunk's scores go.  For a selection: order-preserving keys in
+// LDS, plus the first radix histogram when the chunk needs a select.
+struct LdsSink {
+  ChunkSmem* sm;
+  bool select;
+  __device__ __forceinline__ void operator()(int i, float sc) const {
+    const uint32_t key = score_key(sc);
+    sm->keys[i] = key;
+    if (select) atomicAdd(&sm->hist0[digit0(key)], 1u);
+  }
+};
+
+// For paged logits: the score itself, staged in LDS; the chunk's logits
+// go out in one coalesced pass once the chunk is scored (small scattered
+// stores in the middle of the key stream slow the stream down).
+struct LogitsSink {
+  ChunkSmem* sm;
+  __device__ __forceinline__ void operator()(int i, float sc) const {
+    sm->keys[i] = __float_as_uint(sc);
+  }
+};
+
+// The row's per-head weights (all 1 without a weights tensor) and the
+// weighted sum of the ReLU'd head dots of one key (acc[h] = head h).
+struct HeadWeights {
+  float w[kSelHeads];
+};
+
+__device__ __forceinline__ HeadWeights head_weights(const SelectParams& p, int64_t r) {
+  HeadWeights hw;
+  if (p.weights) {
+    const float4 v = *reinterpret_cast<const float4*>(p.weights + r * kSelHeads);
+    hw.w[0] = v.x;
+    hw.w[1] = v.y;
+    hw.w[2] = v.z;
+    hw.w[3] = v.w;
+  } else {
+#pragma unroll
+    for (int h = 0; h < kSelHeads; ++h) hw.w[h] = 1.f;
+  }
+  return hw;
+}
+
+__device__ __forceinline__ float head_sum(const floatx4& acc, const HeadWeights& hw) {
+  float sum = hw.w[0] * fmaxf(acc[0], 0.f);
+#pragma unroll
+  for (int h = 1; h < kSelHeads; ++h) sum += hw.w[h] * fmaxf(acc[h], 0.f);
+  return sum;
 }
 
 // The physical pages of a chunk (at most 32): lane i holds the page of the
@@ -500,9 +563,10 @@ __device__ __forceinline__ int tile_keys(int t, int tt, int ntiles, int nblk, ui
 
 // fp16 keys.  MFMA k step c covers dims [32c, 32c + 32): lane (n + 16g)
 // holds dims [32c + 8g, +8) of key n (B) or of head n (A).
+template <typename Sink>
 __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem& sm, int64_t r,
                                                 int64_t req, int64_t chunk_base, int nblk,
-                                                bool select) {
+                                                const Sink& sink) {
   constexpr int kUnroll = 4;  // tiles in flight per wave (4 KiB each)
   constexpr int kPageBytes = kPageSlots * kSelDim * 2;
   const int lane = threadIdx.x & 63;
@@ -517,6 +581,7 @@ __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem
       qa[c] = *reinterpret_cast<const half8*>(p.q + (r * kSelHeads + n) * kSelDim + 32 * c + 8 * g);
     }
   }
+  const HeadWeights hw = head_weights(p, r);
   bool page_valid;
   const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
@@ -582,9 +647,8 @@ __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem
       }
       __builtin_amdgcn_wave_barrier();
       // lanes 0..15 hold heads 0..3 of key n
-      const float sc = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) +
-                       fmaxf(acc[3], 0.f);
-      if (g == 0 && 16 * t + n < nblk) store_score(sm, 16 * t + n, sc, select);
+      const float sc = head_sum(acc, hw);
+      if (g == 0 && 16 * t + n < nblk) sink(16 * t + n, sc);
     }
   }
 }
@@ -608,9 +672,10 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
 // visit the 128 dims, so each lane takes 32 contiguous bytes of its key:
 // MFMA k step c gives lane (n + 16g) dims [32g + 8c, +8) of key n (B) or of
 // head n (A).
+template <typename Sink>
 __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm, int64_t r,
                                                  int64_t req, int64_t chunk_base, int nblk,
-                                                 bool select) {
+                                                 const Sink& sink) {
   constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each)
   constexpr int kPageBytes = kPageSlots * kSelDim;
   constexpr int kScaleBytes = kPageSlots * 4;
@@ -626,6 +691,7 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
       qa[c] = *reinterpret_cast<const half8*>(p.q + (r * kSelHeads + n) * kSelDim + 32 * g + 8 * c);
     }
   }
+  const HeadWeights hw = head_weights(p, r);
   bool page_valid;
   const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
@@ -696,37 +762,90 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[2], e4m3x8_to_half8(hi[0], hi[1]), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[3], e4m3x8_to_half8(hi[2], hi[3]), acc, 0, 0, 0);
       __builtin_amdgcn_wave_barrier();
-      const float sum = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) +
-                        fmaxf(acc[3], 0.f);
+      const float sum = head_sum(acc, hw);
       // scale * 2^8 is exact, so this is one rounding of scale * code-sum
       const float sc = sum * (scale[u] * 256.f);
-      if (g == 0 && 16 * t + n < nblk) store_score(sm, 16 * t + n, sc, select);
+      if (g == 0 && 16 * t + n < nblk) sink(16 * t + n, sc);
       issue_scale(u, t + kChunkWaves * kUnroll);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-template <bool kE4M3>
-__global__ __launch_bounds__(kChunkThreads) void qsa_select_chunk_kernel(SelectParams p) {
+// Scores given as a logits matrix: the chunk's nblk columns of row r.
+template <typename Sink>
+__device__ __forceinline__ void score_chunk_logits(const SelectParams& p, int64_t r,
+                                                   int64_t chunk_base, int nblk, const Sink& sink) {
+  constexpr int kUnroll = 8;
+  const float* src = p.logits_in + r * p.logits_stride + chunk_base;
+#pragma unroll 1
+  for (int i0 = threadIdx.x; i0 < nblk; i0 += kChunkThreads * kUnroll) {
+    float v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kChunkThreads;
+      v[u] = i < nblk ? __builtin_nontemporal_load(src + i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kChunkThreads;
+      if (i < nblk) sink(i, v[u]);
+    }
+  }
+}
+
+enum : int { kSrcF16 = 0, kSrcE4M3 = 1, kSrcLogits = 2 };
+
+// kSrc: where the scores come from; kLogitsOut: write them as a logits row
+// (and -inf past the visible blocks) instead of selecting.
+template <int kSrc, bool kLogitsOut>
+__global__ __launch_bounds__(kChunkThreads, 4) void qsa_select_chunk_kernel(SelectParams p) {
   __shared__ ChunkSmem sm;
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x / p.chunks_per_row;
   const int64_t chunk = blockIdx.x % p.chunks_per_row;
   if (r >= p.rows) return;
   const Row row = row_setup(p, r);
-  if (chunk >= row.nchunks) return;
   const int64_t chunk_base = chunk * p.chunk_blocks;
   const int nblk = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
+
+  if constexpr (kLogitsOut) {
+    float* out_row = p.logits_out + r * p.logits_stride;
+    if (nblk > 0) {
+      const LogitsSink sink{&sm};
+      if constexpr (kSrc == kSrcE4M3) {
+        score_chunk_e4m3(p, sm, r, row.req, chunk_base, nblk, sink);
+      } else {
+        score_chunk_f16(p, sm, r, row.req, chunk_base, nblk, sink);
+      }
+      __syncthreads();
+      for (int i = tid; i < nblk; i += kChunkThreads) {
+        __builtin_nontemporal_store(__uint_as_float(sm.keys[i]), out_row + chunk_base + i);
+      }
+    }
+    // -inf from the row's end (or the chunk's start) to the chunk's end; the
+    // last chunk column also covers the columns past all chunks
+    const int64_t lo = max(row.visible, chunk_base);
+    const int64_t hi = chunk == p.chunks_per_row - 1
+                           ? p.logits_width
+                           : min(chunk_base + (int64_t)p.chunk_blocks, p.logits_width);
+    for (int64_t b = lo + tid; b < hi; b += kChunkThreads) out_row[b] = -__builtin_inff();
+    return;
+  }
+
+  if (chunk >= row.nchunks) return;
   const bool select = nblk > kTopKBlocks;
   if (select) {
     for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
     __syncthreads();
   }
-  if (kE4M3) {
-    score_chunk_e4m3(p, sm, r, row.req, chunk_base, nblk, select);
+  const LdsSink sink{&sm, select};
+  if constexpr (kSrc == kSrcLogits) {
+    score_chunk_logits(p, r, chunk_base, nblk, sink);
+  } else if constexpr (kSrc == kSrcE4M3) {
+    score_chunk_e4m3(p, sm, r, row.req, chunk_base, nblk, sink);
   } else {
-    score_chunk_f16(p, sm, r, row.req, chunk_base, nblk, select);
+    score_chunk_f16(p, sm, r, row.req, chunk_base, nblk, sink);
   }
   __syncthreads();
 
@@ -867,13 +986,20 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
 
 }  // namespace
 
-int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
-  if (a.rows == 0) return 0;
+namespace {
+
+SelectParams make_params(const SelectArgs& a, const SelectPlan& plan) {
   SelectParams p;
   p.q = a.q;
+  p.weights = a.weights;
   p.kcache = a.kcache;
   p.kcodes = a.kcodes;
   p.kscale = a.kscale;
+  p.logits_in = a.logits_in;
+  p.logits_out = a.logits_out;
+  p.logits_stride = a.logits_stride;
+  p.logits_width = a.logits_width;
+  p.max_visible = a.max_visible;
   p.block_table = a.block_table;
   p.token_to_req = a.token_to_req;
   p.seq_lens = a.seq_lens;
@@ -890,17 +1016,43 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
   p.chunks_per_row = plan.chunks_per_row;
   p.chunk_blocks = plan.chunk_pages * kPageSlots;
   p.cand_cap = (int)plan.cand_cap;
+  return p;
+}
+
+template <int kSrc, bool kLogitsOut>
+void launch_chunks(const SelectParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut>),
+                     dim3((unsigned)(p.rows * p.chunks_per_row)), dim3(kChunkThreads), 0, s, p);
+}
+
+}  // namespace
+
+int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
+  if (a.rows == 0) return 0;
+  const SelectParams p = make_params(a, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a.kscale) {
-    hipLaunchKernelGGL(qsa_select_chunk_kernel<true>, dim3((unsigned)(a.rows * plan.chunks_per_row)),
-                       dim3(kChunkThreads), 0, s, p);
+  if (a.logits_in) {
+    launch_chunks<kSrcLogits, false>(p, s);
+  } else if (a.kscale) {
+    launch_chunks<kSrcE4M3, false>(p, s);
   } else {
-    hipLaunchKernelGGL(qsa_select_chunk_kernel<false>, dim3((unsigned)(a.rows * plan.chunks_per_row)),
-                       dim3(kChunkThreads), 0, s, p);
+    launch_chunks<kSrcF16, false>(p, s);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.chunks_per_row == 1) return (int)err;
   hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+int launch_paged_logits(const SelectArgs& a, const SelectPlan& plan, void* stream) {
+  if (a.rows == 0) return 0;
+  const SelectParams p = make_params(a, plan);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.kscale) {
+    launch_chunks<kSrcE4M3, true>(p, s);
+  } else {
+    launch_chunks<kSrcF16, true>(p, s);
+  }
   return (int)hipGetLastError();
 }
 

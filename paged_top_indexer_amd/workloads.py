@@ -147,6 +147,15 @@ def with_fp8_keys(w: "Workload", integer: bool) -> "Workload":
     return w
 
 
+def head_weights(rng: np.random.Generator, rows: int, integer: bool = False) -> np.ndarray:
+    """Per-head weights [rows, 4] float32: integers in [-3, 3] (exact sums
+    on integer inputs), or uniform in [-0.5, 1.5] (mostly positive, some
+    negative)."""
+    if integer:
+        return rng.integers(-3, 4, size=(rows, SEL_HEADS)).astype(np.float32)
+    return rng.uniform(-0.5, 1.5, size=(rows, SEL_HEADS)).astype(np.float32)
+
+
 def pages_needed(seq_len: int) -> int:
     """Pages a request of seq_len tokens occupies in the compressed cache."""
     return -(-int(seq_len) // TOKENS_PER_PAGE)

@@ -70,11 +70,15 @@ def check_attn(got16: np.ndarray, want64: np.ndarray, what: str = "") -> float:
     return err
 
 
-def check_select_band(gpu: np.ndarray, ref: np.ndarray, orc, inputs, rows) -> None:
+def check_select_band(gpu: np.ndarray, ref: np.ndarray, orc, inputs, rows,
+                      row_scores=None) -> None:
     """The N(0,1) acceptance rule on the listed rows (inputs as passed to the
     oracle -- six for an fp16 cache, seven with codes and scales for an e4m3
-    cache -- and rows as indices into them)."""
-    if len(inputs) == 7:
+    cache -- and rows as indices into them).  row_scores(r), when given,
+    returns the oracle's scores of row r (e.g. weighted ones)."""
+    if row_scores is not None:
+        q, *_, bt, t2r, sl, qp = inputs
+    elif len(inputs) == 7:
         q, codes, scales, bt, t2r, sl, qp = inputs
         row_scores = lambda r: orc.row_scores_fp8(r, *inputs)  # noqa: E731
     else:

@@ -311,3 +311,88 @@ def test_decode_step_fp8_checks():
     assert call(out=mk(g, B.F16, (2, 3, 256), 2, ptr=s["kscale"].data)) == ALIAS
     assert call(ws_bytes=wsb - 256) == WORKSPACE
     assert call(kscale=mk(g, B.F32, (8, 127), 4)) == SHAPE
+
+
+# ---------------------------------------------------------------------------
+# per-head weights, paged logits, top-k per row
+
+def call_weighted(a, ws, ws_bytes, weights, kscale=None):
+    lib = B.library()
+    opt = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lib.qsa_select_weighted(ctypes.byref(a["q"]), opt(weights), ctypes.byref(a["kcache"]),
+                                   opt(kscale), *[ctypes.byref(a[k]) for k in
+                                                  ("bt", "t2r", "sl", "qp", "out")],
+                                   ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_select_weighted_checks():
+    f, a, ws, wsb = select_args(R=4, W=40)
+    w = mk(f, B.F32, (4, 4), 4)
+    assert call_weighted(a, ws, wsb, None) == NULL
+    assert call_weighted(a, ws, wsb, mk(f, B.F16, (4, 4), 2)) == DTYPE
+    assert call_weighted(a, ws, wsb, mk(f, B.F32, (4, 3), 4)) == SHAPE
+    assert call_weighted(a, ws, wsb, mk(f, B.F32, (5, 4), 4)) == SHAPE
+    assert call_weighted(a, ws, wsb, mk(f, B.F32, (4, 4), 4, ptr=f.alloc(4096) + 4)) == LAYOUT
+    a2 = dict(a, out=mk(f, B.I32, (4, 2051), 4, ptr=w.data))
+    assert call_weighted(a2, ws, wsb, w) == ALIAS
+    assert call_weighted(a, ws, wsb - 1, w) == WORKSPACE
+    assert call_weighted(a, w.data, wsb, w) == ALIAS
+    # an e4m3 cache needs its scales, an fp16 cache must not get them
+    f8, a8, ws8, wsb8 = fp8_args()
+    assert call_weighted(a8, ws8, wsb8, mk(f8, B.F32, (4, 4), 4)) == DTYPE
+    assert call_weighted(a, ws, wsb, w, kscale=mk(f, B.F32, (8, 128), 4)) == DTYPE
+
+
+def call_logits(a, logits, weights=None, kscale=None):
+    lib = B.library()
+    opt = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lib.qsa_paged_logits(ctypes.byref(a["q"]), opt(weights), ctypes.byref(a["kcache"]),
+                                opt(kscale), *[ctypes.byref(a[k]) for k in
+                                               ("bt", "t2r", "sl", "qp")],
+                                opt(logits), None)
+
+
+def test_paged_logits_checks():
+    f, a, ws, wsb = select_args(R=4, W=40)
+    assert call_logits(a, None) == NULL
+    assert call_logits(a, mk(f, B.F16, (4, 5120), 2)) == DTYPE
+    assert call_logits(a, mk(f, B.F32, (4, 5119), 4)) == SHAPE
+    assert call_logits(a, mk(f, B.F32, (3, 5120), 4)) == SHAPE
+    assert call_logits(a, mk(f, B.F32, (4, 5120), 4, stride=(10240, 2))) == LAYOUT
+    assert call_logits(a, mk(f, B.F32, (4, 5120), 4, stride=(5000, 1))) == LAYOUT
+    assert call_logits(a, mk(f, B.F32, (4, 5120), 4, ptr=a["q"].data)) == ALIAS
+    assert call_logits(a, mk(f, B.F32, (4, 5120), 4), weights=mk(f, B.F32, (4, 2), 4)) == SHAPE
+
+
+def test_paged_logits_zero_rows():
+    f, a, ws, wsb = select_args(R=0, W=40)
+    assert call_logits(a, mk(f, B.F32, (0, 5120), 4)) == OK
+
+
+def call_topk(lg, t2r, sl, qp, out, ws, ws_bytes):
+    lib = B.library()
+    return lib.qsa_topk_per_row(*[ctypes.byref(x) for x in (lg, t2r, sl, qp, out)],
+                                ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_topk_per_row_checks():
+    f = Fake()
+    R, Wl = 4, 9000
+    lg = mk(f, B.F32, (R, Wl), 4)
+    t2r, sl, qp = mk(f, B.I32, (R,), 4), mk(f, B.I32, (2,), 4), mk(f, B.I64, (R,), 8)
+    out = mk(f, B.I32, (R, 2051), 4)
+    wsb = B.topk_per_row_workspace_bytes(R, Wl)
+    assert wsb > 0 and B.topk_per_row_workspace_bytes(0, Wl) == 0
+    ws = f.alloc(wsb)
+    assert call_topk(mk(f, B.F16, (R, Wl), 2), t2r, sl, qp, out, ws, wsb) == DTYPE
+    assert call_topk(mk(f, B.F32, (R, 0), 4), t2r, sl, qp, out, ws, wsb) == SHAPE
+    assert call_topk(mk(f, B.F32, (R, Wl), 4, stride=(2 * Wl, 2)), t2r, sl, qp, out, ws, wsb) == LAYOUT
+    assert call_topk(lg, mk(f, B.I32, (R + 1,), 4), sl, qp, out, ws, wsb) == SHAPE
+    assert call_topk(lg, t2r, mk(f, B.I32, (0,), 4), qp, out, ws, wsb) == SHAPE
+    assert call_topk(lg, t2r, sl, mk(f, B.I32, (R,), 4), out, ws, wsb) == DTYPE
+    assert call_topk(lg, t2r, sl, qp, mk(f, B.I32, (R, 2048), 4), ws, wsb) == SHAPE
+    assert call_topk(lg, t2r, sl, qp, mk(f, B.I32, (R, 2051), 4, ptr=lg.data), ws, wsb) == ALIAS
+    assert call_topk(lg, t2r, sl, qp, out, ws, wsb - 1) == WORKSPACE
+    assert call_topk(lg, t2r, sl, qp, out, lg.data, wsb) == ALIAS
+    assert call_topk(mk(f, B.F32, (0, Wl), 4), mk(f, B.I32, (0,), 4), sl, mk(f, B.I64, (0,), 8),
+                     mk(f, B.I32, (0, 2051), 4), 0, 0) == OK
