@@ -26,6 +26,11 @@ Parity status of each function (the pins live in ``tests/oracle_pins.py``):
   the unweighted selection; numpy float64 gather + weights; top-k per row
   against numpy's lexsort on arbitrary logits (negative values, signed zeros,
   repeats, junk past the visible blocks).
+* ``build_metadata`` pinned: batches built request by request (decode,
+  speculative, prefill chunks, empty queries, padding tokens, holes in the
+  block table, invalid common slots) whose per-token request, position,
+  visible blocks, slots and k work items are known by construction; numpy's
+  searchsorted for the request search on random batches.
 """
 
 from __future__ import annotations
@@ -97,6 +102,9 @@ class Oracle:
         lib.qsa_oracle_paged_logits.restype = ctypes.c_int
         lib.qsa_oracle_topk_per_row.argtypes = [i64, i64, p, i64, i64, p, p, p, p]
         lib.qsa_oracle_topk_per_row.restype = ctypes.c_int
+        lib.qsa_oracle_build_metadata.argtypes = [i64, i64, p, p, p, p, i64, i64, i64, i64, i64,
+                                                   p, p, p, p, p, i64]
+        lib.qsa_oracle_build_metadata.restype = ctypes.c_int
         lib.qsa_oracle_mutant.argtypes = []
         lib.qsa_oracle_mutant.restype = ctypes.c_int
         self.lib = lib
@@ -272,6 +280,36 @@ class Oracle:
             self._ptr(sl), self._ptr(qp), self._ptr(out))
         self._check(rc)
         return out
+
+    def build_metadata(self, query_start_loc, seq_lens, block_table, num_tokens: int,
+                       storage_block_size: int = 128, compress_ratio: int = 4,
+                       circular_buffer_size: int = 0, common_slot_mapping=None,
+                       max_num_work: int = 0, with_slots: bool = True) -> dict:
+        """Per-token metadata (token_to_req, logical_positions,
+        visible_blocks, slot_mapping) and the k work items [max_num_work, 2]."""
+        qsl = self._c(query_start_loc, np.int32)
+        sl = self._c(seq_lens, np.int32)
+        bt = self._c(block_table, np.int32)
+        N = sl.shape[0]
+        assert qsl.shape == (N + 1,) and bt.ndim == 2 and bt.shape[0] == N
+        T = int(num_tokens)
+        csm = None if common_slot_mapping is None else self._c(common_slot_mapping, np.int64)
+        if csm is not None:
+            assert csm.shape == (T,)
+        t2r = np.empty(T, np.int32)
+        lp = np.empty(T, np.int64)
+        vis = np.empty(T, np.int32)
+        slots = np.empty(T, np.int64) if with_slots else None
+        work = np.empty((int(max_num_work), 2), np.int32) if max_num_work > 0 else None
+        rc = self.lib.qsa_oracle_build_metadata(
+            N, T, self._ptr(qsl), self._ptr(sl), None if csm is None else self._ptr(csm),
+            self._ptr(bt), bt.shape[1], bt.shape[1], int(storage_block_size), int(compress_ratio),
+            int(circular_buffer_size), self._ptr(t2r), self._ptr(lp), self._ptr(vis),
+            None if slots is None else self._ptr(slots), None if work is None else self._ptr(work),
+            int(max_num_work))
+        self._check(rc)
+        return {"token_to_req": t2r, "logical_positions": lp, "visible_blocks": vis,
+                "slot_mapping": slots, "k_work": work}
 
     def sparse_attn(self, q, kv, indices, scale: float) -> np.ndarray:
         """[R,3,256] float64 attention output.  kv is [..., 512] fp16 with

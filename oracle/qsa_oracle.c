@@ -48,6 +48,13 @@
  *   = the selection above applied to a given logits row, reading its first V
  *   entries only.
  *
+ *   metadata (the vllm qsa_cache.py page, _build_qsa_metadata_kernel and
+ *   its torch fallback): from cumulative query starts and sequence lengths,
+ *   per token its request (the last request whose query starts at or
+ *   before it), its logical position, its visible blocks, its slot in the
+ *   compressed cache (or in the raw-key ring), and the per-request k work
+ *   items, laid out request after request.
+ *
  * Precision: fp16 inputs are widened to double with a conversion written
  * from the IEEE 754 binary16 definition; every dot product and softmax is
  * evaluated in double.  A selection score is rounded once to binary32 at
@@ -550,6 +557,126 @@ int qsa_oracle_sparse_attn(int64_t R, int64_t num_tokens, const uint16_t* q,
   free(logit);
   free(kq);
   return rc;
+}
+
+/* floor(a / b) for b > 0 (C division truncates toward zero). */
+static int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && (a < 0)) q -= 1;
+  return q;
+}
+
+/*
+ * QSA metadata for num_tokens tokens of num_reqs requests.
+ *
+ *   query_start_loc [N+1] int32: query tokens of request r are
+ *       [query_start_loc[r], query_start_loc[r+1]); mapped tokens are those
+ *       below query_start_loc[N], the rest are padding.
+ *   seq_lens [N] int32; block_table [N][table_width] int32 with row stride
+ *   table_stride; common_slot_mapping [num_tokens] int64 or NULL (all >= 0).
+ *   storage_block_size: compressed slots per cache block; compress_ratio;
+ *   circular_buffer_size: > 0 selects the raw-key ring owner.
+ *
+ * Outputs per token: token_to_req (0 for padding), logical_positions (-1
+ * for padding), visible_blocks, slot_mapping (NULL: not written; -1 where
+ * the token writes no slot); k_work [max_num_work][2] (NULL: not written):
+ * (request, index of the item inside the request), -1 past the last item.
+ */
+int qsa_oracle_build_metadata(int64_t num_reqs, int64_t num_tokens,
+                              const int32_t* query_start_loc, const int32_t* seq_lens,
+                              const int64_t* common_slot_mapping, const int32_t* block_table,
+                              int64_t table_width, int64_t table_stride,
+                              int64_t storage_block_size, int64_t compress_ratio,
+                              int64_t circular_buffer_size, int32_t* token_to_req,
+                              int64_t* logical_positions, int32_t* visible_blocks,
+                              int64_t* slot_mapping, int32_t* k_work, int64_t max_num_work) {
+  if (num_reqs < 1 || storage_block_size < 1 || compress_ratio < 1 || circular_buffer_size < 0) {
+    return OR_ERR_ARG;
+  }
+  const int64_t num_mapped = query_start_loc[num_reqs];
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const int mapped = t < num_mapped;
+    int64_t r = 0;
+    int64_t lp = -1;
+    int64_t seq = 0;
+    if (mapped) {
+      /* the last request whose query starts at or before t */
+      for (int64_t c = 0; c < num_reqs; ++c) {
+#if QSA_ORACLE_MUTANT == 17
+        if (query_start_loc[c] < t) r = c; /* planted: a request's first token given to the one before */
+#else
+        if (query_start_loc[c] <= t) r = c;
+#endif
+      }
+      const int64_t start = query_start_loc[r];
+      const int64_t qlen = (int64_t)query_start_loc[r + 1] - start;
+      seq = seq_lens[r];
+      lp = seq - qlen + (t - start);
+#if QSA_ORACLE_MUTANT == 18
+      lp = seq + (t - start) - 1; /* planted: positions counted from the end of the sequence */
+#endif
+    }
+    token_to_req[t] = (int32_t)r;
+    logical_positions[t] = lp;
+    int64_t v = floor_div(lp + 1, compress_ratio);
+    const int64_t cap = floor_div(seq, compress_ratio);
+    if (cap < v) v = cap;
+    if (v < 0) v = 0;
+    visible_blocks[t] = (int32_t)v;
+    if (!slot_mapping) continue;
+    int64_t slot = -1;
+    if (circular_buffer_size > 0) {
+      /* raw-key ring: a request's last circular_buffer_size query tokens
+       * write slot (position mod ring size) of its first block */
+      if (mapped && lp >= 0 && t + circular_buffer_size >= query_start_loc[r + 1] &&
+          table_width > 0) {
+        const int64_t phys = block_table[r * table_stride];
+        if (phys >= 0) slot = phys * circular_buffer_size + lp % circular_buffer_size;
+      }
+    } else if (compress_ratio != 1) {
+      /* compressed cache: the token that completes a group of compress_ratio
+       * tokens writes compressed position lp / compress_ratio */
+      const int64_t cp = (lp > 0 ? lp : 0) / compress_ratio;
+      const int64_t lb = cp / storage_block_size;
+#if QSA_ORACLE_MUTANT == 19
+      int ok = mapped && lp >= 0 && lp % compress_ratio == 0 && lb < table_width; /* planted: group start */
+#else
+      int ok = mapped && lp >= 0 && (lp + 1) % compress_ratio == 0 && lb < table_width;
+#endif
+      if (ok) {
+        const int64_t phys = block_table[r * table_stride + lb];
+        ok = phys >= 0 && (!common_slot_mapping || common_slot_mapping[t] >= 0);
+        if (ok) slot = phys * storage_block_size + cp % storage_block_size;
+      }
+    } else {
+      /* no compression and no ring: the main cache's own slots */
+      slot = common_slot_mapping ? common_slot_mapping[t] : -1;
+    }
+    slot_mapping[t] = slot;
+  }
+  if (k_work) {
+    int64_t w = 0;
+    for (int64_t r = 0; r < num_reqs; ++r) {
+      const int64_t qlen = (int64_t)query_start_loc[r + 1] - query_start_loc[r];
+      const int64_t chunk_start = (int64_t)seq_lens[r] - qlen;
+      int64_t groups = floor_div(seq_lens[r], compress_ratio) - floor_div(chunk_start, compress_ratio);
+#if QSA_ORACLE_MUTANT != 20
+      if (groups < 1) groups = 1; /* the first item also commits the raw suffix */
+#else
+      if (groups < 0) groups = 0; /* planted: no item without a completed group */
+#endif
+      const int64_t count = qlen > 0 ? groups : 0;
+      for (int64_t i = 0; i < count && w < max_num_work; ++i, ++w) {
+        k_work[2 * w] = (int32_t)r;
+        k_work[2 * w + 1] = (int32_t)i;
+      }
+    }
+    for (; w < max_num_work; ++w) {
+      k_work[2 * w] = -1;
+      k_work[2 * w + 1] = -1;
+    }
+  }
+  return OR_OK;
 }
 
 /* Which mistake this build carries (0 = none). */

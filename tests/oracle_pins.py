@@ -476,6 +476,126 @@ def pin_topk_per_row_lexsort(orc):
         assert np.array_equal(got[r], want), f"row {r}"
 
 
+# ---------------------------------------------------------------------------
+# metadata builder
+
+def metadata_batch(seed: int, kinds, pad: int, width: int):
+    """A batch built request by request; returns the builder's inputs and the
+    expected outputs known by construction (no request search anywhere).
+    kinds: per request (seq_len, query_len)."""
+    rng = np.random.default_rng(seed)
+    N = len(kinds)
+    qsl = np.zeros(N + 1, np.int32)
+    for r, (L, q) in enumerate(kinds):
+        qsl[r + 1] = qsl[r] + q
+    mapped = int(qsl[-1])
+    T = mapped + pad
+    sl = np.array([L for L, _ in kinds], np.int32)
+    bt = rng.integers(0, 5000, size=(N, width)).astype(np.int32)
+    bt[rng.random(bt.shape) < 0.1] = -1                      # holes in the table
+    csm = rng.integers(0, 1 << 20, size=T).astype(np.int64)
+    csm[rng.random(T) < 0.05] = -1                           # tokens the main cache skips
+    want = {"token_to_req": np.zeros(T, np.int32), "logical_positions": np.full(T, -1, np.int64),
+            "visible_blocks": np.zeros(T, np.int32), "slot_mapping": np.full(T, -1, np.int64),
+            "ring": np.full(T, -1, np.int64), "work": []}
+    for r, (L, q) in enumerate(kinds):
+        for i in range(q):
+            t = int(qsl[r]) + i
+            pos = L - q + i
+            want["token_to_req"][t] = r
+            want["logical_positions"][t] = pos
+            V, _ = brute_visible(L, pos)
+            want["visible_blocks"][t] = V
+            if (pos + 1) % RATIO == 0:                       # token closing a group
+                group = (pos + 1) // RATIO - 1
+                blk = group // 128
+                if blk < width and bt[r, blk] >= 0 and csm[t] >= 0:
+                    want["slot_mapping"][t] = int(bt[r, blk]) * 128 + group % 128
+            if i >= q - 8 and bt[r, 0] >= 0:                  # last 8 tokens: the ring
+                want["ring"][t] = int(bt[r, 0]) * 8 + pos % 8
+        if q > 0:
+            groups = [g for g in range(L // RATIO) if g * RATIO + RATIO - 1 >= L - q]
+            want["work"] += [(r, i) for i in range(max(len(groups), 1))]
+    return qsl, sl, bt, csm, T, want
+
+
+METADATA_KINDS = [(519, 1), (1004, 4), (0, 0), (20, 3), (9215, 16), (3, 3), (777, 0),
+                  (131072, 1), (40000, 37), (4, 4), (5, 1), (100, 100)]
+
+
+def pin_metadata_by_construction(orc):
+    """Per-token request, position, visible blocks, compressed and ring
+    slots, and the k work items of a batch built request by request: decode,
+    speculative and prefill rows, empty queries, a query as long as its
+    sequence, padding tokens, holes in the table, skipped main-cache slots."""
+    for seed, width in [(0, 400), (1, 3)]:
+        qsl, sl, bt, csm, T, want = metadata_batch(seed, METADATA_KINDS, pad=5, width=width)
+        for M in (len(want["work"]) + 7, max(1, len(want["work"]) - 5)):
+            got = orc.build_metadata(qsl, sl, bt, T, common_slot_mapping=csm, max_num_work=M)
+            for k in ("token_to_req", "logical_positions", "visible_blocks", "slot_mapping"):
+                assert np.array_equal(got[k], want[k]), (seed, k)
+            w = np.full((M, 2), -1, np.int32)
+            n = min(M, len(want["work"]))
+            w[:n] = np.array(want["work"][:n], np.int32).reshape(-1, 2)
+            assert np.array_equal(got["k_work"], w), (seed, "k_work")
+        ring = orc.build_metadata(qsl, sl, bt, T, circular_buffer_size=8)
+        assert np.array_equal(ring["slot_mapping"], want["ring"]), (seed, "ring")
+        plain = orc.build_metadata(qsl, sl, bt, T, compress_ratio=1, common_slot_mapping=csm)
+        assert np.array_equal(plain["slot_mapping"], csm)
+
+
+def pin_metadata_searchsorted(orc):
+    """Request search on random batches (many empty queries) against numpy's
+    searchsorted; positions and visible blocks from their closed forms."""
+    rng = np.random.default_rng(71)
+    for N in (1, 2, 37, 500):
+        q = rng.integers(0, 6, size=N)
+        q[rng.random(N) < 0.3] = 0
+        L = q + rng.integers(0, 3000, size=N)
+        qsl = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+        T = int(qsl[-1]) + 3
+        bt = np.zeros((N, 30), np.int32)
+        got = orc.build_metadata(qsl, L.astype(np.int32), bt, T, with_slots=False)
+        t = np.arange(int(qsl[-1]))
+        r = np.searchsorted(qsl[1:], t, side="right")
+        assert np.array_equal(got["token_to_req"][:t.size], r)
+        assert np.all(got["token_to_req"][t.size:] == 0)
+        lp = L[r] - q[r] + (t - qsl[r])
+        assert np.array_equal(got["logical_positions"][:t.size], lp)
+        assert np.all(got["logical_positions"][t.size:] == -1)
+        vis = np.maximum(0, np.minimum((lp + 1) // 4, L[r] // 4))
+        assert np.array_equal(got["visible_blocks"][:t.size], vis)
+
+
+def pin_metadata_closed_forms(orc):
+    """A prefill from position 0 through an identity table writes compressed
+    slot g exactly at token 4g + 3; a decode row owns exactly one k work item
+    whether or not its token completes a group, and a prefill of n tokens
+    from position s owns floor((s+n)/4) - floor(s/4) items (at least one)."""
+    L = 2000
+    qsl = np.array([0, L], np.int32)
+    bt = np.arange(16, dtype=np.int32).reshape(1, 16)
+    got = orc.build_metadata(qsl, np.array([L], np.int32), bt, L, max_num_work=600)
+    t = np.arange(L)
+    want = np.where((t + 1) % 4 == 0, (t + 1) // 4 - 1, -1)
+    assert np.array_equal(got["slot_mapping"], want)
+    assert np.array_equal(got["k_work"][:500], np.stack([np.zeros(500), np.arange(500)], 1))
+    assert np.all(got["k_work"][500:] == -1)
+    lens = np.array([517, 518, 519, 520, 4, 1], np.int32)          # decode rows
+    qsl = np.arange(len(lens) + 1, dtype=np.int32)
+    got = orc.build_metadata(qsl, lens, np.zeros((len(lens), 8), np.int32), len(lens),
+                             max_num_work=len(lens) + 2)
+    assert np.array_equal(got["k_work"][:len(lens)],
+                          np.stack([np.arange(len(lens)), np.zeros(len(lens))], 1))
+    assert np.all(got["k_work"][len(lens):] == -1)
+    for s0, n in [(0, 3), (1, 9), (6, 2), (7, 1), (8, 16)]:
+        got = orc.build_metadata(np.array([0, n], np.int32), np.array([s0 + n], np.int32),
+                                 np.zeros((1, 8), np.int32), n, max_num_work=40)
+        count = max((s0 + n) // 4 - s0 // 4, 1)
+        assert np.array_equal(got["k_work"][:count, 1], np.arange(count))
+        assert np.all(got["k_work"][count:] == -1)
+
+
 ALL_PINS = [
     pin_half_to_double,
     pin_e4m3_to_double,
@@ -486,6 +606,9 @@ ALL_PINS = [
     pin_weights_of_one,
     pin_paged_logits_gather_normal,
     pin_topk_per_row_lexsort,
+    pin_metadata_by_construction,
+    pin_metadata_searchsorted,
+    pin_metadata_closed_forms,
     pin_select_worked_examples,
     pin_select_brute_force_integer,
     pin_select_multirow_requests,

@@ -1,6 +1,6 @@
 """Each planted mistake in the oracle must be caught by at least one pin.
 
-The oracle source carries sixteen compile-time mutants (a dropped term, a wrong
+The oracle source carries twenty compile-time mutants (a dropped term, a wrong
 sign, an off-by-one, a transposed operand, ...).  Building each one and
 running the pins shows that the pins constrain every step of the oracle.
 """
@@ -27,6 +27,10 @@ MUTANTS = {
     14: "head weights ignored",
     15: "ReLU after the head weight",
     16: "top-k per row reads past the visible blocks",
+    17: "a request's first token given to the request before",
+    18: "logical positions counted from the sequence end",
+    19: "compressed slot written at a group's first token",
+    20: "no k work item without a completed group",
 }
 
 
