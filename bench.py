@@ -16,6 +16,10 @@ Workloads (``--workload``):
   writes the [128, 32768] fp32 logits matrix, qsa_topk_per_row reduces it --
   then attention; the fused weighted selection (qsa_select_weighted) is
   timed on the same inputs for comparison.
+* multi_token_metadata: the multi_token batch with its per-row request ids
+  and positions built on the device each step by qsa_build_metadata (from
+  the cumulative query starts and sequence lengths, k work items included)
+  and fed to qsa_decode_step with no host synchronisation.
 * multi_token: several query rows per request -- 48 speculative-decode
   requests with 4 draft positions each and 4 chunked-prefill requests with
   16 positions each (R=256), lengths uniform in [8192, 65536], an 8192-page
@@ -179,7 +183,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", choices=["long_context", "long_context_fp8",
-                                           "long_context_two_pass", "multi_token"],
+                                           "long_context_two_pass", "multi_token",
+                                           "multi_token_metadata"],
                     default="long_context")
     ap.add_argument("--kv-copies", type=int, default=8,
                     help="distinct KV caches the steps rotate over (one per simulated layer)")
@@ -209,9 +214,12 @@ def main() -> int:
     t0 = time.perf_counter()
     fp8 = args.workload == "long_context_fp8"
     two_pass = args.workload == "long_context_two_pass"
+    meta = args.workload == "multi_token_metadata"
     head_w = None
-    if args.workload == "multi_token":
+    if args.workload in ("multi_token", "multi_token_metadata"):
         w = wl.multi_token_rows(args.seed)
+        if meta:
+            w.name = w.name + "_metadata"
     else:
         w = wl.long_context(args.seed)
         if fp8:
@@ -251,7 +259,31 @@ def main() -> int:
     ws_all = torch.zeros(max(1, qsa.decode_step_workspace_bytes(R, w.block_table.shape[1])),
                          dtype=torch.uint8, device=dev)
 
-    if two_pass:
+    if meta:
+        # the per-row request ids and positions come from the builder
+        qsl = d(wl.query_start_loc(w))
+        meta_ws = torch.zeros(max(1, qsa.build_metadata_workspace_bytes(len(w.seq_lens))),
+                              dtype=torch.uint8, device=dev)
+        meta_out = qsa.qsa_build_metadata(qsl, sel_in[4], sel_in[2], R, max_num_work=R,
+                                          workspace=meta_ws)
+        built_in = [sel_in[0], sel_in[1], sel_in[2], meta_out["token_to_req"], sel_in[4],
+                    meta_out["logical_positions"]]
+
+        def build_metadata():
+            qsa.qsa_build_metadata(qsl, sel_in[4], sel_in[2], R, max_num_work=R, out=meta_out,
+                                   workspace=meta_ws)
+
+        def select_stage(mark=None):
+            build_metadata()
+            if mark is not None:
+                mark.record(stream)
+            select_fn(*built_in, out=idx, workspace=sel_ws)
+
+        def step(i):
+            k, v = kv_views[i % len(kv_views)]
+            build_metadata()
+            decode_fn(*built_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
+    elif two_pass:
         wt = d(head_w)
         logits_width = w.block_table.shape[1] * 128
         logits = torch.empty((R, logits_width), dtype=torch.float32, device=dev)
@@ -297,7 +329,7 @@ def main() -> int:
     for i in range(args.steps):
         k, v = kv_views[i % len(kv_views)]
         events[i][0].record(stream)
-        select_stage(mark=events[i][3] if two_pass else None)
+        select_stage(mark=events[i][3] if (two_pass or meta) else None)
         events[i][1].record(stream)
         qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
         events[i][2].record(stream)
@@ -305,6 +337,12 @@ def main() -> int:
     sel_ms = [e[0].elapsed_time(e[1]) for e in events]
     att_ms = [e[1].elapsed_time(e[2]) for e in events]
     extra = {}
+    if meta:
+        meta_ms = [e[0].elapsed_time(e[3]) for e in events]
+        sel_only_ms = [e[3].elapsed_time(e[1]) for e in events]
+        extra = {"metadata_ms": round(float(np.mean(meta_ms)), 4),
+                 "select_only_ms": round(float(np.mean(sel_only_ms)), 4)}
+        log(f"metadata build {extra['metadata_ms']:.4f} ms, select {extra['select_only_ms']:.4f} ms")
     if two_pass:
         logits_ms = [e[0].elapsed_time(e[3]) for e in events]
         topk_ms = [e[3].elapsed_time(e[1]) for e in events]
@@ -343,7 +381,8 @@ def main() -> int:
         roof_s = extra["logits_ms"] / 1e3
         roof_kernel = "qsa_paged_logits (qsa_select_chunk_kernel, logits out)"
     else:
-        roof_bytes, roof_s = sel_bytes, sel_avg_s
+        roof_bytes = sel_bytes
+        roof_s = extra["select_only_ms"] / 1e3 if meta else sel_avg_s
         roof_kernel = (("qsa_select_fp8" if fp8 else "qsa_select") +
                        " (qsa_select_chunk_kernel + qsa_select_merge_kernel)")
     achieved = roof_bytes / roof_s / 1e9
@@ -381,6 +420,7 @@ def main() -> int:
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
                    "timed_entry_point": ("qsa_paged_logits + qsa_topk_per_row + qsa_sparse_attn"
                                          if two_pass else
+                                         "qsa_build_metadata + qsa_decode_step" if meta else
                                          "qsa_decode_step_fp8" if fp8 else "qsa_decode_step"),
                    **extra,
                    "stage_timing": "separate pass: qsa_select and qsa_sparse_attn with events "

@@ -13,7 +13,9 @@
  * (qsa_select_fp8, qsa_decode_step_fp8), with per-head weights
  * (qsa_select_weighted), and in two passes: scores materialised as a logits
  * matrix (qsa_paged_logits), then a top-k per row over it
- * (qsa_topk_per_row).
+ * (qsa_topk_per_row); and the metadata step before them
+ * (qsa_build_metadata: per-token request, position, visible blocks, cache
+ * slots and k work items).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -312,6 +314,63 @@ QSA_API int qsa_decode_step_fp8(const qsa_tensor* q_sel, const qsa_tensor* kcach
                                 const qsa_tensor* k, const qsa_tensor* v, float softmax_scale,
                                 const qsa_tensor* indices, const qsa_tensor* out, void* workspace,
                                 size_t workspace_bytes, qsa_stream stream);
+
+/* Workspace bytes qsa_build_metadata needs for num_reqs requests when
+ * k_work_metadata is given (0 otherwise). */
+QSA_API size_t qsa_build_metadata_workspace_bytes(int64_t num_reqs);
+
+/*
+ * qsa_build_metadata -- the per-step metadata of the QSA side caches, as the
+ * vllm qsa_cache.py page builds it (_build_qsa_metadata_kernel and its torch
+ * fallback), on the device with no host synchronisation.  Its token_to_req
+ * and logical_positions are the token_to_req and query_pos inputs of the
+ * selection entry points.
+ *
+ *   query_start_loc   I32 [N+1], N >= 1: query tokens of request r are
+ *                     [query_start_loc[r], query_start_loc[r+1]); tokens at
+ *                     or past query_start_loc[N] are padding.
+ *   seq_lens          I32 [N]: tokens of each request (>= its query length).
+ *   block_table       I32 [N, W], stride[1] == 1: the side cache's blocks.
+ *   common_slot_mapping  I64 [T] or NULL: the main cache's slots (< 0: the
+ *                     token writes no slot; NULL: every token writes one).
+ *   storage_block_size   compressed slots per block (>= 1).
+ *   compress_ratio    tokens per compressed key (>= 1).
+ *   circular_buffer_size 0, or the raw-key ring size (> 0 selects the ring
+ *                     owner's slots).
+ *   token_to_req      I32 [T] (T >= 0 tokens), written: the last request
+ *                     whose query starts at or before the token; 0 for
+ *                     padding.
+ *   logical_positions I64 [T], written: seq_len - query_len + offset inside
+ *                     the query; -1 for padding.
+ *   visible_blocks    I32 [T], written: max(0, min(floor((pos+1)/ratio),
+ *                     floor(seq_len/ratio))).
+ *   slot_mapping      I64 [T] or NULL, written: with a ring, a request's
+ *                     last ring-size tokens write block_table[r][0] * ring +
+ *                     pos mod ring; else with ratio > 1 the token that
+ *                     completes a group writes block_table[r][c / B] * B +
+ *                     c mod B for compressed position c = pos / ratio (if
+ *                     that column exists, holds a block >= 0 and the common
+ *                     slot is >= 0); else the common slot.  -1 elsewhere.
+ *   k_work_metadata   I32 [M, 2] or NULL, written: per request with a
+ *                     nonempty query max(floor(L/ratio) - floor((L-q)/ratio),
+ *                     1) items, laid out request after request as (request,
+ *                     index inside the request); (-1, -1) past the last item.
+ *
+ * Outputs must not overlap each other, any input or the workspace
+ * (qsa_build_metadata_workspace_bytes(N) bytes when k_work_metadata is
+ * given).  Device-side preconditions: query_start_loc[0] = 0 and
+ * nondecreasing; seq_lens >= query lengths.  Errors as for qsa_select
+ * (QSA_ERR_ARG for a size or ratio out of range).
+ */
+QSA_API int qsa_build_metadata(const qsa_tensor* query_start_loc, const qsa_tensor* seq_lens,
+                               const qsa_tensor* block_table,
+                               const qsa_tensor* common_slot_mapping,
+                               int64_t storage_block_size, int64_t compress_ratio,
+                               int64_t circular_buffer_size, const qsa_tensor* token_to_req,
+                               const qsa_tensor* logical_positions,
+                               const qsa_tensor* visible_blocks, const qsa_tensor* slot_mapping,
+                               const qsa_tensor* k_work_metadata, void* workspace,
+                               size_t workspace_bytes, qsa_stream stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     decode_step_workspace_bytes,
     kv_views,
     library,
+    build_metadata_workspace_bytes,
+    qsa_build_metadata,
     qsa_decode_step,
     qsa_decode_step_fp8,
     qsa_paged_logits,

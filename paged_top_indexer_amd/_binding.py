@@ -86,6 +86,10 @@ def library() -> ctypes.CDLL:
             lib.qsa_topk_per_row_workspace_bytes.restype = sz
             lib.qsa_topk_per_row.argtypes = [_P] * 5 + [vp, sz, vp]
             lib.qsa_topk_per_row.restype = ctypes.c_int
+            lib.qsa_build_metadata_workspace_bytes.argtypes = [i64]
+            lib.qsa_build_metadata_workspace_bytes.restype = sz
+            lib.qsa_build_metadata.argtypes = [_P] * 4 + [i64, i64, i64] + [_P] * 5 + [vp, sz, vp]
+            lib.qsa_build_metadata.restype = ctypes.c_int
             _lib = lib
         return _lib
 
@@ -333,3 +337,41 @@ def qsa_decode_step_fp8(q_sel, kcache, kscale, block_table, token_to_req, seq_le
                                   ctypes.byref(idd), ctypes.byref(od), ws, ws_bytes,
                                   ctypes.c_void_p(sh)))
     return indices, out
+
+
+def build_metadata_workspace_bytes(num_reqs: int) -> int:
+    return int(library().qsa_build_metadata_workspace_bytes(int(num_reqs)))
+
+
+def qsa_build_metadata(query_start_loc, seq_lens, block_table, num_tokens: int,
+                       storage_block_size: int = 128, compress_ratio: int = 4,
+                       circular_buffer_size: int = 0, common_slot_mapping=None,
+                       max_num_work: int = 0, with_slots: bool = True, out=None,
+                       workspace=None, stream=None) -> dict:
+    """Per-token metadata (token_to_req int32, logical_positions int64,
+    visible_blocks int32, slot_mapping int64) and k work items
+    [max_num_work, 2] int32, as device tensors in a dict (``out`` may hold
+    preallocated ones under the same keys)."""
+    torch = _torch()
+    lib = library()
+    dev = seq_lens.device
+    T = int(num_tokens)
+    o = dict(out or {})
+    o.setdefault("token_to_req", torch.empty(T, dtype=torch.int32, device=dev))
+    o.setdefault("logical_positions", torch.empty(T, dtype=torch.int64, device=dev))
+    o.setdefault("visible_blocks", torch.empty(T, dtype=torch.int32, device=dev))
+    if with_slots:
+        o.setdefault("slot_mapping", torch.empty(T, dtype=torch.int64, device=dev))
+    if max_num_work > 0:
+        o.setdefault("k_work", torch.empty((int(max_num_work), 2), dtype=torch.int32, device=dev))
+    sh = _stream(stream, dev)
+    need = build_metadata_workspace_bytes(seq_lens.shape[0]) if max_num_work > 0 else 0
+    ws, ws_bytes = _ws_args(need, dev, sh, workspace, "metadata")
+    ins = [ctypes.byref(tensor_desc(t)) for t in (query_start_loc, seq_lens, block_table)]
+    outs = [ctypes.byref(tensor_desc(o[k])) for k in ("token_to_req", "logical_positions",
+                                                      "visible_blocks")]
+    check(lib.qsa_build_metadata(*ins, _opt(common_slot_mapping), int(storage_block_size),
+                                 int(compress_ratio), int(circular_buffer_size), *outs,
+                                 _opt(o.get("slot_mapping")), _opt(o.get("k_work")), ws, ws_bytes,
+                                 ctypes.c_void_p(sh)))
+    return o

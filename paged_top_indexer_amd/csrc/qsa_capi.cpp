@@ -661,4 +661,119 @@ QSA_API int qsa_decode_step_fp8(const qsa_tensor* q_sel, const qsa_tensor* kcach
                      q_attn, k, v, softmax_scale, indices, out, workspace, workspace_bytes, stream);
 }
 
+QSA_API size_t qsa_build_metadata_workspace_bytes(int64_t num_reqs) {
+  if (num_reqs <= 0) return 0;
+  return align256((size_t)num_reqs * sizeof(int32_t));
+}
+
+QSA_API int qsa_build_metadata(const qsa_tensor* query_start_loc, const qsa_tensor* seq_lens,
+                               const qsa_tensor* block_table,
+                               const qsa_tensor* common_slot_mapping,
+                               int64_t storage_block_size, int64_t compress_ratio,
+                               int64_t circular_buffer_size, const qsa_tensor* token_to_req,
+                               const qsa_tensor* logical_positions,
+                               const qsa_tensor* visible_blocks, const qsa_tensor* slot_mapping,
+                               const qsa_tensor* k_work_metadata, void* workspace,
+                               size_t workspace_bytes, qsa_stream stream) {
+  g_last_error[0] = '\0';
+  if (storage_block_size < 1 || storage_block_size > ((int64_t)1 << 30)) {
+    return fail(QSA_ERR_ARG, "storage_block_size must be in [1, 2^30]");
+  }
+  if (compress_ratio < 1 || compress_ratio > ((int64_t)1 << 30)) {
+    return fail(QSA_ERR_ARG, "compress_ratio must be in [1, 2^30]");
+  }
+  if (circular_buffer_size < 0 || circular_buffer_size > ((int64_t)1 << 30)) {
+    return fail(QSA_ERR_ARG, "circular_buffer_size must be in [0, 2^30]");
+  }
+  const int64_t any1[1] = {-1};
+  QSA_TRY(check_tensor("seq_lens", seq_lens, QSA_DTYPE_I32, 1, any1));
+  QSA_TRY(check_contiguous("seq_lens", seq_lens));
+  const int64_t N = seq_lens->shape[0];
+  if (N < 1) return fail(QSA_ERR_SHAPE, "seq_lens: needs at least one request");
+  if (N > ((int64_t)1 << 24)) return fail(QSA_ERR_SHAPE, "seq_lens: too many requests");
+  const int64_t qshape[1] = {N + 1};
+  QSA_TRY(check_tensor("query_start_loc", query_start_loc, QSA_DTYPE_I32, 1, qshape));
+  QSA_TRY(check_contiguous("query_start_loc", query_start_loc));
+  const int64_t bshape[2] = {N, -1};
+  QSA_TRY(check_tensor("block_table", block_table, QSA_DTYPE_I32, 2, bshape));
+  const int64_t W = block_table->shape[1];
+  if (W > 1 && block_table->stride[1] != 1) return fail(QSA_ERR_LAYOUT, "block_table: stride[1] must be 1");
+  if (N > 1 && block_table->stride[0] < W) return fail(QSA_ERR_LAYOUT, "block_table: stride[0] < width");
+  QSA_TRY(check_tensor("token_to_req", token_to_req, QSA_DTYPE_I32, 1, any1));
+  QSA_TRY(check_contiguous("token_to_req", token_to_req));
+  const int64_t T = token_to_req->shape[0];
+  if (T > ((int64_t)1 << 31) - 1) return fail(QSA_ERR_SHAPE, "token_to_req: too many tokens");
+  const int64_t tshape[1] = {T};
+  QSA_TRY(check_tensor("logical_positions", logical_positions, QSA_DTYPE_I64, 1, tshape));
+  QSA_TRY(check_contiguous("logical_positions", logical_positions));
+  QSA_TRY(check_tensor("visible_blocks", visible_blocks, QSA_DTYPE_I32, 1, tshape));
+  QSA_TRY(check_contiguous("visible_blocks", visible_blocks));
+  if (common_slot_mapping) {
+    QSA_TRY(check_tensor("common_slot_mapping", common_slot_mapping, QSA_DTYPE_I64, 1, tshape));
+    QSA_TRY(check_contiguous("common_slot_mapping", common_slot_mapping));
+  }
+  if (slot_mapping) {
+    QSA_TRY(check_tensor("slot_mapping", slot_mapping, QSA_DTYPE_I64, 1, tshape));
+    QSA_TRY(check_contiguous("slot_mapping", slot_mapping));
+  }
+  int64_t M = 0;
+  if (k_work_metadata) {
+    const int64_t kshape[2] = {-1, 2};
+    QSA_TRY(check_tensor("k_work_metadata", k_work_metadata, QSA_DTYPE_I32, 2, kshape));
+    QSA_TRY(check_contiguous("k_work_metadata", k_work_metadata));
+    M = k_work_metadata->shape[0];
+    if (M > ((int64_t)1 << 31) - 1) return fail(QSA_ERR_SHAPE, "k_work_metadata: too many items");
+  }
+  // outputs must not overlap each other or any input
+  const qsa_tensor* outs[5] = {token_to_req, logical_positions, visible_blocks, slot_mapping,
+                               k_work_metadata};
+  const char* onames[5] = {"token_to_req", "logical_positions", "visible_blocks", "slot_mapping",
+                           "k_work_metadata"};
+  const qsa_tensor* ins[4] = {query_start_loc, seq_lens, block_table, common_slot_mapping};
+  const char* inames[4] = {"query_start_loc", "seq_lens", "block_table", "common_slot_mapping"};
+  for (int o = 0; o < 5; ++o) {
+    if (!outs[o]) continue;
+    for (int i = 0; i < 4; ++i) {
+      if (ins[i] && overlaps(span_of(outs[o]), span_of(ins[i]))) {
+        return fail(QSA_ERR_ALIAS, "%s overlaps %s", onames[o], inames[i]);
+      }
+    }
+    for (int o2 = o + 1; o2 < 5; ++o2) {
+      if (outs[o2] && overlaps(span_of(outs[o]), span_of(outs[o2]))) {
+        return fail(QSA_ERR_ALIAS, "%s overlaps %s", onames[o], onames[o2]);
+      }
+    }
+  }
+  const size_t need = M > 0 ? qsa_build_metadata_workspace_bytes(N) : 0;
+  Span guarded[9];
+  int ng = 0;
+  for (int o = 0; o < 5; ++o) if (outs[o]) guarded[ng++] = span_of(outs[o]);
+  for (int i = 0; i < 4; ++i) if (ins[i]) guarded[ng++] = span_of(ins[i]);
+  QSA_TRY(check_workspace(workspace, workspace_bytes, need, guarded, ng));
+  if (T == 0 && M == 0) return QSA_OK;
+  qsa::MetaArgs a;
+  a.query_start_loc = static_cast<const int32_t*>(query_start_loc->data);
+  a.seq_lens = static_cast<const int32_t*>(seq_lens->data);
+  a.block_table = static_cast<const int32_t*>(block_table->data);
+  a.common_slot_mapping =
+      common_slot_mapping ? static_cast<const int64_t*>(common_slot_mapping->data) : nullptr;
+  a.token_to_req = static_cast<int32_t*>(token_to_req->data);
+  a.logical_positions = static_cast<int64_t*>(logical_positions->data);
+  a.visible_blocks = static_cast<int32_t*>(visible_blocks->data);
+  a.slot_mapping = slot_mapping ? static_cast<int64_t*>(slot_mapping->data) : nullptr;
+  a.k_work = M > 0 ? static_cast<int32_t*>(k_work_metadata->data) : nullptr;
+  a.work_ends = M > 0 ? static_cast<int32_t*>(workspace) : nullptr;
+  a.num_reqs = N;
+  a.num_tokens = T;
+  a.max_num_work = M;
+  a.table_width = W;
+  a.bt_stride = N > 1 ? block_table->stride[0] : W;
+  a.storage_block_size = storage_block_size;
+  a.compress_ratio = compress_ratio;
+  a.circular_buffer_size = circular_buffer_size;
+  const int err = qsa::launch_metadata(a, stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "metadata launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
 }  // extern "C"

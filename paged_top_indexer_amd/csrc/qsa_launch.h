@@ -80,9 +80,27 @@ struct AttnArgs {
   float scale_log2;        // softmax scale * log2(e)
 };
 
+// Arguments of the metadata builder (all device pointers; outputs written).
+struct MetaArgs {
+  const int32_t* query_start_loc = nullptr;  // [N+1]
+  const int32_t* seq_lens = nullptr;         // [N]
+  const int32_t* block_table = nullptr;      // [N, table_width], row stride bt_stride
+  const int64_t* common_slot_mapping = nullptr;  // [num_tokens] or NULL
+  int32_t* token_to_req = nullptr;           // [num_tokens]
+  int64_t* logical_positions = nullptr;      // [num_tokens]
+  int32_t* visible_blocks = nullptr;         // [num_tokens]
+  int64_t* slot_mapping = nullptr;           // [num_tokens] or NULL
+  int32_t* k_work = nullptr;                 // [max_num_work][2] or NULL
+  int32_t* work_ends = nullptr;              // workspace [N] (with k_work)
+  int64_t num_reqs = 0, num_tokens = 0, max_num_work = 0;
+  int64_t table_width = 0, bt_stride = 0;
+  int64_t storage_block_size = 1, compress_ratio = 1, circular_buffer_size = 0;
+};
+
 // Enqueue the kernels; return the hipError_t of the launch (0 = success).
 int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
+int launch_metadata(const MetaArgs& a, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
 
 }  // namespace qsa

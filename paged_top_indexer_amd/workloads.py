@@ -404,6 +404,42 @@ def multi_token_rows(seed: int = 0, decode_requests: int = 48, next_n: int = 4,
     return Workload(name, seed, q_sel, kcache, bt, t2r, lengths.astype(np.int32), qp, q_attn, kv)
 
 
+def query_start_loc(w: Workload) -> np.ndarray:
+    """Cumulative query starts [N+1] int32 of a workload whose rows are
+    grouped request by request (the metadata builder's input)."""
+    t2r = np.asarray(w.token_to_req)
+    assert np.all(np.diff(t2r) >= 0), "rows must be grouped by request"
+    counts = np.bincount(t2r, minlength=len(w.seq_lens))
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def serving_batch(seed: int = 0, decode: int = 160, spec: int = 48, next_n: int = 4,
+                  prefill: int = 8, chunk: int = 512, empty: int = 16, pad: int = 64):
+    """Builder inputs for a mixed serving step: decode rows (1 token),
+    speculative rows (next_n tokens), chunked-prefill rows (chunk tokens),
+    requests with an empty query, interleaved at random, L ~ U[1024, 131072];
+    a block table of random block ids with 5% holes; a common slot mapping
+    with 2% skipped tokens; pad padding tokens.
+
+    Draw order: request kinds permutation; lengths; block table; holes;
+    common slots; skipped-slot mask.
+    Returns (query_start_loc, seq_lens, block_table, common_slot_mapping,
+    num_tokens)."""
+    rng = np.random.default_rng(seed)
+    kinds = np.array([1] * decode + [next_n] * spec + [chunk] * prefill + [0] * empty)
+    kinds = kinds[rng.permutation(kinds.size)]
+    N = kinds.size
+    L = rng.integers(1024, 131072 + 1, size=N)
+    qsl = np.concatenate([[0], np.cumsum(kinds)]).astype(np.int32)
+    W = pages_needed(131072)
+    bt = rng.integers(0, 1 << 20, size=(N, W)).astype(np.int32)
+    bt[rng.random(bt.shape) < 0.05] = -1
+    T = int(qsl[-1]) + pad
+    csm = rng.integers(0, 1 << 30, size=T).astype(np.int64)
+    csm[rng.random(T) < 0.02] = -1
+    return qsl, L.astype(np.int32), bt, csm, T
+
+
 NAMED = {
     1: tiny_integer,
     2: saturated_row,

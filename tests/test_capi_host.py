@@ -396,3 +396,63 @@ def test_topk_per_row_checks():
     assert call_topk(lg, t2r, sl, qp, out, lg.data, wsb) == ALIAS
     assert call_topk(mk(f, B.F32, (0, Wl), 4), mk(f, B.I32, (0,), 4), sl, mk(f, B.I64, (0,), 8),
                      mk(f, B.I32, (0, 2051), 4), 0, 0) == OK
+
+
+# ---------------------------------------------------------------------------
+# metadata builder
+
+def meta_args(N=3, T=10, W=4, M=8):
+    f = Fake()
+    a = dict(qsl=mk(f, B.I32, (N + 1,), 4), sl=mk(f, B.I32, (N,), 4), bt=mk(f, B.I32, (N, W), 4),
+             csm=mk(f, B.I64, (T,), 8), t2r=mk(f, B.I32, (T,), 4), lp=mk(f, B.I64, (T,), 8),
+             vis=mk(f, B.I32, (T,), 4), slots=mk(f, B.I64, (T,), 8),
+             work=mk(f, B.I32, (M, 2), 4) if M else None)
+    wsb = B.build_metadata_workspace_bytes(N) if M else 0
+    return f, a, (f.alloc(wsb) if wsb else 0), wsb
+
+
+def call_meta(a, ws, wsb, block=128, ratio=4, ring=0):
+    lib = B.library()
+    opt = lambda t: ctypes.byref(t) if t is not None else None  # noqa: E731
+    return lib.qsa_build_metadata(opt(a["qsl"]), opt(a["sl"]), opt(a["bt"]), opt(a["csm"]),
+                                  block, ratio, ring, opt(a["t2r"]), opt(a["lp"]), opt(a["vis"]),
+                                  opt(a["slots"]), opt(a["work"]), ctypes.c_void_p(ws), wsb, None)
+
+
+META_CASES = {
+    "qsl_len": (lambda f, a: a.__setitem__("qsl", mk(f, B.I32, (3,), 4)), SHAPE),
+    "qsl_i64": (lambda f, a: a.__setitem__("qsl", mk(f, B.I64, (4,), 8)), DTYPE),
+    "seq_lens_null": (lambda f, a: a.__setitem__("sl", None), NULL),
+    "table_rows": (lambda f, a: a.__setitem__("bt", mk(f, B.I32, (2, 4), 4)), SHAPE),
+    "table_col_stride": (lambda f, a: a.__setitem__("bt", mk(f, B.I32, (3, 4), 4, stride=(8, 2))), LAYOUT),
+    "positions_i32": (lambda f, a: a.__setitem__("lp", mk(f, B.I32, (10,), 4)), DTYPE),
+    "visible_len": (lambda f, a: a.__setitem__("vis", mk(f, B.I32, (9,), 4)), SHAPE),
+    "csm_i32": (lambda f, a: a.__setitem__("csm", mk(f, B.I32, (10,), 4)), DTYPE),
+    "slots_len": (lambda f, a: a.__setitem__("slots", mk(f, B.I64, (11,), 8)), SHAPE),
+    "work_cols": (lambda f, a: a.__setitem__("work", mk(f, B.I32, (8, 3), 4)), SHAPE),
+    "out_overlap": (lambda f, a: a.__setitem__("vis", mk(f, B.I32, (10,), 4, ptr=a["t2r"].data)), ALIAS),
+    "out_on_input": (lambda f, a: a.__setitem__("lp", mk(f, B.I64, (10,), 8, ptr=a["qsl"].data)), ALIAS),
+}
+
+
+@pytest.mark.parametrize("case", sorted(META_CASES))
+def test_metadata_fail_closed(case):
+    mutate, want = META_CASES[case]
+    f, a, ws, wsb = meta_args()
+    mutate(f, a)
+    rc = call_meta(a, ws, wsb)
+    assert rc == want, (rc, B.library().qsa_last_error())
+
+
+def test_metadata_scalar_and_workspace_checks():
+    f, a, ws, wsb = meta_args()
+    assert call_meta(a, ws, wsb, block=0) == ARG
+    assert call_meta(a, ws, wsb, ratio=0) == ARG
+    assert call_meta(a, ws, wsb, ring=-1) == ARG
+    assert wsb > 0 and B.build_metadata_workspace_bytes(0) == 0
+    assert call_meta(a, ws, wsb - 1) == WORKSPACE
+    assert call_meta(a, 0, wsb) == WORKSPACE
+    assert call_meta(a, a["t2r"].data, wsb) == ALIAS
+    # no tokens and no work items: nothing to do
+    f, a, ws, wsb = meta_args(T=0, M=0)
+    assert call_meta(a, 0, 0) == OK
