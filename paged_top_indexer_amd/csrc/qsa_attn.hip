@@ -28,6 +28,7 @@
 
 #include <cstdint>
 
+#include "qsa_device.h"
 #include "qsa_launch.h"
 
 namespace qsa {
@@ -70,8 +71,9 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t r = blockIdx.x / p.splits;
-  const int split = blockIdx.x % p.splits;
+  const RowCol id = row_col_of_block(blockIdx.x, p.splits);  // XCD-aware placement
+  const int64_t r = id.row;
+  const int split = (int)id.col;
   if (r >= p.rows) return;
 
   const int n = lane & 15;  // token row of A / head column of B
@@ -221,8 +223,9 @@ constexpr int kMaxSplits = 64;
 __global__ __launch_bounds__(kThreads) void qsa_attn_combine_kernel(AttnParams p) {
   __shared__ float weight[kMaxSplits];
   __shared__ float total;
-  const int64_t r = blockIdx.x / kAttHeads;
-  const int h = blockIdx.x % kAttHeads;
+  const RowCol id = row_col_of_block(blockIdx.x, kAttHeads);
+  const int64_t r = id.row;
+  const int h = (int)id.col;
   const int tid = threadIdx.x;
   if (r >= p.rows) return;
   if (tid < 64) {
@@ -273,12 +276,12 @@ int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
   p.splits = plan.splits;
   p.split_positions = plan.split_positions;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(qsa_attn_kernel, dim3((unsigned)(a.rows * plan.splits)), dim3(kThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL(qsa_attn_kernel, dim3((unsigned)(padded_rows(a.rows) * plan.splits)),
+                     dim3(kThreads), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return (int)err;
-  hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)(a.rows * kAttHeads)), dim3(kThreads),
-                     0, s, p);
+  hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)(padded_rows(a.rows) * kAttHeads)),
+                     dim3(kThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 

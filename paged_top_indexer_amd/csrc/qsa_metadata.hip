@@ -29,7 +29,7 @@
 #include <cstdint>
 
 #include "qsa_launch.h"
-#include "qsa_wave.h"
+#include "qsa_device.h"
 
 namespace qsa {
 namespace {

@@ -56,13 +56,13 @@
 #include <cstdint>
 
 #include "qsa_launch.h"
-#include "qsa_wave.h"
+#include "qsa_device.h"
 
 namespace qsa {
 namespace {
 
 constexpr int kChunkThreads = 256;
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 512;  // 2 waves per SIMD hide part of the LDS latency
 constexpr int kMaxChunkPages = 32;
 constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
 constexpr int kBins = 2048;       // radix digit of up to 11 bits
@@ -212,7 +212,6 @@ __device__ void radix_pick(const uint32_t* h, uint32_t krem, Scratch& s) {
 template <int NT, typename KeyAt>
 __device__ void radix_select(KeyAt key_at, int n, int k, Scratch& s, uint32_t* hist0,
                              uint32_t* hist1, uint32_t& T, int& need_eq, int& eq_total) {
-  static_assert(NT <= 256, "Scratch holds 4 waves");
   const int tid = threadIdx.x;
   for (int i = tid; i < kBins; i += NT) hist1[i] = 0;
   if (tid < 64) radix_pick<kBins>(hist0, (uint32_t)k, s);
@@ -366,12 +365,16 @@ __device__ __forceinline__ uint64_t xor_lane64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// One compare-exchange stage of the descending bitonic network.
+// One compare-exchange stage of the descending bitonic network.  Only the
+// holders (threads 0..255, whole waves) compute; every thread meets the
+// barriers of the LDS stages.
 template <int SIZE, int STRIDE>
 __device__ __forceinline__ void bitonic_stage(uint64_t& a, uint64_t& b, uint64_t* xchg) {
   const int tid = threadIdx.x;
+  const bool holder = tid < kTopKBlocks / 2;
   const bool desc = ((2 * tid) & SIZE) == 0;
   if constexpr (STRIDE == 1) {
+    if (!holder) return;
     const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
     a = desc ? hi : lo;
     b = desc ? lo : hi;
@@ -379,16 +382,20 @@ __device__ __forceinline__ void bitonic_stage(uint64_t& a, uint64_t& b, uint64_t
     constexpr int X = STRIDE / 2;
     uint64_t oa, ob;
     if constexpr (X >= 64) {
-      xchg[2 * tid] = a;
-      xchg[2 * tid + 1] = b;
+      if (holder) {
+        xchg[2 * tid] = a;
+        xchg[2 * tid + 1] = b;
+      }
       __syncthreads();
-      oa = xchg[(2 * tid) ^ STRIDE];
-      ob = xchg[(2 * tid + 1) ^ STRIDE];
+      oa = holder ? xchg[(2 * tid) ^ STRIDE] : a;
+      ob = holder ? xchg[(2 * tid + 1) ^ STRIDE] : b;
       __syncthreads();
     } else {
+      if (!holder) return;
       oa = xor_lane64<X>(a);
       ob = xor_lane64<X>(b);
     }
+    if (!holder) return;
     const bool keep_hi = ((tid & X) == 0) == desc;
     a = keep_hi ? (a > oa ? a : oa) : (a > oa ? oa : a);
     b = keep_hi ? (b > ob ? b : ob) : (b > ob ? ob : b);
@@ -411,12 +418,13 @@ __device__ __forceinline__ void bitonic_sort(uint64_t& a, uint64_t& b, uint64_t*
 // order; missing entries count as 0, which sorts last because every real
 // entry has a nonzero low word) are sorted descending; each block is
 // expanded to its 4 tokens, the tail appended and the row padded with -1.
-// Needs 256 threads and a barrier between the writes of `list` and the
-// call; `xchg` (512 entries) may be `list` itself.
+// Threads 0..255 hold the entries (any workgroup of at least 256 threads;
+// all of them must call); needs a barrier between the writes of `list` and
+// the call; `xchg` (512 entries) may be `list` itself.
 __device__ void sort_expand_write(const uint64_t* list, int k, int64_t visible, int tail,
                                   int32_t* out_row, uint64_t* xchg) {
   const int tid = threadIdx.x;
-  uint64_t a = 2 * tid < k ? list[2 * tid] : 0;
+  uint64_t a = 2 * tid < k ? list[2 * tid] : 0;  // k <= 512: threads >= 256 hold 0
   uint64_t b = 2 * tid + 1 < k ? list[2 * tid + 1] : 0;
   bitonic_sort<kTopKBlocks>(a, b, xchg);
   // thread t holds ranks 2t and 2t+1: tokens 8t .. 8t+7
@@ -431,7 +439,7 @@ __device__ void sort_expand_write(const uint64_t* list, int k, int64_t visible, 
     }
   }
   const int sel_tokens = kRatio * k;
-  for (int i = sel_tokens + tid; i < kOutWidth; i += 256) {
+  for (int i = sel_tokens + tid; i < kOutWidth; i += (int)blockDim.x) {
     out_row[i] = i < sel_tokens + tail ? (int32_t)(kRatio * visible + (i - sel_tokens)) : -1;
   }
 }
@@ -784,14 +792,17 @@ __device__ __forceinline__ void score_chunk_logits(const SelectParams& p, int64_
 
 enum : int { kSrcF16 = 0, kSrcE4M3 = 1, kSrcLogits = 2 };
 
+
+
 // kSrc: where the scores come from; kLogitsOut: write them as a logits row
 // (and -inf past the visible blocks) instead of selecting.
 template <int kSrc, bool kLogitsOut>
 __global__ __launch_bounds__(kChunkThreads, 4) void qsa_select_chunk_kernel(SelectParams p) {
   __shared__ ChunkSmem sm;
   const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x / p.chunks_per_row;
-  const int64_t chunk = blockIdx.x % p.chunks_per_row;
+  const RowCol id = row_col_of_block(blockIdx.x, p.chunks_per_row);  // XCD-aware placement
+  const int64_t r = id.row;
+  const int64_t chunk = id.col;
   if (r >= p.rows) return;
   const Row row = row_setup(p, r);
   const int64_t chunk_base = chunk * p.chunk_blocks;
@@ -882,7 +893,7 @@ struct MergeSmem {
 __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectParams p) {
   __shared__ MergeSmem sm;
   const int tid = threadIdx.x;
-  const int64_t r = blockIdx.x;
+  const int64_t r = row_on_xcd(blockIdx.x % kXcds, blockIdx.x / kXcds);
   if (r >= p.rows) return;
   const Row row = row_setup(p, r);
   if (row.nchunks == 1) return;  // finished by the chunk kernel
@@ -912,7 +923,7 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
     }
     // 16-byte loads, kLoadUnroll of them in flight per thread (the batch
     // start is a multiple of 4 candidates and the workspace is 256-aligned)
-    constexpr int kLoadUnroll = 4;
+    constexpr int kLoadUnroll = 2;
     const int nb4 = nb >> 2;
     const uint4* k4 = reinterpret_cast<const uint4*>(ckeys + base);
     const uint4* b4 = reinterpret_cast<const uint4*>(cblocks + base);
@@ -1010,7 +1021,8 @@ SelectParams make_params(const SelectArgs& a, const SelectPlan& plan) {
 template <int kSrc, bool kLogitsOut>
 void launch_chunks(const SelectParams& p, hipStream_t s) {
   hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut>),
-                     dim3((unsigned)(p.rows * p.chunks_per_row)), dim3(kChunkThreads), 0, s, p);
+                     dim3((unsigned)(p.chunks_per_row * padded_rows(p.rows))), dim3(kChunkThreads),
+                     0, s, p);
 }
 
 }  // namespace
@@ -1028,7 +1040,8 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.chunks_per_row == 1) return (int)err;
-  hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)a.rows), dim3(kMergeThreads), 0, s, p);
+  hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)padded_rows(a.rows)),
+                     dim3(kMergeThreads), 0, s, p);
   return (int)hipGetLastError();
 }
 
