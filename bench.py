@@ -131,6 +131,62 @@ def stored_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def read_ceiling(torch, qsa, dev, gib: int = 2, reps: int = 5) -> float:
+    """The box's practical HBM read ceiling (GB/s): qsa_read_probe streaming
+    `gib` GiB with nontemporal loads, `reps` times between HIP events."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    qsa.qsa_read_probe(buf, sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev)
+    ev[0].record(stream)
+    for _ in range(reps):
+        qsa.qsa_read_probe(buf, sink)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    gbs = (gib << 30) * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9
+    del buf
+    return gbs
+
+
+def r1_latencies(torch, qsa, wl, dev, calls: int = 64) -> dict:
+    """Mean single-row latencies of the pages' own cases (their figures are
+    for an Intel XPU; context only): selection of the 519-token row (129
+    blocks) and of the saturated 9215-token row (2303 blocks), and
+    attention over the saturated row's 2051 indices."""
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+
+    def mean_ms(fn):
+        for _ in range(5):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(calls):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / calls
+
+    out = {}
+    tiny = [d(a) for a in wl.tiny_integer(0).select_inputs()]
+    idx1 = torch.empty((1, 2051), dtype=torch.int32, device=dev)
+    out["select_519_tokens_ms"] = round(mean_ms(lambda: qsa.qsa_select(*tiny, out=idx1)), 5)
+    sat = wl.saturated_row(0)
+    satd = [d(a) for a in sat.select_inputs()]
+    out["select_2303_blocks_ms"] = round(mean_ms(lambda: qsa.qsa_select(*satd, out=idx1)), 5)
+    kvd = d(sat.kv)
+    k, v = qsa.kv_views(kvd)
+    q = d(sat.q_attn)
+    qsa.qsa_select(*satd, out=idx1)
+    o = torch.empty((1, 3, 256), dtype=torch.float16, device=dev)
+    out["attention_width_2051_ms"] = round(
+        mean_ms(lambda: qsa.qsa_sparse_attn(q, k, v, idx1, wl.SOFTMAX_SCALE, out=o)), 5)
+    out["pages_intel_xpu_ms"] = {"select_519_tokens": 0.053155, "select_2303_blocks": 0.319464,
+                                 "attention_width_2051": 0.710274}
+    return out
+
+
 def cpu_baseline(w, scale: float, fp8: bool = False, weights=None,
                  max_seconds: float = 20.0) -> dict:
     """The CPU oracle (single-threaded C, unmodified) on the host cores: the
@@ -181,6 +237,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the read-ceiling probe and the single-row latencies")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", choices=["long_context", "long_context_fp8",
                                            "long_context_two_pass", "multi_token",
@@ -387,6 +445,10 @@ def main() -> int:
                        " (qsa_select_chunk_kernel + qsa_select_merge_kernel)")
     achieved = roof_bytes / roof_s / 1e9
     traffic = stored_traffic(w.name)
+    ceiling = None if args.no_context else read_ceiling(torch, qsa, dev)
+    context = None if args.no_context else r1_latencies(torch, qsa, wl, dev)
+    if ceiling:
+        log(f"read ceiling {ceiling:.0f} GB/s; single-row latencies {context}")
     rows_per_s = R / (ms_per_step / 1e3)
     step_bytes = sel_bytes + att_bytes + (R * logits_width * 8 if two_pass else 0)
     step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
@@ -412,6 +474,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": roof_kernel,
+                     "ceiling": None if ceiling is None else round(ceiling, 1),
+                     "frac_of_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
                      "bytes_per_launch": roof_bytes, "avg_launch_ms": round(roof_s * 1e3, 4)},
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
                    "attention_bytes": att_bytes,
@@ -426,6 +490,8 @@ def main() -> int:
                    "stage_timing": "separate pass: qsa_select and qsa_sparse_attn with events "
                                    "between them"},
     }
+    if context is not None:
+        result["single_row_latency"] = context
     if not args.no_cpu_baseline:
         base = cpu_baseline(w, scale, fp8=fp8, weights=head_w)
         outs = base.pop("_outs")

@@ -291,6 +291,15 @@ int check_workspace(void* ws, size_t have, size_t need, Span guarded[], int ngua
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// A launch of `cols` workgroups per row over `rows` rows must fit one grid.
+int check_grid(const char* what, int64_t rows, int64_t cols) {
+  if (qsa::padded_rows(rows) > qsa::kMaxGrid / (cols > 0 ? cols : 1)) {
+    return fail(QSA_ERR_SHAPE, "%s: %lld rows x %lld workgroups per row exceed one launch", what,
+                (long long)rows, (long long)cols);
+  }
+  return QSA_OK;
+}
+
 }  // namespace
 
 namespace qsa {
@@ -380,6 +389,7 @@ int select_impl(const qsa_tensor* q, const qsa_tensor* weights, const qsa_tensor
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
   const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
+  QSA_TRY(check_grid("selection", v.rows, plan.chunks_per_row));
   Span guarded[9] = {span_of(q),        span_of(kcache),   span_of(block_table),
                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
                      span_of(out),      e4m3 ? span_of(kscale) : Span(),
@@ -420,6 +430,8 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   if (sv.rows == 0) return QSA_OK;
   const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width);
   const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
+  QSA_TRY(check_grid("selection", sv.rows, splan.chunks_per_row));
+  QSA_TRY(check_grid("attention", av.rows, aplan.splits));
   const size_t sel_bytes = align256(splan.bytes);
   const size_t need = sel_bytes + aplan.bytes;
   qsa_tensor whole = *k;
@@ -545,6 +557,7 @@ QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
   const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
+  QSA_TRY(check_grid("paged logits", v.rows, plan.chunks_per_row));
   qsa::SelectArgs a;
   fill_select_args(a, q, weights, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
                    query_pos, nullptr, nullptr, v);
@@ -590,6 +603,7 @@ QSA_API int qsa_topk_per_row(const qsa_tensor* logits, const qsa_tensor* token_t
   const int64_t width = logits->shape[1];
   const int64_t pages = (width + QSA_PAGE_SLOTS - 1) / QSA_PAGE_SLOTS;
   const qsa::SelectPlan plan = qsa::plan_select(R, pages);
+  QSA_TRY(check_grid("top-k", R, plan.chunks_per_row));
   Span guarded[5] = {span_of(logits), span_of(token_to_req), span_of(seq_lens),
                      span_of(query_pos), span_of(out)};
   QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 5));
@@ -619,6 +633,7 @@ QSA_API int qsa_sparse_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_
   QSA_TRY(validate_attn(q, k, v, indices, softmax_scale, out, false, &view));
   if (view.rows == 0) return QSA_OK;
   const qsa::AttnPlan plan = qsa::plan_attn(view.rows);
+  QSA_TRY(check_grid("attention", view.rows, plan.splits));
   qsa_tensor whole = *k;
   whole.ndim = 1;
   whole.shape[0] = view.tokens * 2 * QSA_ATT_DIM;
@@ -773,6 +788,28 @@ QSA_API int qsa_build_metadata(const qsa_tensor* query_start_loc, const qsa_tens
   a.circular_buffer_size = circular_buffer_size;
   const int err = qsa::launch_metadata(a, stream);
   if (err) return fail(QSA_ERR_LAUNCH, "metadata launch failed (hipError %d)", err);
+  return QSA_OK;
+}
+
+QSA_API int qsa_read_probe(const void* data, size_t bytes, void* sink, size_t sink_bytes,
+                           qsa_stream stream) {
+  g_last_error[0] = '\0';
+  if (!data || !sink) return fail(QSA_ERR_NULL, "read probe: data and sink must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(data) % 16 || bytes % 16) {
+    return fail(QSA_ERR_LAYOUT, "read probe: data must be 16-byte aligned and a multiple of 16 bytes");
+  }
+  if (reinterpret_cast<uintptr_t>(sink) % 4 || sink_bytes < 4) {
+    return fail(QSA_ERR_WORKSPACE, "read probe: sink needs 4 aligned bytes");
+  }
+  Span d, k;
+  d.lo = reinterpret_cast<uintptr_t>(data);
+  d.hi = d.lo + bytes;
+  k.lo = reinterpret_cast<uintptr_t>(sink);
+  k.hi = k.lo + 4;
+  if (overlaps(d, k)) return fail(QSA_ERR_ALIAS, "read probe: sink overlaps data");
+  if (bytes == 0) return QSA_OK;
+  const int err = qsa::launch_read_probe(data, (int64_t)bytes, static_cast<uint32_t*>(sink), stream);
+  if (err) return fail(QSA_ERR_LAUNCH, "read probe launch failed (hipError %d)", err);
   return QSA_OK;
 }
 

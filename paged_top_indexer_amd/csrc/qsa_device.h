@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "qsa_launch.h"
+
 namespace qsa {
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: row_shr 1, 2,
@@ -31,16 +33,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 // workgroup of XCD b % 8; that XCD's s-th row is row_on_xcd(b % 8, s).
 // Grids are padded to whole groups on all XCDs; workgroups mapped past the
 // last row exit.
-constexpr int kXcds = 8;
-constexpr int kRowGroup = 4;
-
+// (kXcds, kRowGroup and padded_rows are in qsa_launch.h, shared with the
+// host code that sizes the grids.)
 __device__ __forceinline__ int64_t row_on_xcd(int64_t xcd, int64_t s) {
   return kRowGroup * (kXcds * (s / kRowGroup) + xcd) + s % kRowGroup;
-}
-
-// Rows a grid must cover, rounded up to whole groups on all XCDs.
-__host__ __device__ constexpr int64_t padded_rows(int64_t rows) {
-  return (rows + kXcds * kRowGroup - 1) / (kXcds * kRowGroup) * (kXcds * kRowGroup);
 }
 
 // (row, column) of workgroup b of a grid with `cols` workgroups per row.

@@ -20,6 +20,17 @@ constexpr int kAttDim = 256;
 constexpr int kKvRow = 512;
 constexpr int kKvPageTokens = 512;
 
+// Row-indexed grids are padded to whole groups of kRowGroup rows on each of
+// the kXcds XCDs (see qsa_device.h); a launch holds at most kMaxGrid
+// workgroups.
+constexpr int kXcds = 8;
+constexpr int kRowGroup = 4;
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+
+constexpr int64_t padded_rows(int64_t rows) {
+  return (rows + kXcds * kRowGroup - 1) / (kXcds * kRowGroup) * (kXcds * kRowGroup);
+}
+
 // Launch plan of the selection.  A row's visible blocks are cut into chunks
 // of `chunk_pages` cache pages; one workgroup of the chunk kernel scores one
 // chunk and keeps its best min(512, chunk) blocks (a row with a single
@@ -101,6 +112,7 @@ struct MetaArgs {
 int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_metadata(const MetaArgs& a, void* stream);
+int launch_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
 
 }  // namespace qsa

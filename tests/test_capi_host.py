@@ -456,3 +456,25 @@ def test_metadata_scalar_and_workspace_checks():
     # no tokens and no work items: nothing to do
     f, a, ws, wsb = meta_args(T=0, M=0)
     assert call_meta(a, 0, 0) == OK
+
+
+def test_launch_size_limits():
+    """Shapes whose grid would not fit one launch are refused before
+    anything is launched (grid sizes are never truncated)."""
+    f, a, ws, wsb = select_args(R=(1 << 30), W=(1 << 22))
+    assert call_select(a, ws, 1 << 62) == SHAPE
+    assert b"exceed one launch" in B.library().qsa_last_error()
+    g, at, aws, awsb, base = attn_args(R=(1 << 30))
+    assert call_attn(at, aws, 1 << 62) == SHAPE
+
+
+def test_read_probe_checks():
+    lib = B.library()
+    f = Fake()
+    d, k = f.alloc(1 << 20), f.alloc(64)
+    assert lib.qsa_read_probe(None, 1 << 20, ctypes.c_void_p(k), 4, None) == NULL
+    assert lib.qsa_read_probe(ctypes.c_void_p(d + 8), 1 << 20, ctypes.c_void_p(k), 4, None) == LAYOUT
+    assert lib.qsa_read_probe(ctypes.c_void_p(d), (1 << 20) + 4, ctypes.c_void_p(k), 4, None) == LAYOUT
+    assert lib.qsa_read_probe(ctypes.c_void_p(d), 1 << 20, ctypes.c_void_p(k), 2, None) == WORKSPACE
+    assert lib.qsa_read_probe(ctypes.c_void_p(d), 1 << 20, ctypes.c_void_p(d + 64), 4, None) == ALIAS
+    assert lib.qsa_read_probe(ctypes.c_void_p(d), 0, ctypes.c_void_p(k), 4, None) == OK
