@@ -23,7 +23,9 @@ Workloads (``--workload``):
 * multi_token: several query rows per request -- 48 speculative-decode
   requests with 4 draft positions each and 4 chunked-prefill requests with
   16 positions each (R=256), lengths uniform in [8192, 65536], an 8192-page
-  N(0,1) compressed-key cache (256 MiB).
+  N(0,1) compressed-key cache (256 MiB).  The selection queries go in as
+  runs of 4 rows ([64, 4, 4, 128], --rows-per-run), so each run's keys are
+  read once; the row-by-row selection is timed beside it.
 
 Inputs are seeded synthetic data, resident in HBM before timing starts.
 
@@ -244,6 +246,9 @@ def main() -> int:
                                            "long_context_two_pass", "multi_token",
                                            "multi_token_metadata"],
                     default="long_context")
+    ap.add_argument("--rows-per-run", type=int, default=0,
+                    help="pass the selection queries as [R/n, n, 4, 128] (runs of n rows of "
+                         "one request); default 4 for the multi_token workloads, else 1")
     ap.add_argument("--kv-copies", type=int, default=8,
                     help="distinct KV caches the steps rotate over (one per simulated layer)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -295,6 +300,12 @@ def main() -> int:
     else:
         sel_in = [d(a) for a in w.select_inputs()]
         select_fn, decode_fn = qsa.qsa_select, qsa.qsa_decode_step
+    multi = args.workload in ("multi_token", "multi_token_metadata")
+    run = args.rows_per_run or (4 if multi else 1)
+    q_rows = sel_in[0]
+    if run > 1:
+        assert w.rows % run == 0, "rows must split into whole runs"
+        sel_in[0] = q_rows.view(w.rows // run, run, 4, 128)
     # Consecutive decode steps of a model read different layers' caches.  The
     # steps here rotate over distinct KV caches (8 x 128 MiB by default, four
     # times the 256 MB Infinity Cache) so that no step finds its KV in the
@@ -418,6 +429,19 @@ def main() -> int:
                  "fused_weighted_select_ms": round(fused_ev[0].elapsed_time(fused_ev[1]) / args.steps, 4)}
         log(f"two-pass: logits {extra['logits_ms']:.4f} ms + top-k {extra['topk_ms']:.4f} ms; "
             f"fused weighted select {extra['fused_weighted_select_ms']:.4f} ms")
+    if run > 1 and not meta:
+        # the same selection with the queries passed row by row, for comparison
+        flat_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        flat_idx = torch.empty_like(idx)
+        flat_in = [q_rows] + sel_in[1:]
+        select_fn(*flat_in, out=flat_idx, workspace=sel_ws)
+        flat_ev[0].record(stream)
+        for _ in range(args.steps):
+            select_fn(*flat_in, out=flat_idx, workspace=sel_ws)
+        flat_ev[1].record(stream)
+        torch.cuda.synchronize()
+        extra["select_row_by_row_ms"] = round(flat_ev[0].elapsed_time(flat_ev[1]) / args.steps, 4)
+        log(f"selection row by row {extra['select_row_by_row_ms']:.4f} ms")
     log(f"step {ms_per_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms); stages: select "
         f"{np.mean(sel_ms):.4f} ms (min {np.min(sel_ms):.4f}), attention {np.mean(att_ms):.4f} ms")
 
@@ -470,7 +494,7 @@ def main() -> int:
                  "synthetic (seeded N(0,1) fp16 keys/queries/KV, per-head weights U[-0.5, 1.5], "
                  "random permuted block tables)" if two_pass else
                  "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)"),
-        "config": workload_config(w, len(kv_sets)),
+        "config": {**workload_config(w, len(kv_sets)), "rows_per_run": run},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": roof_kernel,

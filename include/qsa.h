@@ -122,7 +122,8 @@ QSA_API void qsa_constants(int32_t* token_topk, int32_t* compress_ratio,
                            int32_t* out_width, int32_t* topk_blocks);
 
 /* Workspace bytes qsa_select needs for `rows` query rows and a block table
- * of `table_width` columns.  0 when rows == 0. */
+ * of `table_width` columns, with q given either way ([R,4,128] or
+ * [B,n,4,128], see qsa_select).  0 when rows == 0. */
 QSA_API size_t qsa_select_workspace_bytes(int64_t rows, int64_t table_width);
 
 /* Workspace bytes qsa_sparse_attn needs for `rows` rows. */
@@ -137,7 +138,17 @@ QSA_API size_t qsa_decode_step_workspace_bytes(int64_t rows, int64_t table_width
  * top-512 selection, expands blocks to 2,048 tokens, appends the tail and
  * writes caller-owned [R,2051] int32 output; "Exact contracts", selection).
  *
- *   q            F16 [R,4,128] contiguous: 4 indexer heads per query row.
+ *   q            F16 [R,4,128] contiguous: 4 indexer heads per query row;
+ *                or F16 [B,n,4,128] contiguous for R = B*n rows that come
+ *                in runs of n consecutive rows of one request, as the
+ *                paged MQA logits call on the page "[XPU] Enable multiple
+ *                key kernels for sparse attention" takes its queries with
+ *                next_n positions per request (speculative decode).  Then
+ *                up to 4 rows of a run are scored against one read of the
+ *                request's keys.  The shape only groups the work: each
+ *                row's request and position still come from token_to_req
+ *                and query_pos, and a run that spans several requests is
+ *                still correct (its requests' keys are read one by one).
  *   kcache       F16 [P,128,1,128] contiguous, P >= 1: compressed keys, 128
  *                per page (vllm qsa_cache.py page: the compressed cache's
  *                block table and slot mapping).

@@ -181,12 +181,20 @@ def _ws_args(nbytes, device, stream_handle, ws, kind):
     return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
 
 
+def _rows(q):
+    """Query rows of a selection query: [R,4,128], or [B,n,4,128] for R = B*n
+    rows in runs of n rows of one request (scored up to 4 at a time)."""
+    return q.shape[0] * q.shape[1] if q.dim() == 4 else q.shape[0]
+
+
 def qsa_select(q, kcache, block_table, token_to_req, seq_lens, query_pos, out=None,
                workspace=None, stream=None):
-    """Paged top-512 selection; returns out ([R,2051] int32)."""
+    """Paged top-512 selection; returns out ([R,2051] int32).  q is
+    [R,4,128], or [B,n,4,128] when rows come in runs of n rows of one
+    request (speculative-decode positions): the runs share key reads."""
     torch = _torch()
     lib = library()
-    R = q.shape[0]
+    R = _rows(q)
     if out is None:
         out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
     sh = _stream(stream, q.device)
@@ -203,7 +211,7 @@ def qsa_select_fp8(q, kcache, kscale, block_table, token_to_req, seq_lens, query
     [P,128,1,128], kscale float32 [P,128]); returns out ([R,2051] int32)."""
     torch = _torch()
     lib = library()
-    R = q.shape[0]
+    R = _rows(q)
     if out is None:
         out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
     sh = _stream(stream, q.device)
@@ -226,7 +234,7 @@ def qsa_select_weighted(q, weights, kcache, block_table, token_to_req, seq_lens,
     codes with kscale); returns out ([R,2051] int32)."""
     torch = _torch()
     lib = library()
-    R = q.shape[0]
+    R = _rows(q)
     if out is None:
         out = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q.device)
     sh = _stream(stream, q.device)
@@ -246,7 +254,7 @@ def qsa_paged_logits(q, kcache, block_table, token_to_req, seq_lens, query_pos, 
     the block table's width x 128; -inf past each row's visible blocks)."""
     torch = _torch()
     lib = library()
-    R = q.shape[0]
+    R = _rows(q)
     if logits is None:
         W = block_table.shape[1] * 128 if width is None else int(width)
         logits = torch.empty((R, W), dtype=torch.float32, device=q.device)
@@ -283,7 +291,7 @@ def qsa_sparse_attn(q, k, v, indices, softmax_scale: float, out=None, workspace=
     """Sparse attention over index rows; returns out ([R,3,256] fp16)."""
     torch = _torch()
     lib = library()
-    R = q.shape[0]
+    R = _rows(q)
     if out is None:
         out = torch.empty((R, 3, 256), dtype=torch.float16, device=q.device)
     sh = _stream(stream, q.device)
@@ -300,7 +308,7 @@ def qsa_decode_step(q_sel, kcache, block_table, token_to_req, seq_lens, query_po
     """Selection then attention on one stream; returns (indices, out)."""
     torch = _torch()
     lib = library()
-    R = q_sel.shape[0]
+    R = _rows(q_sel)
     if indices is None:
         indices = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q_sel.device)
     if out is None:
@@ -324,7 +332,7 @@ def qsa_decode_step_fp8(q_sel, kcache, kscale, block_table, token_to_req, seq_le
     (indices, out)."""
     torch = _torch()
     lib = library()
-    R = q_sel.shape[0]
+    R = _rows(q_sel)
     if indices is None:
         indices = torch.empty((R, OUT_WIDTH), dtype=torch.int32, device=q_sel.device)
     if out is None:

@@ -118,6 +118,7 @@ int check_aligned(const char* name, const qsa_tensor* t, uintptr_t align) {
 
 struct SelectView {
   int64_t rows = 0, pages = 0, reqs = 0, width = 0, bt_stride = 0;
+  int group = 1;  // rows scored per key stream (q given as [B, n, 4, 128]: min(n, 4))
 };
 
 // The selection family's inputs.  e4m3 false: an fp16 key cache (kscale
@@ -126,11 +127,23 @@ int validate_select_inputs(const qsa_tensor* q, const qsa_tensor* weights,
                            const qsa_tensor* kcache, const qsa_tensor* kscale, bool e4m3,
                            const qsa_tensor* bt, const qsa_tensor* t2r, const qsa_tensor* sl,
                            const qsa_tensor* qp, SelectView* v) {
+  // q is [R, 4, 128], or [B, n, 4, 128] for R = B * n rows in runs of n
+  // consecutive rows (next_n draft positions of one request): then rows are
+  // scored min(n, 4) at a time against one read of their keys.  Each row's
+  // request and position still come from token_to_req and query_pos; the
+  // run length only groups the work.
+  const bool runs = q && q->ndim == 4;
   const int64_t any3[3] = {-1, QSA_SEL_HEADS, QSA_SEL_DIM};
-  QSA_TRY(check_tensor("q", q, QSA_DTYPE_F16, 3, any3));
+  const int64_t any4[4] = {-1, -1, QSA_SEL_HEADS, QSA_SEL_DIM};
+  QSA_TRY(runs ? check_tensor("q", q, QSA_DTYPE_F16, 4, any4)
+               : check_tensor("q", q, QSA_DTYPE_F16, 3, any3));
   QSA_TRY(check_contiguous("q", q));
   QSA_TRY(check_aligned("q", q, 16));
-  const int64_t R = q->shape[0];
+  if (runs && (q->shape[0] > ((int64_t)1 << 30) || q->shape[1] > ((int64_t)1 << 30))) {
+    return fail(QSA_ERR_SHAPE, "q: too many rows");
+  }
+  const int64_t R = runs ? q->shape[0] * q->shape[1] : q->shape[0];
+  v->group = runs ? (int)std::max<int64_t>(1, std::min<int64_t>(q->shape[1], qsa::kMaxGroup)) : 1;
   const int64_t kshape[4] = {-1, QSA_PAGE_SLOTS, 1, QSA_SEL_DIM};
   QSA_TRY(check_tensor("kcache", kcache, e4m3 ? QSA_DTYPE_E4M3 : QSA_DTYPE_F16, 4, kshape));
   QSA_TRY(check_contiguous("kcache", kcache));
@@ -300,6 +313,11 @@ int check_grid(const char* what, int64_t rows, int64_t cols) {
   return QSA_OK;
 }
 
+// Grid rows of the chunk kernel: one per group of plan.group query rows.
+int64_t plan_groups(const qsa::SelectPlan& plan, int64_t rows) {
+  return (rows + plan.group - 1) / plan.group;
+}
+
 }  // namespace
 
 namespace qsa {
@@ -308,11 +326,13 @@ namespace qsa {
 // kernel about 1024 workgroups (4 per compute unit on 256 CUs, its
 // occupancy), so long rows are split across the chip while short batches
 // keep chunks small.
-SelectPlan plan_select(int64_t rows, int64_t table_width) {
+SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
   SelectPlan p;
+  p.group = std::max(1, std::min(group, kMaxGroup));
+  const int64_t groups = (rows + p.group - 1) / p.group;
   const int64_t w = table_width > 0 ? table_width : 1;
-  int pages = 32;
-  while (pages > 1 && rows * ((w + pages - 1) / pages) < 1024) pages >>= 1;
+  int pages = max_chunk_pages(p.group);
+  while (pages > 1 && groups * ((w + pages - 1) / pages) < 1024) pages >>= 1;
   p.chunk_pages = pages;
   p.chunks_per_row = (w + pages - 1) / pages;
   p.cand_cap = std::min<int64_t>(kTopKBlocks, (int64_t)pages * kPageSlots);
@@ -388,8 +408,8 @@ int select_impl(const qsa_tensor* q, const qsa_tensor* weights, const qsa_tensor
   QSA_TRY(check_select_output("out", out, q, weights, kcache, kscale, e4m3, block_table,
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
-  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
-  QSA_TRY(check_grid("selection", v.rows, plan.chunks_per_row));
+  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width, v.group);
+  QSA_TRY(check_grid("selection", plan_groups(plan, v.rows), plan.chunks_per_row));
   Span guarded[9] = {span_of(q),        span_of(kcache),   span_of(block_table),
                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
                      span_of(out),      e4m3 ? span_of(kscale) : Span(),
@@ -428,9 +448,9 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
     }
   }
   if (sv.rows == 0) return QSA_OK;
-  const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width);
+  const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width, sv.group);
   const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
-  QSA_TRY(check_grid("selection", sv.rows, splan.chunks_per_row));
+  QSA_TRY(check_grid("selection", plan_groups(splan, sv.rows), splan.chunks_per_row));
   QSA_TRY(check_grid("attention", av.rows, aplan.splits));
   const size_t sel_bytes = align256(splan.bytes);
   const size_t need = sel_bytes + aplan.bytes;
@@ -495,7 +515,12 @@ QSA_API void qsa_constants(int32_t* token_topk, int32_t* compress_ratio, int32_t
 
 QSA_API size_t qsa_select_workspace_bytes(int64_t rows, int64_t table_width) {
   if (rows <= 0) return 0;
-  return qsa::plan_select(rows, table_width).bytes;
+  // enough for every row grouping (q as [R, 4, 128] or [B, n, 4, 128])
+  size_t bytes = 0;
+  for (int group = 1; group <= qsa::kMaxGroup; ++group) {
+    bytes = std::max(bytes, qsa::plan_select(rows, table_width, group).bytes);
+  }
+  return bytes;
 }
 
 QSA_API size_t qsa_sparse_attn_workspace_bytes(int64_t rows) {
@@ -556,8 +581,8 @@ QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
   QSA_TRY(check_select_output("logits", logits, q, weights, kcache, kscale, e4m3, block_table,
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
-  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width);
-  QSA_TRY(check_grid("paged logits", v.rows, plan.chunks_per_row));
+  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width, v.group);
+  QSA_TRY(check_grid("paged logits", plan_groups(plan, v.rows), plan.chunks_per_row));
   qsa::SelectArgs a;
   fill_select_args(a, q, weights, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
                    query_pos, nullptr, nullptr, v);

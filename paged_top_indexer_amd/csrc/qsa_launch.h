@@ -31,12 +31,23 @@ constexpr int64_t padded_rows(int64_t rows) {
   return (rows + kXcds * kRowGroup - 1) / (kXcds * kRowGroup) * (kXcds * kRowGroup);
 }
 
+// Query rows scored together against one key stream: 4 rows x 4 heads fill
+// the 16 rows of the MFMA's A operand.
+constexpr int kMaxGroup = 4;
+
+// Largest chunk (in cache pages) for groups of `group` rows: the chunk
+// kernel keeps group * chunk_pages * 128 scores in LDS (at most 4096), and a
+// group's rows are selected one per wave from at most 1024 scores each.
+constexpr int max_chunk_pages(int group) { return group <= 1 ? 32 : 8; }
+
 // Launch plan of the selection.  A row's visible blocks are cut into chunks
 // of `chunk_pages` cache pages; one workgroup of the chunk kernel scores one
-// chunk and keeps its best min(512, chunk) blocks (a row with a single
-// chunk is finished there).  The merge kernel then takes each multi-chunk
-// row's candidates to the final top-512.
+// chunk for a group of `group` consecutive query rows (reading each of the
+// group's requests' keys once) and keeps each row's best min(512, chunk)
+// blocks (a row with a single chunk is finished there).  The merge kernel
+// then takes each multi-chunk row's candidates to the final top-512.
 struct SelectPlan {
+  int group = 1;               // query rows per chunk workgroup (1..4)
   int chunk_pages = 1;         // pages per chunk (1, 2, 4, 8, 16 or 32)
   int64_t chunks_per_row = 1;  // grid columns per row (ceil(W / chunk_pages))
   int64_t cand_cap = 0;        // candidate slots per chunk: min(512, 128*chunk_pages)
@@ -45,7 +56,7 @@ struct SelectPlan {
   size_t bytes = 0;            // total workspace bytes (0 = none needed)
 };
 
-SelectPlan plan_select(int64_t rows, int64_t table_width);
+SelectPlan plan_select(int64_t rows, int64_t table_width, int group = 1);
 
 // Launch plan of the attention kernel: `splits` workgroups per row, each
 // covering `split_positions` index positions (4 waves x tiles of 16).

@@ -93,6 +93,7 @@ struct SelectParams {
   int64_t chunks_per_row;
   int chunk_blocks;
   int cand_cap;
+  int group;  // consecutive query rows per chunk workgroup (1..4)
 };
 
 // Small scratch of the block-wide helpers (at most 4 waves per workgroup).
@@ -187,18 +188,24 @@ __device__ void radix_pick(const uint32_t* h, uint32_t krem, Scratch& s) {
   const uint32_t incl = wave_incl_scan(local);
   const uint32_t excl = incl - local;
   if (excl < krem && krem <= incl) {
-    uint32_t acc = excl;
+    // (the bin is recorded as its offset j, so that no per-bin index stays
+    // live across a caller's loop)
+    uint32_t acc = excl, before = 0, count = 0;
+    int at = 0;
     bool done = false;
 #pragma unroll
     for (int j = kPer - 1; j >= 0; --j) {
       if (!done && acc + c[j] >= krem) {
-        s.pick[0] = (uint32_t)(lo + j);
-        s.pick[1] = krem - acc;
-        s.pick[2] = c[j];
+        at = j;
+        before = acc;
+        count = c[j];
         done = true;
       }
       acc += c[j];
     }
+    s.pick[0] = (uint32_t)(lo + at);
+    s.pick[1] = krem - before;
+    s.pick[2] = count;
   }
 }
 
@@ -444,7 +451,134 @@ __device__ void sort_expand_write(const uint64_t* list, int k, int64_t visible, 
   }
 }
 
+// The same, as a call: inside the chunk kernel's loop over a group's rows
+// an inlined sort would keep its LDS exchange addresses live across the
+// loop (register spills).
+__device__ __noinline__ void sort_expand_write_call(const uint64_t* list, int k, int64_t visible,
+                                                    int tail, int32_t* out_row, uint64_t* xchg) {
+  sort_expand_write(list, k, visible, tail, out_row, xchg);
+}
+
 constexpr int kChunkWaves = kChunkThreads / 64;
+constexpr int kWaveBins = 256;  // 8-bit radix digits of the one-wave select
+static_assert(kChunkWaves >= kMaxGroup, "one wave per row of a group");
+// chunk size of groups of several rows (max_chunk_pages): a wave holds 16
+// keys per lane
+constexpr int kGroupChunkBlocks = 8 * kPageSlots;
+static_assert(kMaxGroup * kGroupChunkBlocks <= kMaxChunkBlocks, "group scores fit in LDS");
+
+// One wave: emit the best min(k, n) of the n keys keys[0..n) (LDS, n <=
+// 64 * kPer) under the total order (key descending, index ascending) as
+// emit(slot, i, key) with distinct slots 0..min(k, n)-1.  The keys are held
+// in registers (lane l takes indices l, l + 64, ...); an MSB-first radix
+// select over digits of up to 8 bits, starting at the highest bit in which
+// the keys differ (the scores of a chunk share their sign and leading
+// exponent bits, which would put every key in one bin), counts into `hist`
+// (this wave's kWaveBins entries of LDS) and stops at the first digit whose
+// boundary bin is taken whole; keys equal to a fully resolved threshold are
+// taken in index order.  No workgroup barrier: the waves of a workgroup
+// select different rows at the same time.
+template <int kPer, typename Emit>
+__device__ void wave_topk(const uint32_t* keys, int n, int k, uint32_t* hist, Emit emit) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t x[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = 64 * u + lane;
+    x[u] = i < n ? keys[i] : 0u;
+  }
+  // selected: keys > T, plus (when need_eq >= 0) the first need_eq keys == T
+  // in index order; need_eq < 0 means every key >= T
+  uint32_t T = 0;
+  int need_eq = -1;
+  if (k < n) {
+    // bits in which some keys differ: (OR of all) ^ (AND of all)
+    uint32_t all_or = 0, all_and = 0xFFFFFFFFu;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (64 * u + lane < n) {
+        all_or |= x[u];
+        all_and &= x[u];
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      all_or |= (uint32_t)__shfl_xor((int)all_or, m);
+      all_and &= (uint32_t)__shfl_xor((int)all_and, m);
+    }
+    const uint32_t differ = all_or ^ all_and;
+    int top = differ ? 31 - __builtin_clz(differ) : -1;  // highest differing bit
+    // bits every key shares (all of them when the keys are all equal)
+    uint32_t pmask = top < 0 ? 0xFFFFFFFFu : top >= 31 ? 0u : ~((2u << top) - 1u);
+    uint32_t prefix = all_and & pmask;
+    int krem = k;  // rank of the boundary among the keys matching prefix
+    bool whole = false;
+#pragma unroll 1
+    for (; top >= 0 && !whole; top -= 8) {
+      const int shift = max(top - 7, 0);
+      const uint32_t dmask = (2u << (top - shift)) - 1u;  // digit of bits top..shift
+#pragma unroll
+      for (int b = lane; b < kWaveBins; b += 64) hist[b] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        if (64 * u + lane < n && (x[u] & pmask) == prefix) {
+          atomicAdd(&hist[(x[u] >> shift) & dmask], 1u);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // lane l holds the digits 255 - 4l down to 252 - 4l
+      const uint4 h = *reinterpret_cast<const uint4*>(hist + kWaveBins - 4 - 4 * lane);
+      const uint32_t local = h.x + h.y + h.z + h.w;
+      const uint32_t incl = wave_incl_scan(local);
+      const uint32_t excl = incl - local;
+      const bool owner = excl < (uint32_t)krem && (uint32_t)krem <= incl;
+      uint32_t digit = 0, before = 0, count = 0;
+      if (owner) {
+        const uint32_t c[4] = {h.w, h.z, h.y, h.x};  // digits 255 - 4l - j
+        uint32_t acc = excl;
+        bool done = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!done && acc + c[j] >= (uint32_t)krem) {
+            digit = (uint32_t)(kWaveBins - 1 - 4 * lane - j);
+            before = acc;
+            count = c[j];
+            done = true;
+          }
+          acc += c[j];
+        }
+      }
+      const int src = __builtin_ctzll(__ballot(owner));
+      digit = __builtin_amdgcn_readlane(digit, src);
+      before = __builtin_amdgcn_readlane(before, src);
+      count = __builtin_amdgcn_readlane(count, src);
+      prefix |= digit << shift;
+      pmask |= dmask << shift;
+      krem -= (int)before;
+      whole = (int)count == krem;
+    }
+    // all bits resolved and the keys equal to T only partly in (or all
+    // keys equal): the first krem of them in index order
+    T = prefix;
+    need_eq = whole ? -1 : krem;
+  }
+  int base = 0, eq_left = need_eq;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = 64 * u + lane;
+    const bool valid = i < n;
+    const bool gt = valid && (need_eq < 0 ? x[u] >= T : x[u] > T);
+    const bool eq = valid && need_eq >= 0 && x[u] == T;
+    const uint64_t meq = __ballot(eq);
+    const bool take = gt || (eq && __popcll(meq & below) < eq_left);
+    if (need_eq >= 0) eq_left -= min(eq_left, __popcll(meq));
+    const uint64_t mt = __ballot(take);
+    if (take) emit(base + __popcll(mt & below), i, x[u]);
+    base += __popcll(mt);
+  }
+}
 
 // 40 KiB: four workgroups per CU.
 struct ChunkSmem {
@@ -463,18 +597,23 @@ struct ChunkSmem {
       uint64_t sorted[kTopKBlocks];
       Scratch s;
     } sel;
+    // one wave per row (groups of several rows): a radix histogram per wave
+    alignas(16) uint32_t wave_hist[kChunkWaves][kWaveBins];
   } u;
 };
 
-// Where a chunk's scores go.  For a selection: order-preserving keys in
-// LDS, plus the first radix histogram when the chunk needs a select.
+// Where a chunk's scores go: score i of the group's row j lands at
+// keys[j * stride + i].  For a selection: order-preserving keys, plus the
+// first radix histogram when a single-row group's chunk needs a select
+// (groups of several rows count it row by row after scoring).
 struct LdsSink {
   ChunkSmem* sm;
-  bool select;
-  __device__ __forceinline__ void operator()(int i, float sc) const {
+  int stride;
+  bool count;
+  __device__ __forceinline__ void operator()(int j, int i, float sc) const {
     const uint32_t key = score_key(sc);
-    sm->keys[i] = key;
-    if (select) atomicAdd(&sm->hist0[digit0(key)], 1u);
+    sm->keys[j * stride + i] = key;
+    if (count) atomicAdd(&sm->hist0[digit0(key)], 1u);
   }
 };
 
@@ -483,10 +622,28 @@ struct LdsSink {
 // stores in the middle of the key stream slow the stream down).
 struct LogitsSink {
   ChunkSmem* sm;
-  __device__ __forceinline__ void operator()(int i, float sc) const {
-    sm->keys[i] = __float_as_uint(sc);
+  int stride;
+  __device__ __forceinline__ void operator()(int j, int i, float sc) const {
+    sm->keys[j * stride + i] = __float_as_uint(sc);
   }
 };
+
+// The query rows scored in one pass over a chunk's keys: rows r0 + j for
+// the set bits j of `mask`, all of one request.  nblk[j] = the chunk's
+// blocks visible to row r0 + j (0 outside the mask); the pass streams
+// nblk_max keys.
+struct PassRows {
+  int64_t r0;
+  uint32_t mask;
+  int nblk[kMaxGroup];
+  int nblk_max;
+};
+
+// a[j] for a lane-varying j, with constant indices only (the array stays
+// in registers).
+__device__ __forceinline__ int pick_row(const int (&a)[kMaxGroup], int j) {
+  return j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[2] : a[3];
+}
 
 // The row's per-head weights (all 1 without a weights tensor) and the
 // weighted sum of the ReLU'd head dots of one key (acc[h] = head h).
@@ -558,26 +715,32 @@ __device__ __forceinline__ int tile_keys(int t, int tt, int ntiles, int nblk, ui
 }
 
 // fp16 keys.  MFMA k step c covers dims [32c, 32c + 32): lane (n + 16g)
-// holds dims [32c + 8g, +8) of key n (B) or of head n (A).
+// holds dims [32c + 8g, +8) of key n (B) or of A row n = head n % 4 of the
+// pass's row n / 4.  The result of key n for row j (its 4 heads) lands in
+// lane n + 16j.
 template <typename Sink>
-__device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem& sm, int64_t r,
-                                                int64_t req, int64_t chunk_base, int nblk,
-                                                const Sink& sink) {
+__device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem& sm,
+                                                const PassRows& pr, int64_t req,
+                                                int64_t chunk_base, const Sink& sink) {
   constexpr int kUnroll = 4;  // tiles in flight per wave (4 KiB each)
   constexpr int kPageBytes = kPageSlots * kSelDim * 2;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15;  // key column of B / head row of A
-  const int g = lane >> 4;  // 8-element slice of each 32-wide k step
+  const int n = lane & 15;  // key column of B / row of A
+  const int g = lane >> 4;  // 8-element slice of each 32-wide k step / row of the result
+  const int nblk = pr.nblk_max;
   half8 qa[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     qa[c] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (n < kSelHeads) {
-      qa[c] = *reinterpret_cast<const half8*>(p.q + (r * kSelHeads + n) * kSelDim + 32 * c + 8 * g);
+    if ((pr.mask >> (n >> 2)) & 1) {
+      const int64_t qrow = (pr.r0 + (n >> 2)) * kSelHeads + (n & 3);
+      qa[c] = *reinterpret_cast<const half8*>(p.q + qrow * kSelDim + 32 * c + 8 * g);
     }
   }
-  const HeadWeights hw = head_weights(p, r);
+  const bool out_row = (pr.mask >> g) & 1;
+  const HeadWeights hw = head_weights(p, out_row ? pr.r0 + g : pr.r0);
+  const int row_nblk = pick_row(pr.nblk, g);  // 0 for lanes of rows outside the pass
   bool page_valid;
   const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
@@ -642,9 +805,9 @@ __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[c], kb, acc, 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
-      // lanes 0..15 hold heads 0..3 of key n
+      // lane n + 16g holds heads 0..3 of key n for the pass's row g
       const float sc = head_sum(acc, hw);
-      if (g == 0 && 16 * t + n < nblk) sink(16 * t + n, sc);
+      if (16 * t + n < row_nblk) sink(g, 16 * t + n, sc);
     }
   }
 }
@@ -667,11 +830,11 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
 // e4m3 keys.  The dot product does not care in which order the k steps
 // visit the 128 dims, so each lane takes 32 contiguous bytes of its key:
 // MFMA k step c gives lane (n + 16g) dims [32g + 8c, +8) of key n (B) or of
-// head n (A).
+// A row n (head n % 4 of the pass's row n / 4); results as for fp16 keys.
 template <typename Sink>
-__device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm, int64_t r,
-                                                 int64_t req, int64_t chunk_base, int nblk,
-                                                 const Sink& sink) {
+__device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm,
+                                                 const PassRows& pr, int64_t req,
+                                                 int64_t chunk_base, const Sink& sink) {
   constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each)
   constexpr int kPageBytes = kPageSlots * kSelDim;
   constexpr int kScaleBytes = kPageSlots * 4;
@@ -679,15 +842,19 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int nblk = pr.nblk_max;
   half8 qa[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     qa[c] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (n < kSelHeads) {
-      qa[c] = *reinterpret_cast<const half8*>(p.q + (r * kSelHeads + n) * kSelDim + 32 * g + 8 * c);
+    if ((pr.mask >> (n >> 2)) & 1) {
+      const int64_t qrow = (pr.r0 + (n >> 2)) * kSelHeads + (n & 3);
+      qa[c] = *reinterpret_cast<const half8*>(p.q + qrow * kSelDim + 32 * g + 8 * c);
     }
   }
-  const HeadWeights hw = head_weights(p, r);
+  const bool out_row = (pr.mask >> g) & 1;
+  const HeadWeights hw = head_weights(p, out_row ? pr.r0 + g : pr.r0);
+  const int row_nblk = pick_row(pr.nblk, g);
   bool page_valid;
   const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
@@ -761,7 +928,7 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
       const float sum = head_sum(acc, hw);
       // scale * 2^8 is exact, so this is one rounding of scale * code-sum
       const float sc = sum * (scale[u] * 256.f);
-      if (g == 0 && 16 * t + n < nblk) sink(16 * t + n, sc);
+      if (16 * t + n < row_nblk) sink(g, 16 * t + n, sc);
       issue_scale(u, t + kChunkWaves * kUnroll);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -785,7 +952,7 @@ __device__ __forceinline__ void score_chunk_logits(const SelectParams& p, int64_
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i = i0 + u * kChunkThreads;
-      if (i < nblk) sink(i, v[u]);
+      if (i < nblk) sink(0, i, v[u]);
     }
   }
 }
@@ -795,88 +962,185 @@ enum : int { kSrcF16 = 0, kSrcE4M3 = 1, kSrcLogits = 2 };
 
 
 // kSrc: where the scores come from; kLogitsOut: write them as a logits row
-// (and -inf past the visible blocks) instead of selecting.
-template <int kSrc, bool kLogitsOut>
+// (and -inf past the visible blocks) instead of selecting.  Workgroup (g, c)
+// scores chunk c of the rows of group g (p.group consecutive rows; kGroup =
+// 1 when p.group is 1, else kMaxGroup); rows of the group that share a
+// request are scored in one pass over its keys (a group that spans several
+// requests takes one pass per request).
+template <int kSrc, bool kLogitsOut, int kGroup>
 __global__ __launch_bounds__(kChunkThreads, 4) void qsa_select_chunk_kernel(SelectParams p) {
   __shared__ ChunkSmem sm;
   const int tid = threadIdx.x;
   const RowCol id = row_col_of_block(blockIdx.x, p.chunks_per_row);  // XCD-aware placement
-  const int64_t r = id.row;
+  const int group = kGroup == 1 ? 1 : p.group;
+  const int64_t r0 = id.row * group;
   const int64_t chunk = id.col;
-  if (r >= p.rows) return;
-  const Row row = row_setup(p, r);
+  if (r0 >= p.rows) return;
+  const int rows_here = kGroup == 1 ? 1 : (int)min((int64_t)group, p.rows - r0);
   const int64_t chunk_base = chunk * p.chunk_blocks;
-  const int nblk = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
 
-  if constexpr (kLogitsOut) {
-    float* out_row = p.logits_out + r * p.logits_stride;
-    if (nblk > 0) {
-      const LogitsSink sink{&sm};
-      if constexpr (kSrc == kSrcE4M3) {
-        score_chunk_e4m3(p, sm, r, row.req, chunk_base, nblk, sink);
-      } else {
-        score_chunk_f16(p, sm, r, row.req, chunk_base, nblk, sink);
-      }
-      __syncthreads();
-      for (int i = tid; i < nblk; i += kChunkThreads) {
-        __builtin_nontemporal_store(__uint_as_float(sm.keys[i]), out_row + chunk_base + i);
-      }
+  // The group's rows (uniform values, constant indices): request, blocks of
+  // this chunk, and which rows have work here (a selection's chunk past a
+  // row's last one has none; paged logits fill every column).
+  int64_t req[kMaxGroup];
+  int nblk[kMaxGroup];
+  uint32_t live = 0;   // rows with work in this chunk
+  uint32_t single = 0; // rows whose only chunk this is (finished here)
+  Row row0;
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) {
+    req[j] = -1;
+    nblk[j] = 0;
+    if (j < rows_here) {
+      const Row row = row_setup(p, r0 + j);
+      if (j == 0) row0 = row;
+      req[j] = row.req;
+      nblk[j] = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
+      if (kLogitsOut || chunk < row.nchunks) live |= 1u << j;
+      if (row.nchunks == 1) single |= 1u << j;
     }
-    // -inf from the row's end (or the chunk's start) to the chunk's end; the
-    // last chunk column also covers the columns past all chunks
-    const int64_t lo = max(row.visible, chunk_base);
-    const int64_t hi = chunk == p.chunks_per_row - 1
-                           ? p.logits_width
-                           : min(chunk_base + (int64_t)p.chunk_blocks, p.logits_width);
-    for (int64_t b = lo + tid; b < hi; b += kChunkThreads) out_row[b] = -__builtin_inff();
-    return;
   }
+  if (live == 0) return;
 
-  if (chunk >= row.nchunks) return;
-  const bool select = nblk > kTopKBlocks;
-  if (select) {
+  const bool count_hist = !kLogitsOut && kGroup == 1 && nblk[0] > kTopKBlocks;
+  if (count_hist) {
     for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
     __syncthreads();
   }
-  const LdsSink sink{&sm, select};
-  if constexpr (kSrc == kSrcLogits) {
-    score_chunk_logits(p, r, chunk_base, nblk, sink);
-  } else if constexpr (kSrc == kSrcE4M3) {
-    score_chunk_e4m3(p, sm, r, row.req, chunk_base, nblk, sink);
+  auto score_all = [&](const auto& sink) {
+    if constexpr (kSrc == kSrcLogits) {
+      score_chunk_logits(p, r0, chunk_base, nblk[0], sink);  // one row per group
+      return;
+    }
+    uint32_t todo = 0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      if (((live >> j) & 1) && nblk[j] > 0) todo |= 1u << j;
+    }
+#pragma unroll 1
+    while (todo != 0) {
+      const int lead = __builtin_ctz(todo);
+      const int64_t rq = lead == 0 ? req[0] : lead == 1 ? req[1] : lead == 2 ? req[2] : req[3];
+      PassRows pr;
+      pr.r0 = r0;
+      pr.mask = 0;
+      pr.nblk_max = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxGroup; ++j) {
+        const bool in = j < kGroup && ((todo >> j) & 1) && req[j] == rq;
+        pr.nblk[j] = in ? nblk[j] : 0;
+        pr.mask |= in ? 1u << j : 0u;
+        pr.nblk_max = max(pr.nblk_max, pr.nblk[j]);
+      }
+      todo &= ~pr.mask;
+      if constexpr (kSrc == kSrcE4M3) {
+        score_chunk_e4m3(p, sm, pr, rq, chunk_base, sink);
+      } else {
+        score_chunk_f16(p, sm, pr, rq, chunk_base, sink);
+      }
+    }
+  };
+  if constexpr (kLogitsOut) {
+    score_all(LogitsSink{&sm, p.chunk_blocks});
   } else {
-    score_chunk_f16(p, sm, r, row.req, chunk_base, nblk, sink);
+    score_all(LdsSink{&sm, p.chunk_blocks, count_hist});
   }
   __syncthreads();
 
-  // ---- chunk top-k ---------------------------------------------------------
-  const int k_local = min(kTopKBlocks, nblk);
-  uint32_t T = 0, bcut = 0xFFFFFFFFu;  // every key >= 0: all are taken
-  auto lds_key = [&](int i) { return sm.keys[i]; };
-  auto block_of = [&](int i) { return (uint32_t)(chunk_base + i); };
-  Scratch& s = sm.u.sel.s;
-  if (select) {
-    topk_threshold<kChunkThreads>(lds_key, block_of, nblk, k_local, s, sm.hist0, sm.u.sel.hist1,
-                                  T, bcut);
-  }
-
-  if (row.nchunks == 1) {
-    uint64_t* sorted = sm.u.sel.sorted;
-    compact_topk<kChunkThreads>(
-        lds_key, block_of, nblk, T, bcut,
-        [&](uint32_t slot, int i, uint32_t x) { sorted[slot] = pack(x, block_of(i)); }, s);
-    sort_expand_write(sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth, sorted);
+  if constexpr (kLogitsOut) {
+#pragma unroll 1
+    for (int j = 0; j < rows_here; ++j) {
+      const int64_t r = r0 + j;
+      const Row row = row_setup(p, r);
+      const int nb = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
+      float* out_row = p.logits_out + r * p.logits_stride;
+      const uint32_t* keys = sm.keys + j * p.chunk_blocks;
+      for (int i = tid; i < nb; i += kChunkThreads) {
+        __builtin_nontemporal_store(__uint_as_float(keys[i]), out_row + chunk_base + i);
+      }
+      // -inf from the row's end (or the chunk's start) to the chunk's end;
+      // the last chunk column also covers the columns past all chunks
+      const int64_t lo = max(row.visible, chunk_base);
+      const int64_t hi = chunk == p.chunks_per_row - 1
+                             ? p.logits_width
+                             : min(chunk_base + (int64_t)p.chunk_blocks, p.logits_width);
+      for (int64_t b = lo + tid; b < hi; b += kChunkThreads) out_row[b] = -__builtin_inff();
+    }
     return;
   }
-  const int64_t cbase = (r * p.chunks_per_row + chunk) * p.cand_cap;
-  uint32_t* ckeys = p.cand_keys + cbase;
-  uint32_t* cblocks = p.cand_blocks + cbase;
-  compact_topk<kChunkThreads>(
-      lds_key, block_of, nblk, T, bcut,
-      [&](uint32_t slot, int i, uint32_t x) {
-        ckeys[slot] = x;
-        cblocks[slot] = block_of(i);
-      },
-      s);
+
+  // ---- chunk top-k, row by row ---------------------------------------------
+  auto row_topk = [&](int j, const Row& row) {
+    const int64_t r = r0 + j;
+    const int nb = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
+    const bool select = nb > kTopKBlocks;
+    const uint32_t* keys = sm.keys + j * p.chunk_blocks;
+    if (select && !count_hist) {
+      for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < nb; i += kChunkThreads) atomicAdd(&sm.hist0[digit0(keys[i])], 1u);
+      __syncthreads();
+    }
+    const int k_local = min(kTopKBlocks, nb);
+    uint32_t T = 0, bcut = 0xFFFFFFFFu;  // every key >= 0: all are taken
+    auto lds_key = [&](int i) { return keys[i]; };
+    auto block_of = [&](int i) { return (uint32_t)(chunk_base + i); };
+    Scratch& s = sm.u.sel.s;
+    if (select) {
+      topk_threshold<kChunkThreads>(lds_key, block_of, nb, k_local, s, sm.hist0, sm.u.sel.hist1,
+                                    T, bcut);
+    }
+    if (row.nchunks == 1) {
+      uint64_t* sorted = sm.u.sel.sorted;
+      compact_topk<kChunkThreads>(
+          lds_key, block_of, nb, T, bcut,
+          [&](uint32_t slot, int i, uint32_t x) { sorted[slot] = pack(x, block_of(i)); }, s);
+      if constexpr (kGroup == 1) {
+        sort_expand_write(sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth, sorted);
+      } else {
+        sort_expand_write_call(sorted, k_local, row.visible, row.tail, p.out + r * kOutWidth,
+                               sorted);
+      }
+    } else {
+      const int64_t cbase = (r * p.chunks_per_row + chunk) * p.cand_cap;
+      uint32_t* ckeys = p.cand_keys + cbase;
+      uint32_t* cblocks = p.cand_blocks + cbase;
+      compact_topk<kChunkThreads>(
+          lds_key, block_of, nb, T, bcut,
+          [&](uint32_t slot, int i, uint32_t x) {
+            ckeys[slot] = x;
+            cblocks[slot] = block_of(i);
+          },
+          s);
+    }
+  };
+  if constexpr (kGroup == 1) {
+    row_topk(0, row0);
+  } else {
+    // rows of several chunks: wave j keeps row j's best keys of the chunk,
+    // all rows at once
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (wave < rows_here && (((live & ~single) >> wave) & 1)) {
+      const int64_t r = r0 + wave;
+      const int64_t cbase = (r * p.chunks_per_row + chunk) * p.cand_cap;
+      uint32_t* ckeys = p.cand_keys + cbase;
+      uint32_t* cblocks = p.cand_blocks + cbase;
+      wave_topk<kGroupChunkBlocks / 64>(
+          sm.keys + wave * p.chunk_blocks, pick_row(nblk, wave), kTopKBlocks,
+          sm.u.wave_hist[wave], [&](int slot, int i, uint32_t x) {
+            ckeys[slot] = x;
+            cblocks[slot] = (uint32_t)(chunk_base + i);
+          });
+    }
+    // rows finished here (a single chunk) are sorted and written block-wide
+#pragma unroll 1
+    for (int j = 0; j < rows_here; ++j) {
+      if (((live & single) >> j) & 1) {
+        __syncthreads();  // the LDS scratch is free again
+        row_topk(j, row_setup(p, r0 + j));
+      }
+    }
+  }
 }
 
 struct MergeSmem {
@@ -893,7 +1157,10 @@ struct MergeSmem {
 __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectParams p) {
   __shared__ MergeSmem sm;
   const int tid = threadIdx.x;
-  const int64_t r = row_on_xcd(blockIdx.x % kXcds, blockIdx.x / kXcds);
+  // row s % group of the chunk kernel's (s / group)-th group on this XCD:
+  // a row is merged on the XCD that scored it
+  const int64_t s = blockIdx.x / kXcds;
+  const int64_t r = row_on_xcd(blockIdx.x % kXcds, s / p.group) * p.group + s % p.group;
   if (r >= p.rows) return;
   const Row row = row_setup(p, r);
   if (row.nchunks == 1) return;  // finished by the chunk kernel
@@ -1015,14 +1282,23 @@ SelectParams make_params(const SelectArgs& a, const SelectPlan& plan) {
   p.chunks_per_row = plan.chunks_per_row;
   p.chunk_blocks = plan.chunk_pages * kPageSlots;
   p.cand_cap = (int)plan.cand_cap;
+  p.group = plan.group;
   return p;
 }
 
 template <int kSrc, bool kLogitsOut>
 void launch_chunks(const SelectParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut>),
-                     dim3((unsigned)(p.chunks_per_row * padded_rows(p.rows))), dim3(kChunkThreads),
-                     0, s, p);
+  const int64_t groups = (p.rows + p.group - 1) / p.group;
+  const dim3 grid((unsigned)(p.chunks_per_row * padded_rows(groups)));
+  if constexpr (kSrc != kSrcLogits) {  // (logits rows are never grouped)
+    if (p.group > 1) {
+      hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, kMaxGroup>), grid,
+                         dim3(kChunkThreads), 0, s, p);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, 1>), grid, dim3(kChunkThreads), 0,
+                     s, p);
 }
 
 }  // namespace
@@ -1040,7 +1316,8 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.chunks_per_row == 1) return (int)err;
-  hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)padded_rows(a.rows)),
+  const int64_t groups = (a.rows + p.group - 1) / p.group;
+  hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)(padded_rows(groups) * p.group)),
                      dim3(kMergeThreads), 0, s, p);
   return (int)hipGetLastError();
 }

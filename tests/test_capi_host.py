@@ -145,6 +145,11 @@ SELECT_CASES = {
     "out_aliases_kcache": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2051), 4, ptr=a["kcache"].data)), ALIAS),
     "out_aliases_q": (lambda f, a: a.__setitem__("out", mk(f, B.I32, (4, 2051), 4, ptr=a["q"].data + 64)), ALIAS),
     "null_table": (lambda f, a: a.__setitem__("bt", None), NULL),
+    # q as runs [B, n, 4, 128]: R = B * n must match the per-row inputs
+    "runs_heads": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (2, 2, 3, 128), 2)), SHAPE),
+    "runs_rows": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (2, 3, 4, 128), 2)), SHAPE),
+    "runs_dtype": (lambda f, a: a.__setitem__("q", mk(f, B.F32, (2, 2, 4, 128), 4)), DTYPE),
+    "runs_strided": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (2, 2, 4, 128), 2, stride=(2048, 512, 128, 1))), LAYOUT),
 }
 
 
@@ -456,6 +461,26 @@ def test_metadata_scalar_and_workspace_checks():
     # no tokens and no work items: nothing to do
     f, a, ws, wsb = meta_args(T=0, M=0)
     assert call_meta(a, 0, 0) == OK
+
+
+def test_select_runs_zero_rows_and_workspace():
+    """q given as runs [B, n, 4, 128]: zero rows either way is a no-op; the
+    grouped plan cuts rows into smaller chunks (more candidates) and the
+    workspace query covers it."""
+    for shape in [(0, 4, 4, 128), (3, 0, 4, 128)]:
+        f, a, ws, wsb = select_args(R=0)
+        a["q"] = mk(f, B.F16, shape, 2)
+        assert call_select(a, 0, 0) == OK
+    R, W = 128, 256
+    f, a, ws, wsb = select_args(R=R, W=W)
+    # 4-row groups: 32 groups x 32 chunks of 8 pages, 512 candidates each
+    assert wsb >= R * 32 * 512 * 8
+    a["q"] = mk(f, B.F16, (R // 4, 4, 4, 128), 2)
+    assert call_select(a, ws, R * 8 * 512 * 8) == WORKSPACE  # sized for rows one by one
+    f, a, ws, wsb = select_args(R=R, W=W)
+    a["q"] = mk(f, B.F16, (R // 4, 4, 4, 128), 2)
+    a["t2r"] = mk(f, B.I32, (R + 1,), 4)
+    assert call_select(a, ws, wsb) == SHAPE
 
 
 def test_launch_size_limits():
