@@ -831,13 +831,18 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
 // visit the 128 dims, so each lane takes 32 contiguous bytes of its key:
 // MFMA k step c gives lane (n + 16g) dims [32g + 8c, +8) of key n (B) or of
 // A row n (head n % 4 of the pass's row n / 4); results as for fp16 keys.
+// Each wave walks whole pages (pages wave, wave + 4, ... of the chunk; eight
+// 16-key tiles each), so a page's 128 scales are read once per wave as two
+// coalesced 256-byte loads (slots l and 64 + l in lane l), one page ahead,
+// and a tile takes its keys' scales from them with a lane permute.
 template <typename Sink>
 __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm,
                                                  const PassRows& pr, int64_t req,
                                                  int64_t chunk_base, const Sink& sink) {
-  constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each)
+  constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each): one page
   constexpr int kPageBytes = kPageSlots * kSelDim;
   constexpr int kScaleBytes = kPageSlots * 4;
+  static_assert(kUnroll * 16 == kPageSlots, "a pipeline pass is one page");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;
@@ -859,19 +864,22 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
   const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
   const int ntiles = (nblk + 15) >> 4;
-  if (wave >= ntiles) return;
+  const int npages = (nblk + kPageSlots - 1) / kPageSlots;
+  // the wave's tiles: k-th = tile k % 8 of the wave's (k / 8)-th page
+  const int nk = npages > wave ? kUnroll * ((npages - wave + kChunkWaves - 1) / kChunkWaves) : 0;
+  if (nk == 0) return;
+  auto tile_of = [&](int k) { return kUnroll * (wave + kChunkWaves * (k / kUnroll)) + k % kUnroll; };
   u32x4(*stage)[8] = sm.u.stage8[wave];
   const int s8 = lane & 7;     // 16-byte chunk of a key this lane loads
   const int k8 = lane >> 3;    // key of the 8-key half tile this lane loads
 
   // Coalesced nontemporal loads: instruction c reads keys 8c..8c+7 of a
-  // tile (1 KiB contiguous), lane l taking chunk l % 8 of key 8c + l / 8;
-  // every lane also reads the scale of key l % 16 (64 bytes per tile).
+  // tile (1 KiB contiguous), lane l taking chunk l % 8 of key 8c + l / 8.
   u32x4 raw[kUnroll][2];
-  float scale[kUnroll];
-  auto issue_keys = [&](int u, int t) {
-    const int tt = min(t, ntiles - 1);
-    const int live = tile_keys(t, tt, ntiles, nblk, valid_mask);
+  auto issue_keys = [&](int u, int k) {
+    const int tt = tile_of(min(k, nk - 1));
+    const int on_page = (int)((valid_mask >> (tt >> 3)) & 1);
+    const int live = k < nk && tt < ntiles ? min(16, nblk - 16 * tt) * on_page : 0;
     const int32_t page = __builtin_amdgcn_readlane(pages, tt >> 3);
     const __amdgpu_buffer_rsrc_t rk = page_rsrc(p.kcodes + (int64_t)page * kPageSlots * kSelDim,
                                                 kPageBytes);
@@ -884,37 +892,43 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
                                                        kNontemporal));
     }
   };
-  auto issue_scale = [&](int u, int t) {
-    const int tt = min(t, ntiles - 1);
-    const int live = tile_keys(t, tt, ntiles, nblk, valid_mask);
-    const int32_t page = __builtin_amdgcn_readlane(pages, tt >> 3);
+  // the 128 scales of the page whose first tile is the wave's k-th
+  auto issue_scales = [&](float (&dst)[2], int k) {
+    const int pg = tile_of(min(k, nk - 1)) >> 3;  // page within the chunk
+    const bool ok = k < nk && ((valid_mask >> pg) & 1);
+    const int32_t page = __builtin_amdgcn_readlane(pages, pg);
     const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kscale + (int64_t)page * kPageSlots, kScaleBytes);
-    const uint32_t off = (uint32_t)(((16 * tt) & (kPageSlots - 1)) + n) * 4;
-    scale[u] = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rs, n < live ? off : kOutOfRange, 0,
-                                                    kNontemporal));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      dst[h] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? (uint32_t)(64 * h + lane) * 4
+                                                             : kOutOfRange,
+                                                      0, kNontemporal));
+    }
   };
-  // Rolling pipeline, as in the fp16 scorer; a slot's scale is refilled
-  // only once its score is stored, so the old and new scale never need two
-  // registers (the scheduling barriers keep the loads in the order the
-  // per-tile waits rely on).
+  // Rolling pipeline, as in the fp16 scorer, one page per pass: slot u holds
+  // tile u of the current page and is refilled with tile u of the next one;
+  // the next page's scales are loaded with its first tile (the scheduling
+  // barriers keep the loads in the order the per-tile waits rely on).
+  float scale_cur[2], scale_next[2];
+  issue_scales(scale_cur, 0);
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    issue_keys(u, wave + u * kChunkWaves);
-    issue_scale(u, wave + u * kChunkWaves);
+    issue_keys(u, u);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll 1
-  for (int t0 = wave; t0 < ntiles; t0 += kChunkWaves * kUnroll) {
+  for (int k0 = 0; k0 < nk; k0 += kUnroll) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kChunkWaves;
+      const int tt = tile_of(k0 + u);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int key = 8 * c + k8;
         stage[key][s8 ^ (key & 7)] = raw[u][c];
       }
-      issue_keys(u, t + kChunkWaves * kUnroll);
+      issue_keys(u, k0 + u + kUnroll);
+      if (u == 0) issue_scales(scale_next, k0 + kUnroll);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_wave_barrier();
       const u32x4 lo = stage[n][(2 * g) ^ (n & 7)];      // dims [32g, 32g + 16)
@@ -926,12 +940,17 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
       acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[3], e4m3x8_to_half8(hi[2], hi[3]), acc, 0, 0, 0);
       __builtin_amdgcn_wave_barrier();
       const float sum = head_sum(acc, hw);
+      // key n of tile u is page slot 16u + n: in lane (16u + n) % 64 of
+      // scale_cur[u / 4]
+      const float scale = __builtin_bit_cast(
+          float, __builtin_amdgcn_ds_bpermute(4 * (16 * (u % 4) + n),
+                                              __builtin_bit_cast(int, scale_cur[u / 4])));
       // scale * 2^8 is exact, so this is one rounding of scale * code-sum
-      const float sc = sum * (scale[u] * 256.f);
-      if (16 * t + n < row_nblk) sink(g, 16 * t + n, sc);
-      issue_scale(u, t + kChunkWaves * kUnroll);
-      __builtin_amdgcn_sched_barrier(0);
+      const float sc = sum * (scale * 256.f);
+      if (16 * tt + n < row_nblk) sink(g, 16 * tt + n, sc);
     }
+    scale_cur[0] = scale_next[0];
+    scale_cur[1] = scale_next[1];
   }
 }
 
