@@ -57,7 +57,7 @@ if ROOT not in sys.path:
 METRIC = "select+sparse-attn decode rows/sec and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
-                  for f in ("qsa_select.hip", "qsa_device.h", "qsa_launch.h", "qsa_capi.cpp")]
+                  for f in ("qsa_select.hip", "qsa_device.h", "qsa_launch.h", "qsa_select_plan.cpp")]
 
 
 def log(msg: str) -> None:

@@ -21,7 +21,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["qsa_select.hip", "qsa_attn.hip", "qsa_metadata.hip", "qsa_probe.hip"]
-HOST_SOURCES = ["qsa_capi.cpp"]
+HOST_SOURCES = ["qsa_capi.cpp", "qsa_select_plan.cpp"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -93,7 +93,18 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
   const int pos_begin = split * p.split_positions + wave * wave_positions;
   const int pos_end = min(kOutWidth, pos_begin + wave_positions);
   const int32_t* idx_row = p.indices + r * kOutWidth;
+  // The wave's indices come 64 at a time, one per lane, the next 64 loaded
+  // while the current ones are used: a tile's gathers wait only for their
+  // own data.
+  auto group_index = [&](int g0) {
+    const int gp = g0 + lane;
+    return gp < pos_end ? idx_row[gp] : -1;
+  };
+  int32_t idx_next = group_index(pos_begin);
 
+  int32_t group_idx = -1;
+  bool group_valid = false;
+  uint64_t group_mask = 0;
   float m_run = -INFINITY;  // running max of head n (base-2 logits)
   float l_run = 0.f;        // this lane's share of the running sum of head n
   float o[kAttHeads][4];
@@ -104,12 +115,17 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
 
 #pragma unroll 1
   for (int tile = pos_begin; tile < pos_end; tile += 16) {
-    const int pos = tile + n;
-    int32_t idx = -1;
-    if (pos < pos_end) idx = idx_row[pos];
-    const bool valid = idx >= 0 && idx < p.num_tokens;
-    const int64_t tok = valid ? idx : 0;
-    const uint64_t vmask = __ballot(valid);  // bit t: position tile + t is valid
+    const int sub = ((tile - pos_begin) >> 4) & 3;  // tile within its group of 64 positions
+    if (sub == 0) {
+      group_idx = idx_next;
+      group_valid = group_idx >= 0 && group_idx < p.num_tokens;
+      group_mask = __ballot(group_valid);
+      idx_next = group_index(tile + 64);
+    }
+    // lane l: the token of position tile + l % 16
+    const int32_t idx = __builtin_amdgcn_ds_bpermute(4 * (16 * sub + n), group_valid ? group_idx : 0);
+    const int64_t tok = idx;
+    const uint64_t vmask = (group_mask >> (16 * sub)) & 0xFFFFull;  // bit t: position tile + t is valid
 
     // K rows of the 16 positions (A operand) and this lane's slice of the
     // 16 V rows, all issued before any math.
@@ -120,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
     half4 vv[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int64_t tt = __builtin_amdgcn_readlane((int)tok, t);
+      const int64_t tt = __builtin_amdgcn_readlane(idx, t);
       vv[t] = *reinterpret_cast<const half4*>(p.kv + tt * kKvRow + kAttDim + 4 * lane);
     }
 

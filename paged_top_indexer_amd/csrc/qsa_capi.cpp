@@ -322,40 +322,18 @@ int64_t plan_groups(const qsa::SelectPlan& plan, int64_t rows) {
 
 namespace qsa {
 
-// Chunk size: the largest of 32/16/8/4/2/1 pages that still gives the chunk
-// kernel about 1024 workgroups (4 per compute unit on 256 CUs, its
-// occupancy), so long rows are split across the chip while short batches
-// keep chunks small.
-SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
-  SelectPlan p;
-  p.group = std::max(1, std::min(group, kMaxGroup));
-  const int64_t groups = (rows + p.group - 1) / p.group;
-  const int64_t w = table_width > 0 ? table_width : 1;
-  int pages = max_chunk_pages(p.group);
-  while (pages > 1 && groups * ((w + pages - 1) / pages) < 1024) pages >>= 1;
-  p.chunk_pages = pages;
-  p.chunks_per_row = (w + pages - 1) / pages;
-  p.cand_cap = std::min<int64_t>(kTopKBlocks, (int64_t)pages * kPageSlots);
-  if (rows == 0 || p.chunks_per_row == 1) {
-    p.bytes = 0;
-    return p;
-  }
-  size_t off = 0;
-  const size_t cands = (size_t)rows * (size_t)p.chunks_per_row * (size_t)p.cand_cap;
-  p.keys_off = off;
-  off = align256(off + cands * sizeof(uint32_t));
-  p.blocks_off = off;
-  off = align256(off + cands * sizeof(uint32_t));
-  p.bytes = off;
-  return p;
-}
 
-// Split length: 128 index positions per workgroup (two 16-position tiles
-// per wave) for batches, shorter for small batches so that a single row
-// still spreads over enough workgroups.
+// Split length: enough splits for about one resident round of attention
+// workgroups over the batch (3 per CU on 256 CUs), in multiples of 64 index
+// positions (each wave loads its indices 64 at a time), at most 33 splits of
+// 64 positions; a batch of 768 rows or more gets one split per row.
 AttnPlan plan_attn(int64_t rows) {
   AttnPlan p;
-  p.split_positions = rows >= 16 ? 128 : 64;
+  constexpr int64_t kResident = 768;
+  constexpr int64_t kMaxSplits = (kOutWidth + 63) / 64;
+  const int64_t want =
+      rows > 0 ? std::min(kMaxSplits, std::max<int64_t>(1, (kResident + rows - 1) / rows)) : 1;
+  p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
   p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
   if (rows == 0) return p;
   size_t off = 0;
