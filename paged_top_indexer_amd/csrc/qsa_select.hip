@@ -12,10 +12,13 @@
 // top-k per row over the logits matrix).
 //
 // Design (MI355X / CDNA4):
-//  * Chunk kernel, grid = rows x chunks.  A chunk is `chunk_pages` cache
-//    pages (128 compressed keys of 256 B each per page, one contiguous
-//    32 KiB run).  Workgroups whose chunk lies past the row's visible blocks
-//    exit at once.
+//  * Chunk kernel, grid = row groups x chunks.  A chunk is `chunk_pages`
+//    cache pages (128 compressed keys of 256 B each per page, one contiguous
+//    32 KiB run).  A group is one query row, or up to 4 consecutive rows
+//    when the queries come as runs [B, n, 4, 128] (several positions of one
+//    request): the group's rows of one request share one read of the keys.
+//    Workgroups whose chunk lies past every row's visible blocks exit at
+//    once.
 //  * Key caches: fp16 keys (256 B each), or e4m3 codes (128 B each) with one
 //    fp32 scale per key.  An e4m3 code becomes the binary16 pattern of
 //    code * 2^-8 by moving its sign to bit 15 and its 7 exponent+fraction
@@ -28,24 +31,27 @@
 //  * Sources and outputs: the chunk kernel scores keys (fp16 or e4m3) or
 //    reads scores from a logits matrix, and either selects (top-k) or
 //    writes the scores out as logits (-inf past the visible blocks).
-//  * Scoring: each wave scores tiles of 16 keys with
-//    v_mfma_f32_16x16x32_f16: A = the 4 query heads (rows 4..15 zero),
-//    B = 16 keys.  Lane l loads key (l % 16), bytes [64c + 16(l/16), +16)
-//    for c = 0..3, so every load instruction reads 16 keys x 64 contiguous
-//    bytes.  The 4 head dots of key n land in lane n, so ReLU + head sum is
-//    lane-local.  Scores go to LDS as order-preserving uint32 keys (the
-//    sign-magnitude bit pattern turned into an unsigned order, -0 mapped
-//    onto +0), and the first radix histogram is counted as the scores
-//    arrive, under the memory latency.
-//  * Chunk top-k: an MSB-first radix select (digits of 11, 11 and 10 bits)
-//    finds the k-th largest key; it stops early once the bin holding the
-//    k-th key is taken whole.  When keys equal to that threshold are only
-//    partly in, a second radix select over the complemented block index of
-//    those keys finds the last block that is in, so the tie rule (smaller
-//    block first) is decided explicitly and survivors can be compacted in
-//    any order (one pass, wave ballots, one LDS atomic per batch).  A row
-//    that fits in one chunk is sorted, expanded and written right there
-//    (one launch does all the work).
+//  * Scoring: keys stream in with coalesced nontemporal buffer loads (one
+//    instruction = whole keys, 1 KiB contiguous) several 16-key tiles ahead,
+//    and pass through a per-wave LDS tile into the B operand of
+//    v_mfma_f32_16x16x32_f16; A = 4 heads of up to 4 rows (A row m = head
+//    m % 4 of row m / 4), so the 4 head dots of key n for row j land in
+//    lane n + 16j and ReLU + head sum is lane-local.  Scores go to LDS as
+//    order-preserving uint32 keys (the sign-magnitude bit pattern turned
+//    into an unsigned order, -0 mapped onto +0); for a single row the first
+//    radix histogram is counted as the scores arrive, under the memory
+//    latency.
+//  * Chunk top-k of a single row: an MSB-first radix select (digits of 11,
+//    11 and 10 bits) finds the k-th largest key; it stops early once the bin
+//    holding the k-th key is taken whole.  When keys equal to that threshold
+//    are only partly in, a second radix select over the complemented block
+//    index of those keys finds the last block that is in, so the tie rule
+//    (smaller block first) is decided explicitly and survivors can be
+//    compacted in any order (one pass, wave ballots, one LDS atomic per
+//    batch).  The rows of a group are selected one per wave, at the same
+//    time (a radix select over keys held in registers, no workgroup
+//    barriers).  A row that fits in one chunk is sorted, expanded and
+//    written right there (one launch does all the work).
 //  * Merge kernel, one workgroup per multi-chunk row: the chunks' candidate
 //    lists are staged through LDS in batches (behind the running best 512)
 //    and reduced with the same select.  The winners are bitonic-sorted in
