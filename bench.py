@@ -454,6 +454,12 @@ def main() -> int:
     sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
                                          key_bytes=132 if fp8 else 256)
     att_bytes = attn_algorithmic_bytes(got_idx)
+    # kernel launches of one timed step at these shapes (the committed kernel
+    # traces show one call of each per step)
+    kernels_per_step = (["qsa_metadata_kernel"] if meta else []) + (
+        ["qsa_select_chunk_kernel (paged logits)", "qsa_select_chunk_kernel (top-k per row)"]
+        if two_pass else ["qsa_select_chunk_kernel"]) + [
+        "qsa_select_merge_kernel", "qsa_attn_kernel", "qsa_attn_combine_kernel"]
     sel_avg_s = float(np.mean(sel_ms)) / 1e3
     att_avg_s = float(np.mean(att_ms)) / 1e3
     if two_pass:
@@ -502,6 +508,12 @@ def main() -> int:
                      "frac_of_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
                      "bytes_per_launch": roof_bytes, "avg_launch_ms": round(roof_s * 1e3, 4)},
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
+                   # per-step event times of the instrumented pass (K samples each)
+                   "select_ms_median": round(float(np.median(sel_ms)), 4),
+                   "select_ms_min": round(float(np.min(sel_ms)), 4),
+                   "attention_ms_median": round(float(np.median(att_ms)), 4),
+                   "attention_ms_min": round(float(np.min(att_ms)), 4),
+                   "kernels_per_step": kernels_per_step,
                    "attention_bytes": att_bytes,
                    "attention_gbs": round(att_bytes / att_avg_s / 1e9, 1),
                    "step_gbs": round(step_gbs, 1),

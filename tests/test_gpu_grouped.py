@@ -173,3 +173,35 @@ def test_multi_token_decode_step(multi_token):
     assert same.size > w.rows // 2
     want = orc().sparse_attn(w.q_attn[same], w.kv, want_idx[same], SCALE)
     check_attn(out[same], want, "grouped multi-token rows with identical selection")
+
+
+def test_runs_full_size_chunks_integer():
+    """A batch large enough for the grouped plan's full chunks (8 pages =
+    1024 blocks): 64 groups of 4 rows.  One prefill run crosses the chunk
+    boundary (V = 1023..1027), so a group mixes rows finished in the chunk
+    kernel with rows merged later; fp16 keys, e4m3 keys and per-head
+    weights, bit-exact."""
+    rng = np.random.default_rng(123)
+    rows_per_req = [16] + [4] * 60
+    lengths = [4108] + list(rng.integers(4000, 65536, size=59)) + [65536]
+    pages = sum(wl.pages_needed(L) for L in lengths) + 8
+    q, kcache, bt, t2r, sl, qp = request_rows(17, rows_per_req, lengths, pages, palette=5)
+    V = np.maximum(0, np.minimum((qp + 1) // 4, sl[t2r] // 4))
+    assert V[:16].min() <= 1024 < V[:16].max()
+    assert qsa.select_workspace_bytes(len(t2r), bt.shape[1]) > 0
+    want = orc().select(q, kcache, bt, t2r, sl, qp)
+    banner("select runs full-size chunks R=256")
+    assert_rows_equal(select_runs((q, kcache, bt, t2r, sl, qp), 4), want)
+    codes, scales = wl.fp8_integer_keys(rng, kcache)
+    banner("select_fp8 runs full-size chunks R=256")
+    got = qsa.qsa_select_fp8(runs(q, 4), dev_e4m3(codes), dev(scales), dev(bt), dev(t2r), dev(sl),
+                             dev(qp))
+    torch.cuda.synchronize()
+    assert_rows_equal(got.cpu().numpy(), want)
+    w = wl.head_weights(rng, q.shape[0], integer=True)
+    want_w = orc().select_weighted(q, w, bt, t2r, sl, qp, kcache=kcache)
+    banner("select_weighted runs full-size chunks R=256")
+    got = qsa.qsa_select_weighted(runs(q, 4), dev(w), dev(kcache), dev(bt), dev(t2r), dev(sl),
+                                  dev(qp))
+    torch.cuda.synchronize()
+    assert_rows_equal(got.cpu().numpy(), want_w)
