@@ -205,3 +205,25 @@ def test_runs_full_size_chunks_integer():
                                   dev(qp))
     torch.cuda.synchronize()
     assert_rows_equal(got.cpu().numpy(), want_w)
+
+
+def test_decode_step_deterministic(multi_token):
+    """The decode step (grouped queries, several chunks per row, split
+    attention) gives identical bytes on 100 repeated calls."""
+    w = multi_token
+    q, kcache, bt, t2r, sl, qp = w.select_inputs()
+    kvd = dev(w.kv)
+    k, v = qsa.kv_views(kvd)
+    args = [runs(q, 4), dev(kcache), dev(bt), dev(t2r), dev(sl), dev(qp), dev(w.q_attn), k, v]
+    idx = torch.empty((w.rows, 2051), dtype=torch.int32, device=kvd.device)
+    out = torch.empty((w.rows, 3, 256), dtype=torch.float16, device=kvd.device)
+    banner(f"decode determinism x100 {w.name}")
+    ref = None
+    for i in range(100):
+        idx.fill_(-7)
+        out.fill_(7)
+        qsa.qsa_decode_step(*args, SCALE, indices=idx, out=out)
+        got = (idx.cpu().numpy(), out.view(torch.int16).cpu().numpy())
+        if ref is None:
+            ref = got
+        assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), f"repeat {i} differs"
