@@ -1176,6 +1176,7 @@ struct MergeSmem {
   uint64_t sorted[kTopKBlocks];
   alignas(16) uint32_t hist0[kBins];
   alignas(16) uint32_t hist1[kBins];
+  uint32_t red_and[kMergeThreads / 64], red_or[kMergeThreads / 64];
   Scratch s;
 };
 
@@ -1205,13 +1206,19 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
     const int nb = min(kBatch, m - base);
     for (int i = tid; i < kBins; i += kMergeThreads) sm.hist0[i] = 0;
     __syncthreads();
-    // list = [running best] + [next batch]; the first radix histogram is
-    // counted on the way into LDS
+    // list = [running best] + [next batch], with the AND and OR of its keys:
+    // the candidates are the best keys of their chunks and share their
+    // leading bits, so the select runs on the keys shifted left past the
+    // bits they all share (same order, same ties; without the shift the
+    // first radix digit would put them in a few bins, and the histogram's
+    // LDS atomics would serialise)
+    uint32_t kand = 0xFFFFFFFFu, kor = 0;
     for (int i = tid; i < best_n; i += kMergeThreads) {
       const uint32_t x = sm.best_keys[i];
       sm.keys[i] = x;
       sm.blocks[i] = sm.best_blocks[i];
-      atomicAdd(&sm.hist0[digit0(x)], 1u);
+      kand &= x;
+      kor |= x;
     }
     // 16-byte loads, kLoadUnroll of them in flight per thread (the batch
     // start is a multiple of 4 candidates and the workspace is 256-aligned)
@@ -1240,7 +1247,8 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
           for (int e = 0; e < 4; ++e) {
             sm.keys[at + e] = xs[e];
             sm.blocks[at + e] = bs[e];
-            atomicAdd(&sm.hist0[digit0(xs[e])], 1u);
+            kand &= xs[e];
+            kor |= xs[e];
           }
         }
       }
@@ -1249,22 +1257,44 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
       const uint32_t x = ckeys[base + i];
       sm.keys[best_n + i] = x;
       sm.blocks[best_n + i] = cblocks[base + i];
-      atomicAdd(&sm.hist0[digit0(x)], 1u);
+      kand &= x;
+      kor |= x;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
+      kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
+    }
+    if ((tid & 63) == 0) {
+      sm.red_and[tid >> 6] = kand;
+      sm.red_or[tid >> 6] = kor;
     }
     __syncthreads();
+    uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
+#pragma unroll
+    for (int w = 0; w < kMergeThreads / 64; ++w) {
+      all_and &= sm.red_and[w];
+      all_or |= sm.red_or[w];
+    }
+    const uint32_t differ = all_and ^ all_or;
+    const int shift = differ ? __builtin_clz(differ) : 0;  // bits every key shares
     const int n_list = best_n + nb;
     const int kk = min(k, n_list);
-    uint32_t T = 0, bcut = 0xFFFFFFFFu;
-    auto lds_key = [&](int i) { return sm.keys[i]; };
+    auto lds_key = [&](int i) { return sm.keys[i] << shift; };
     auto block_of = [&](int i) { return sm.blocks[i]; };
+    if (n_list > kk) {
+      for (int i = tid; i < n_list; i += kMergeThreads) atomicAdd(&sm.hist0[digit0(lds_key(i))], 1u);
+      __syncthreads();
+    }
+    uint32_t T = 0, bcut = 0xFFFFFFFFu;
     if (n_list > kk) {
       topk_threshold<kMergeThreads>(lds_key, block_of, n_list, kk, sm.s, sm.hist0, sm.hist1, T,
                                     bcut);
     }
     compact_topk<kMergeThreads>(
         lds_key, block_of, n_list, T, bcut,
-        [&](uint32_t slot, int i, uint32_t x) {
-          sm.best_keys[slot] = x;
+        [&](uint32_t slot, int i, uint32_t) {
+          sm.best_keys[slot] = sm.keys[i];  // the key itself, not its shifted form
           sm.best_blocks[slot] = sm.blocks[i];
         },
         sm.s);
