@@ -1,0 +1,84 @@
+"""Seeded random sweep of selection configurations against the oracle,
+bit-exact on integer inputs: batch sizes, row lengths and table widths that
+pick every chunk size of both plans, shared physical pages, palettes that
+force exact ties, padded rows, queries passed row by row or as runs of n
+rows, fp16 or e4m3 keys, with or without per-head weights.  Each case is
+drawn from its own seed, so a failure names a reproducible configuration."""
+
+import numpy as np
+import pytest
+import torch
+
+from paged_top_indexer_amd import workloads as wl
+import paged_top_indexer_amd as qsa
+from gpu_util import banner, dev, dev_e4m3, orc
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+def random_case(seed: int):
+    rng = np.random.default_rng(1000 + seed)
+    n_req = int(rng.integers(1, 40))
+    run = int(rng.choice([1, 1, 2, 3, 4, 5, 8]))  # rows per request (and the runs hint)
+    long_tail = rng.random() < 0.5
+    hi = 131072 if long_tail else 20000
+    lengths = rng.integers(0, hi, size=n_req)
+    tiny = rng.random(n_req) < 0.1  # empty and shorter-than-a-block requests
+    lengths[tiny] = rng.integers(0, 8, size=int(tiny.sum()))
+    need = [wl.pages_needed(int(L)) for L in lengths]
+    width = max(need + [1]) + int(rng.integers(0, 3))
+    P = max(16, sum(need) // int(rng.choice([1, 2, 4])) + 4)  # pages may be shared by chance
+    palette = int(rng.choice([0, 3, 16]))
+    if palette:
+        pal = wl.int_f16(rng, -4, 4, (palette, 128))
+        kcache = pal[rng.integers(0, palette, size=(P, 128))].reshape(P, 128, 1, 128)
+    else:
+        kcache = wl.int_f16(rng, -4, 4, (P, 128, 1, 128))
+    bt = np.full((n_req, width), -1, dtype=np.int32)
+    for i, n in enumerate(need):
+        if n:
+            bt[i, :n] = rng.choice(P, size=n, replace=n > P)
+    t2r = np.repeat(np.arange(n_req, dtype=np.int32), run)
+    qp = np.concatenate([int(L) - run + np.arange(run) for L in lengths]).astype(np.int64)
+    pad = rng.random(t2r.size) < 0.05
+    qp[pad] = -1
+    q = wl.int_f16(rng, -2 if palette else -4, 2 if palette else 4, (t2r.size, 4, 128))
+    fp8 = rng.random() < 0.3
+    weights = wl.head_weights(rng, t2r.size, integer=True) if rng.random() < 0.3 else None
+    hint = run if rng.random() < 0.7 else 1
+    return dict(q=q, kcache=kcache, bt=bt, t2r=t2r, sl=lengths.astype(np.int32), qp=qp, fp8=fp8,
+                weights=weights, hint=hint, rng=rng, desc=f"seed={seed} reqs={n_req} run={run} "
+                f"hint={hint} W={width} P={P} palette={palette} fp8={fp8} weights={weights is not None}")
+
+
+@pytest.mark.parametrize("seed", range(CASES))
+def test_random_selection_bit_exact(seed):
+    c = random_case(seed)
+    q, kcache, bt, t2r, sl, qp = c["q"], c["kcache"], c["bt"], c["t2r"], c["sl"], c["qp"]
+    R = q.shape[0]
+    banner(f"random selection R={R} {c['desc']}")
+    if c["weights"] is not None:
+        want = orc().select_weighted(q, c["weights"], bt, t2r, sl, qp, kcache=kcache)
+    else:
+        want = orc().select(q, kcache, bt, t2r, sl, qp)
+    qd = dev(q)
+    if c["hint"] > 1:
+        qd = qd.view(R // c["hint"], c["hint"], 4, 128)
+    args = [dev(bt), dev(t2r), dev(sl), dev(qp)]
+    if c["fp8"]:
+        codes, scales = wl.fp8_integer_keys(c["rng"], kcache)
+        kc, ks = dev_e4m3(codes), dev(scales)
+    else:
+        kc, ks = dev(kcache), None
+    if c["weights"] is not None:
+        got = qsa.qsa_select_weighted(qd, dev(c["weights"]), kc, *args, kscale=ks)
+    elif c["fp8"]:
+        got = qsa.qsa_select_fp8(qd, kc, ks, *args)
+    else:
+        got = qsa.qsa_select(qd, kc, *args)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    bad = np.flatnonzero(~np.all(got == want, axis=1))
+    assert bad.size == 0, f"{c['desc']}: rows differ: {bad[:10]}"
