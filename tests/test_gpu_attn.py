@@ -131,3 +131,34 @@ def test_inputs_unchanged_and_fail_closed():
         qsa.qsa_sparse_attn(q.float(), k, v, idx, SCALE, out=out)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+# Batch sizes across the split plan: 33 splits of 64 positions for small
+# batches, fewer and longer splits as rows grow, one split per row (the
+# kernel writes the output itself, no combine) from 768 rows up.
+SPLIT_BATCHES = [1, 2, 5, 16, 33, 100, 300, 767, 768, 900]
+
+
+@pytest.mark.parametrize("rows", SPLIT_BATCHES)
+def test_split_plans(rows):
+    """Random index rows (valid widths from 0 to 2051, holes, repeats, a few
+    out-of-range entries treated as holes) over a 64-page cache."""
+    rng = np.random.default_rng(77 + rows)
+    pages = 64
+    kv = wl.normal_f16(rng, (pages, 512, 512))
+    q = wl.normal_f16(rng, (rows, 3, 256))
+    idx = np.full((rows, 2051), -1, dtype=np.int32)
+    widths = rng.integers(0, 2052, size=rows)
+    widths[rng.random(rows) < 0.3] = 2051
+    for r in range(rows):
+        idx[r, :widths[r]] = rng.integers(0, pages * 512, size=widths[r])
+    holes = rng.random(idx.shape) < 0.05
+    idx[holes] = -1
+    repeat = (rng.random(idx.shape) < 0.05) & (idx >= 0)
+    idx[repeat] = idx[repeat][::-1]  # repeats of other valid entries
+    oob = rng.random(idx.shape) < 0.002
+    idx[oob] = pages * 512 + 7  # past the cache: a hole
+    banner(f"attn split plan rows={rows} workspace={qsa.sparse_attn_workspace_bytes(rows)}")
+    got = attn_gpu(q, kv, idx, SCALE)
+    ref_idx = np.where(idx < pages * 512, idx, -1).astype(np.int32)
+    check_attn(got, orc().sparse_attn(q, kv, ref_idx, SCALE), f"rows={rows}")
