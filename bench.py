@@ -189,6 +189,40 @@ def r1_latencies(torch, qsa, wl, dev, calls: int = 64) -> dict:
     return out
 
 
+def batched_step(torch, qsa, wl, dev, steps: int = 20) -> dict:
+    """The batched configuration (64 rows, lengths uniform in [512, 32768],
+    requests 2i and 2i+1 sharing their first pages): mean decode-step time
+    and the selection stage's algorithmic rate; context only."""
+    w = wl.batched_shared(0)
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    sel = [d(a) for a in w.select_inputs()]
+    kvd = d(w.kv)
+    k, v = qsa.kv_views(kvd)
+    q = d(w.q_attn)
+    idx = torch.empty((w.rows, 2051), dtype=torch.int32, device=dev)
+    out = torch.empty((w.rows, 3, 256), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def mean_ms(fn):
+        for _ in range(5):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / steps
+
+    step = mean_ms(lambda: qsa.qsa_decode_step(*sel, q, k, v, wl.SOFTMAX_SCALE, indices=idx,
+                                               out=out))
+    select = mean_ms(lambda: qsa.qsa_select(*sel, out=idx))
+    sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req)
+    return {"workload": w.name, "rows": int(w.rows), "step_ms": round(step, 4),
+            "rows_per_s": round(w.rows / step * 1e3, 1), "select_ms": round(select, 4),
+            "select_algorithmic_gbs": round(sel_bytes / select / 1e6, 1)}
+
+
 def cpu_baseline(w, scale: float, fp8: bool = False, weights=None,
                  max_seconds: float = 20.0) -> dict:
     """The CPU oracle (single-threaded C, unmodified) on the host cores: the
@@ -477,6 +511,7 @@ def main() -> int:
     traffic = stored_traffic(w.name)
     ceiling = None if args.no_context else read_ceiling(torch, qsa, dev)
     context = None if args.no_context else r1_latencies(torch, qsa, wl, dev)
+    batched = None if args.no_context else batched_step(torch, qsa, wl, dev)
     if ceiling:
         log(f"read ceiling {ceiling:.0f} GB/s; single-row latencies {context}")
     rows_per_s = R / (ms_per_step / 1e3)
@@ -528,6 +563,7 @@ def main() -> int:
     }
     if context is not None:
         result["single_row_latency"] = context
+        result["batched_64_rows"] = batched
     if not args.no_cpu_baseline:
         base = cpu_baseline(w, scale, fp8=fp8, weights=head_w)
         outs = base.pop("_outs")
