@@ -553,6 +553,7 @@ def main() -> int:
                    "attention_gbs": round(att_bytes / att_avg_s / 1e9, 1),
                    "step_gbs": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "step_frac_of_ceiling": round(step_gbs / ceiling, 4) if ceiling else None,
                    "timed_entry_point": ("qsa_paged_logits + qsa_topk_per_row + qsa_sparse_attn"
                                          if two_pass else
                                          "qsa_build_metadata + qsa_decode_step" if meta else
