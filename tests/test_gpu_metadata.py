@@ -90,10 +90,15 @@ def test_builder_feeds_selection():
     d_q, d_kc, d_bt, d_sl = dev(w.q_sel), dev(w.kcache), dev(w.block_table), dev(w.seq_lens)
     m = qsa.qsa_build_metadata(dev(qsl), d_sl, d_bt, w.rows)
     idx = qsa.qsa_select(d_q, d_kc, d_bt, m["token_to_req"], d_sl, m["logical_positions"])
+    # the same rows passed as runs of 4 (the batch's requests own 4 or 16 rows)
+    idx4 = qsa.qsa_select(d_q.view(w.rows // 4, 4, 4, 128), d_kc, d_bt, m["token_to_req"], d_sl,
+                          m["logical_positions"])
     torch.cuda.synchronize()
     assert np.array_equal(m["token_to_req"].cpu().numpy(), w.token_to_req)
     assert np.array_equal(m["logical_positions"].cpu().numpy(), w.query_pos)
     V = np.array([orc().row_extent(int(w.seq_lens[w.token_to_req[r]]), int(w.query_pos[r]))[0]
                   for r in range(w.rows)])
     assert np.array_equal(m["visible_blocks"].cpu().numpy(), V)
-    assert np.array_equal(idx.cpu().numpy(), orc().select(*w.select_inputs()))
+    want = orc().select(*w.select_inputs())
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(idx4.cpu().numpy(), want)
