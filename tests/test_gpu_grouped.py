@@ -227,3 +227,25 @@ def test_decode_step_deterministic(multi_token):
         if ref is None:
             ref = got
         assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), f"repeat {i} differs"
+
+
+def test_multi_token_decode_step_fp8():
+    """qsa_decode_step_fp8 with grouped queries over the multi-token batch's
+    keys absmax-quantized to e4m3: selection within the band of the oracle's
+    e4m3 scores, attention on the rows whose selection is the oracle's."""
+    w = wl.with_fp8_keys(wl.multi_token_rows(0), integer=False)
+    inputs = w.select_inputs_fp8()
+    q, codes, scales, bt, t2r, sl, qp = inputs
+    kvd = dev(w.kv)
+    k, v = qsa.kv_views(kvd)
+    banner(f"decode_fp8 runs {w.name}")
+    idx, out = qsa.qsa_decode_step_fp8(runs(q, 4), dev_e4m3(codes), dev(scales), dev(bt), dev(t2r),
+                                       dev(sl), dev(qp), dev(w.q_attn), k, v, SCALE)
+    torch.cuda.synchronize()
+    idx, out = idx.cpu().numpy(), out.cpu().numpy()
+    want_idx = orc().select_fp8(*inputs)
+    check_select_band(idx, want_idx, orc(), inputs, range(w.rows))
+    same = np.flatnonzero(np.all(idx == want_idx, axis=1))
+    assert same.size > w.rows // 2
+    want = orc().sparse_attn(w.q_attn[same], w.kv, want_idx[same], SCALE)
+    check_attn(out[same], want, "grouped e4m3 multi-token rows with identical selection")
