@@ -205,6 +205,16 @@ def test_runs_full_size_chunks_integer():
                                   dev(qp))
     torch.cuda.synchronize()
     assert_rows_equal(got.cpu().numpy(), want_w)
+    banner("paged_logits runs full-size chunks R=256")
+    grouped = qsa.qsa_paged_logits(runs(q, 4), dev(kcache), dev(bt), dev(t2r), dev(sl), dev(qp),
+                                   weights=dev(w))
+    flat = qsa.qsa_paged_logits(dev(q), dev(kcache), dev(bt), dev(t2r), dev(sl), dev(qp),
+                                weights=dev(w))
+    torch.cuda.synchronize()
+    grouped = grouped.cpu().numpy()
+    assert np.array_equal(grouped, flat.cpu().numpy())
+    want_l = orc().paged_logits(q, w, bt, t2r, sl, qp, grouped.shape[1], kcache=kcache)
+    assert np.array_equal(grouped, want_l.astype(np.float32))
 
 
 def test_decode_step_deterministic(multi_token):
