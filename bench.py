@@ -223,21 +223,45 @@ def batched_step(torch, qsa, wl, dev, steps: int = 20) -> dict:
             "select_algorithmic_gbs": round(sel_bytes / select / 1e6, 1)}
 
 
+def host_cpu() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """The CPU threads this process may run on, at most 16 (the host share of
+    one GPU on a shared node, whatever the machine's own count)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def cpu_baseline(w, scale: float, fp8: bool = False, weights=None,
-                 max_seconds: float = 20.0) -> dict:
-    """The CPU oracle (single-threaded C, unmodified) on the host cores: the
-    whole decode step of the first rows of the same workload, until all rows
-    are done or max_seconds of work have been spent."""
+                 max_seconds: float = 20.0, threaded_seconds: float = 8.0) -> dict:
+    """The CPU oracle (plain C, unmodified) on the host cores: the whole decode
+    step of the first rows of the same workload, single-threaded until all
+    rows are done or max_seconds of work have been spent; then the same
+    per-row calls with the rows dealt to host_threads() threads (the C calls
+    release the interpreter lock and keep no shared state) for about
+    threaded_seconds, cycling over the rows."""
+    import itertools
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
 
     orc = oracle.default()
-    inputs = w.select_inputs()
-    done = 0
-    t0 = time.perf_counter()
-    outs = []
-    while done < w.rows and time.perf_counter() - t0 < max_seconds:
-        r = np.array([done])
-        q, kc, bt, t2r, sl, qp = inputs
+    q, kc, bt, t2r, sl, qp = w.select_inputs()
+
+    def one_row(i: int):
+        r = np.array([i])
         if fp8:
             sel = orc.select_fp8(q[r], w.kcodes, w.kscale, bt, t2r[r], sl, qp[r])
         elif weights is not None:
@@ -246,13 +270,60 @@ def cpu_baseline(w, scale: float, fp8: bool = False, weights=None,
             sel = orc.topk_per_row(lg, t2r[r], sl, qp[r])
         else:
             sel = orc.select(q[r], kc, bt, t2r[r], sl, qp[r])
-        att = orc.sparse_attn(w.q_attn[r], w.kv, sel, scale)
-        outs.append((sel, att))
+        return sel, orc.sparse_attn(w.q_attn[r], w.kv, sel, scale)
+
+    done = 0
+    t0 = time.perf_counter()
+    outs = []
+    while done < w.rows and time.perf_counter() - t0 < max_seconds:
+        outs.append(one_row(done))
         done += 1
     dt = time.perf_counter() - t0
+
+    threads = host_threads()
+    ticket = itertools.count()  # next() on a count is atomic under the interpreter lock
+    t1 = time.perf_counter()
+    stop = t1 + threaded_seconds
+
+    def worker(_):
+        n = 0
+        while time.perf_counter() < stop:
+            one_row(next(ticket) % w.rows)
+            n += 1
+        return n
+
+    with ThreadPoolExecutor(threads) as ex:
+        done_t = sum(ex.map(worker, range(threads)))
+    dt_t = time.perf_counter() - t1
     return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {w.rows} rows of the same workload, select + attention "
-                      f"per row, {dt:.1f} s single-threaded", "_outs": outs}
+                      f"per row, {dt:.1f} s single-threaded",
+            "host_cpu": host_cpu(), "host_threads": threads,
+            "threaded": {"value": done_t / dt_t, "unit": "rows/s", "cores": threads,
+                         "sample": f"{done_t} rows (row i mod {w.rows}) dealt to {threads} "
+                                   f"threads, {dt_t:.1f} s"},
+            "_outs": outs}
+
+
+def gpu_clocks():
+    """GPU clocks and power as rocm-smi reports them right after the timed
+    region (None if it cannot be read); the bench does not pin clocks."""
+    import subprocess
+
+    try:
+        p = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        rec = json.loads(p.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    if not isinstance(rec, dict):
+        return None
+    keep = {}
+    for card, fields in rec.items():
+        if isinstance(fields, dict):
+            keep[card] = {k: v for k, v in fields.items()
+                          if any(t in k.lower() for t in ("sclk", "mclk", "fclk", "power"))}
+    return keep or None
 
 
 def workload_config(w, kv_copies: int) -> dict:
@@ -425,6 +496,7 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = t_ev[0].elapsed_time(t_ev[1]) / args.steps
+    clocks = None if args.no_context else gpu_clocks()
 
     # Per-stage times for the roofline: the same two stages through their own
     # entry points, with events recorded on the launch stream around each.
@@ -565,6 +637,7 @@ def main() -> int:
     if context is not None:
         result["single_row_latency"] = context
         result["batched_64_rows"] = batched
+        result["gpu_clocks_after_timing"] = clocks
     if not args.no_cpu_baseline:
         base = cpu_baseline(w, scale, fp8=fp8, weights=head_w)
         outs = base.pop("_outs")
@@ -575,7 +648,8 @@ def main() -> int:
         result["cpu_baseline"] = base
         result["parity"] = {"rows_checked": len(outs), "selection_identical": int(same),
                             "attention_max_abs_err": max(errs) if errs else None}
-        log(f"oracle: {base['value']:.2f} rows/s; identical selections {same}/{len(outs)}")
+        log(f"oracle: {base['value']:.2f} rows/s, {base['threaded']['value']:.2f} rows/s on "
+            f"{base['host_threads']} threads; identical selections {same}/{len(outs)}")
     print(json.dumps(result), flush=True)
     return 0
 

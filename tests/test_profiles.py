@@ -1,0 +1,64 @@
+"""The committed rocprofv3 summaries agree with the code they describe: the
+stored HBM counters were taken on the current kernel sources (otherwise the
+bench reports no traffic), and every kernel trace shows one dispatch of each
+kernel per selection and per decode step."""
+
+import json
+import os
+import re
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+WORKLOADS = ["long_context_R128_L131072", "long_context_R128_L131072_fp8",
+             "long_context_R128_L131072_two_pass", "multi_token_R256_next4_prefill16",
+             "multi_token_R256_next4_prefill16_metadata"]
+
+
+def trace_calls(workload: str) -> tuple[dict, int]:
+    """Kernel name -> calls from the summary table, and the number of steps
+    the run made (the sum of the counts in its 'Calls = ...' line)."""
+    with open(os.path.join(PROFILES, f"kernel_trace_decode_step_{workload}.md")) as f:
+        text = f.read()
+    calls = {}
+    for m in re.finditer(r"^\| (qsa\S.*?) \| (\d+) \|", text, re.M):
+        calls[m.group(1)] = int(m.group(2))
+    protocol = re.search(r"Calls = (\d+) warm-up \+ (\d+) timed .*? \+ (\d+) instrumented "
+                         r"steps .*?\+ (\d+) parity step", text, re.S)
+    assert protocol, f"{workload}: no call protocol line"
+    return calls, sum(int(g) for g in protocol.groups())
+
+
+@pytest.mark.parametrize("workload", WORKLOADS)
+def test_counters_taken_on_current_sources(workload):
+    with open(os.path.join(PROFILES, f"select_{workload}_counters.json")) as f:
+        rec = json.load(f)
+    assert rec["workload"] == workload
+    assert rec["source_hash"] == bench.kernel_source_hash(), \
+        "kernel sources changed since the counters were taken: profile again"
+    assert bench.stored_traffic(workload) == rec["hbm_bytes_per_launch"] > 0
+
+
+@pytest.mark.parametrize("workload", WORKLOADS)
+def test_one_dispatch_per_step(workload):
+    calls, steps = trace_calls(workload)
+    assert calls["qsa_attn_kernel"] == calls["qsa_attn_combine_kernel"] == steps
+    chunk = {k: v for k, v in calls.items() if k.startswith("qsa_select_chunk_kernel<")}
+    # a selection is one chunk launch and one merge launch; the paged-logits
+    # form (second template argument true) writes the matrix and has no merge
+    selecting = sum(v for k, v in chunk.items() if k.split(",")[1].strip() == "false")
+    assert calls["qsa_select_merge_kernel"] == selecting
+    if workload.endswith("_two_pass"):
+        assert chunk["qsa_select_chunk_kernel<0, true, 1>"] == steps
+        assert chunk["qsa_select_chunk_kernel<2, false, 1>"] == steps
+    elif workload.endswith("_metadata"):
+        builder = [v for k, v in calls.items() if "qsa_metadata_kernel" in k]
+        assert builder and builder[0] >= steps
+        assert sum(chunk.values()) == steps
+    else:
+        # the timed instantiation runs once per step (the multi-token run adds
+        # a row-by-row comparison through the one-row instantiation)
+        assert steps in chunk.values()
