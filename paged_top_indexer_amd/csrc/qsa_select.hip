@@ -20,12 +20,10 @@
 //    Workgroups whose chunk lies past every row's visible blocks exit at
 //    once.
 //  * Key caches: fp16 keys (256 B each), or e4m3 codes (128 B each) with one
-//    fp32 scale per key.  An e4m3 code becomes the binary16 pattern of
-//    code * 2^-8 by moving its sign to bit 15 and its 7 exponent+fraction
-//    bits to bits 7..13 (the biases 7 and 15 differ by 8; subnormals map
-//    onto subnormals), so the same fp16 MFMA scores both; the factor 2^8 is
-//    folded into the key's scale, which multiplies the head sum (a scale is
-//    >= 0, so scale * sum ReLU(q.k) = sum ReLU(q.(scale k))).
+//    fp32 scale per key.  e4m3 codes are decoded to their exact binary16
+//    values by the hardware conversion, so the same fp16 MFMA scores both;
+//    the key's scale multiplies the head sum (a scale is >= 0, so
+//    scale * sum ReLU(q.k) = sum ReLU(q.(scale k))).
 //  * Per-head weights (optional, fp32 per row and head) multiply each
 //    head's ReLU term; weighted scores may be negative.
 //  * Sources and outputs: the chunk kernel scores keys (fp16 or e4m3) or
@@ -818,19 +816,20 @@ __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem
   }
 }
 
-// Two e4m3 codes (bytes 0,1 of w when hi is false, bytes 2,3 when true) as
-// two binary16 patterns of code * 2^-8.
-__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w, bool hi) {
-  // z: first code in byte 1, second code in byte 3
-  const uint32_t z = hi ? (((w >> 8) & 0x0000FF00u) | (w & 0xFF000000u))
-                        : (((w & 0x000000FFu) << 8) | ((w & 0x0000FF00u) << 16));
-  return (z & 0x80008000u) | ((z >> 1) & 0x3F803F80u);
-}
-
+// Eight e4m3 codes (the bytes of w0 then w1, in order) as binary16.  Every
+// finite e4m3 value is exact in binary16, and gfx950's
+// v_cvt_scalef32_pk_f16_fp8 decodes the OCP e4m3 format two codes at a time
+// (word select 0: bytes 0,1; 1: bytes 2,3); with scale 1.0 it is the plain
+// conversion.  One instruction per two codes: decoding by integer shifts and
+// masks took ~6 vector instructions per pair and made the scorer partly
+// ALU-bound.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
-  u32x4 h = {e4m3x2_to_f16x2(w0, false), e4m3x2_to_f16x2(w0, true), e4m3x2_to_f16x2(w1, false),
-             e4m3x2_to_f16x2(w1, true)};
-  return __builtin_bit_cast(half8, h);
+  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // e4m3 keys.  The dot product does not care in which order the k steps
@@ -951,8 +950,8 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
       const float scale = __builtin_bit_cast(
           float, __builtin_amdgcn_ds_bpermute(4 * (16 * (u % 4) + n),
                                               __builtin_bit_cast(int, scale_cur[u / 4])));
-      // scale * 2^8 is exact, so this is one rounding of scale * code-sum
-      const float sc = sum * (scale * 256.f);
+      // one rounding of scale * code-sum
+      const float sc = sum * scale;
       if (16 * tt + n < row_nblk) sink(g, 16 * tt + n, sc);
     }
     scale_cur[0] = scale_next[0];

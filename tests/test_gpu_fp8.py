@@ -128,3 +128,43 @@ def test_fail_closed_through_binding():
         qsa.qsa_select(q, codes8, bt, t2r, sl, qp, out=out)
     torch.cuda.synchronize()
     assert torch.all(out == 77)
+
+
+def e4m3_value(c: int) -> float:
+    """The value of an OCP e4m3 code from its bit fields: sign bit 7,
+    exponent bits 6..3 with bias 7, fraction bits 2..0; exponent 0 is
+    subnormal (fraction/8 * 2^-6)."""
+    sign = -1.0 if c & 0x80 else 1.0
+    e, m = (c >> 3) & 0xF, c & 7
+    return sign * (m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+
+
+def test_every_code_logits():
+    """Sign and magnitude of every finite code, read back as scores: key i
+    holds code c_i at dim 7 with scale 2^j; head 0 = +1 and head 1 = -1/2 on
+    dim 7, so the key scores 2^j * v for v = e4m3(c_i) >= 0 and
+    2^j * |v| / 2 for v < 0, exactly (a sign error or a wrong exponent bias
+    changes the value)."""
+    rng = np.random.default_rng(5)
+    codes_all = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    n = 2 * codes_all.size
+    pages = -(-n // 128)
+    codes = np.zeros((pages, 128, 1, 128), np.uint8)
+    b = np.arange(n)
+    per_key = np.concatenate([codes_all, rng.permutation(codes_all)])
+    codes[b // 128, b % 128, 0, 7] = per_key
+    exps = rng.integers(-6, 7, size=(pages, 128))
+    scales = np.ldexp(np.float32(1), exps).astype(np.float32)
+    q = np.zeros((1, 4, 128), np.float16)
+    q[0, 0, 7], q[0, 1, 7] = 1.0, -0.5
+    bt = np.arange(pages, dtype=np.int32).reshape(1, pages)
+    t2r, sl, qp = wl.decode_rows([4 * n + 1])
+    banner("paged_logits e4m3 every code, signed")
+    lg = qsa.qsa_paged_logits(dev(q), dev_e4m3(codes), dev(bt), dev(t2r), dev(sl), dev(qp),
+                              kscale=dev(scales))
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy()[0]
+    v = np.array([e4m3_value(int(c)) for c in per_key])
+    want = np.where(v >= 0, v, -v / 2) * np.ldexp(1.0, exps.reshape(-1)[:n])
+    assert np.array_equal(lg[:n], want.astype(np.float32))
+    assert np.all(np.isneginf(lg[n:]))
