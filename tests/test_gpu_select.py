@@ -69,6 +69,21 @@ def test_integer_plans_bit_exact(rows, width, lengths, palette):
     assert bad.size == 0, f"rows differ: {bad[:10]}"
 
 
+@pytest.mark.parametrize("palette", [None, 3], ids=["int4", "palette3"])
+def test_very_long_rows_bit_exact(palette):
+    """Rows of 2^20 and 1000003 tokens (262144 and 250000 blocks, 2048 table
+    entries): two rows get 4-page chunks, 512 per row, so each row's merge
+    takes up to 262144 candidates in 32 batches; with a 3-key palette almost
+    every score ties and block order decides."""
+    lengths = [1 << 20, 1000003]
+    inputs = integer_inputs(77 if palette is None else 78, lengths, 2048, 2048, palette=palette,
+                            q_range=4 if palette is None else 1)
+    banner(f"select very long rows L={lengths} palette={palette}")
+    got = select_gpu(*inputs)
+    want = orc().select(*inputs)
+    assert np.array_equal(got, want)
+
+
 def test_multirow_requests_and_padding():
     """Several query rows of one request (prefill-style positions), a padded
     row (position -1), an out-of-range request id (treated as empty)."""

@@ -18,9 +18,10 @@ WORKLOADS = ["long_context_R128_L131072", "long_context_R128_L131072_fp8",
              "multi_token_R256_next4_prefill16_metadata"]
 
 
-def trace_calls(workload: str) -> tuple[dict, int]:
-    """Kernel name -> calls from the summary table, and the number of steps
-    the run made (the sum of the counts in its 'Calls = ...' line)."""
+def trace_calls(workload: str) -> tuple[dict, int, int]:
+    """Kernel name -> calls from the summary table, the number of steps the
+    run made (the sum of the counts in its 'Calls = ...' line) and the number
+    of back-to-back roofline calls after them."""
     with open(os.path.join(PROFILES, f"kernel_trace_decode_step_{workload}.md")) as f:
         text = f.read()
     calls = {}
@@ -29,7 +30,9 @@ def trace_calls(workload: str) -> tuple[dict, int]:
     protocol = re.search(r"Calls = (\d+) warm-up \+ (\d+) timed .*? \+ (\d+) instrumented "
                          r"steps .*?\+ (\d+) parity step", text, re.S)
     assert protocol, f"{workload}: no call protocol line"
-    return calls, sum(int(g) for g in protocol.groups())
+    roof = re.search(r"plus (\d+) back-to-back roofline calls", text)
+    assert roof, f"{workload}: no roofline calls in the protocol line"
+    return calls, sum(int(g) for g in protocol.groups()), int(roof.group(1))
 
 
 @pytest.mark.parametrize("workload", WORKLOADS)
@@ -44,7 +47,7 @@ def test_counters_taken_on_current_sources(workload):
 
 @pytest.mark.parametrize("workload", WORKLOADS)
 def test_one_dispatch_per_step(workload):
-    calls, steps = trace_calls(workload)
+    calls, steps, roof = trace_calls(workload)
     assert calls["qsa_attn_kernel"] == calls["qsa_attn_combine_kernel"] == steps
     chunk = {k: v for k, v in calls.items() if k.startswith("qsa_select_chunk_kernel<")}
     # a selection is one chunk launch and one merge launch; the paged-logits
@@ -52,13 +55,14 @@ def test_one_dispatch_per_step(workload):
     selecting = sum(v for k, v in chunk.items() if k.split(",")[1].strip() == "false")
     assert calls["qsa_select_merge_kernel"] == selecting
     if workload.endswith("_two_pass"):
-        assert chunk["qsa_select_chunk_kernel<0, true, 1>"] == steps
+        assert chunk["qsa_select_chunk_kernel<0, true, 1>"] == steps + roof
         assert chunk["qsa_select_chunk_kernel<2, false, 1>"] == steps
     elif workload.endswith("_metadata"):
         builder = [v for k, v in calls.items() if "qsa_metadata_kernel" in k]
         assert builder and builder[0] >= steps
-        assert sum(chunk.values()) == steps
+        assert sum(chunk.values()) == steps + roof
     else:
-        # the timed instantiation runs once per step (the multi-token run adds
-        # a row-by-row comparison through the one-row instantiation)
-        assert steps in chunk.values()
+        # the timed instantiation runs once per step and per roofline call
+        # (the multi-token run adds a row-by-row comparison through the
+        # one-row instantiation)
+        assert steps + roof in chunk.values()
