@@ -155,7 +155,10 @@ def r1_latencies(torch, qsa, wl, dev, calls: int = 64) -> dict:
     """Mean single-row latencies of the pages' own cases (their figures are
     for an Intel XPU; context only): selection of the 519-token row (129
     blocks) and of the saturated 9215-token row (2303 blocks), and
-    attention over the saturated row's 2051 indices."""
+    attention over the saturated row's 2051 indices.  `*_ms`: calls back to
+    back from Python (host marshalling and launch included); `graph_*_ms`:
+    the same calls captured once in a HIP graph and replayed (device time
+    per call; the replayed outputs are checked against the eager ones)."""
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     stream = torch.cuda.current_stream(dev)
 
@@ -170,20 +173,51 @@ def r1_latencies(torch, qsa, wl, dev, calls: int = 64) -> dict:
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / calls
 
+    def graph_ms(fn, result):
+        fn()
+        torch.cuda.synchronize()
+        eager = result.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        result.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(result, eager), "graph replay differs from the eager call"
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / calls
+
     out = {}
-    tiny = [d(a) for a in wl.tiny_integer(0).select_inputs()]
+    tiny_w = wl.tiny_integer(0)
+    tiny = [d(a) for a in tiny_w.select_inputs()]
     idx1 = torch.empty((1, 2051), dtype=torch.int32, device=dev)
-    out["select_519_tokens_ms"] = round(mean_ms(lambda: qsa.qsa_select(*tiny, out=idx1)), 5)
+    ws_t = torch.zeros(max(1, qsa.select_workspace_bytes(1, tiny_w.block_table.shape[1])),
+                       dtype=torch.uint8, device=dev)
+    sel_tiny = lambda: qsa.qsa_select(*tiny, out=idx1, workspace=ws_t)  # noqa: E731
+    out["select_519_tokens_ms"] = round(mean_ms(sel_tiny), 5)
+    out["graph_select_519_tokens_ms"] = round(graph_ms(sel_tiny, idx1), 5)
     sat = wl.saturated_row(0)
     satd = [d(a) for a in sat.select_inputs()]
-    out["select_2303_blocks_ms"] = round(mean_ms(lambda: qsa.qsa_select(*satd, out=idx1)), 5)
+    ws_s = torch.zeros(max(1, qsa.select_workspace_bytes(1, sat.block_table.shape[1])),
+                       dtype=torch.uint8, device=dev)
+    sel_sat = lambda: qsa.qsa_select(*satd, out=idx1, workspace=ws_s)  # noqa: E731
+    out["select_2303_blocks_ms"] = round(mean_ms(sel_sat), 5)
+    out["graph_select_2303_blocks_ms"] = round(graph_ms(sel_sat, idx1), 5)
     kvd = d(sat.kv)
     k, v = qsa.kv_views(kvd)
     q = d(sat.q_attn)
-    qsa.qsa_select(*satd, out=idx1)
+    sel_sat()
     o = torch.empty((1, 3, 256), dtype=torch.float16, device=dev)
-    out["attention_width_2051_ms"] = round(
-        mean_ms(lambda: qsa.qsa_sparse_attn(q, k, v, idx1, wl.SOFTMAX_SCALE, out=o)), 5)
+    ws_a = torch.zeros(max(1, qsa.sparse_attn_workspace_bytes(1)), dtype=torch.uint8, device=dev)
+    attn = lambda: qsa.qsa_sparse_attn(q, k, v, idx1, wl.SOFTMAX_SCALE, out=o,  # noqa: E731
+                                       workspace=ws_a)
+    out["attention_width_2051_ms"] = round(mean_ms(attn), 5)
+    out["graph_attention_width_2051_ms"] = round(graph_ms(attn, o), 5)
     out["pages_intel_xpu_ms"] = {"select_519_tokens": 0.053155, "select_2303_blocks": 0.319464,
                                  "attention_width_2051": 0.710274}
     return out

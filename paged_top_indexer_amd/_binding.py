@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import struct
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,15 +29,23 @@ class QsaTensor(ctypes.Structure):
                 ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
 
 
+# qsa_tensor's bytes: data, dtype, ndim, shape[4], stride[4] (packed in one
+# call: filling the ctypes fields one by one costs several us per call)
+_DESC = struct.Struct("<Qii4q4q")
+assert _DESC.size == ctypes.sizeof(QsaTensor)
+_PAD = ((), (0,), (0, 0), (0, 0, 0), (0, 0, 0, 0))
+
+
 def descriptor(data_ptr: int, dtype: int, shape, stride) -> QsaTensor:
-    t = QsaTensor()
-    t.data = ctypes.c_void_p(int(data_ptr))
-    t.dtype = int(dtype)
-    t.ndim = len(shape)
-    for i, (s, st) in enumerate(zip(shape, stride)):
-        t.shape[i] = int(s)
-        t.stride[i] = int(st)
-    return t
+    """A qsa_tensor; more than 4 dims keep ndim (the library rejects them)
+    with the first 4 extents and strides."""
+    n = len(shape)
+    if n <= 4:
+        pad = _PAD[4 - n]
+        raw = _DESC.pack(data_ptr, dtype, n, *shape, *pad, *stride, *pad)
+    else:
+        raw = _DESC.pack(data_ptr, dtype, n, *shape[:4], *stride[:4])
+    return QsaTensor.from_buffer_copy(raw)
 
 
 _lib = None
@@ -128,17 +137,21 @@ def _torch():
     return torch
 
 
+_CODES: dict = {}
+
+
 def _dtype_code(t) -> int:
-    torch = _torch()
-    codes = {torch.float16: F16, torch.int32: I32, torch.int64: I64, torch.float32: F32,
-             torch.float8_e4m3fn: E4M3}
-    return codes.get(t.dtype, 0)
+    if not _CODES:
+        torch = _torch()
+        _CODES.update({torch.float16: F16, torch.int32: I32, torch.int64: I64,
+                       torch.float32: F32, torch.float8_e4m3fn: E4M3})
+    return _CODES.get(t.dtype, 0)
 
 
 def tensor_desc(t) -> QsaTensor:
     """Descriptor of a torch tensor (the element pointer includes the storage
     offset).  Unsupported dtypes get code 0, which the library rejects."""
-    return descriptor(t.data_ptr(), _dtype_code(t), tuple(t.shape), tuple(t.stride()))
+    return descriptor(t.data_ptr(), _dtype_code(t), t.shape, t.stride())
 
 
 def kv_views(kv):

@@ -48,7 +48,8 @@ constexpr int max_chunk_pages(int group) { return group <= 1 ? 32 : 8; }
 // then takes each multi-chunk row's candidates to the final top-512.
 struct SelectPlan {
   int group = 1;               // query rows per chunk workgroup (1..4)
-  int chunk_pages = 1;         // pages per chunk (1, 2, 4, 8, 16 or 32)
+  int chunk_pages = 1;         // pages per chunk (1, 2, 4, 8, 16 or 32; or the
+                               // whole table when it has at most 4 pages)
   int64_t chunks_per_row = 1;  // grid columns per row (ceil(W / chunk_pages))
   int64_t cand_cap = 0;        // candidate slots per chunk: min(512, 128*chunk_pages)
   size_t keys_off = 0;         // byte offsets inside the workspace

@@ -40,8 +40,11 @@ def test_constants_and_status_strings():
 def test_workspace_sizes():
     assert B.select_workspace_bytes(0, 256) == 0
     assert B.sparse_attn_workspace_bytes(0) == 0
-    # one chunk per row needs no workspace
+    # one chunk per row needs no workspace: a table of at most 4 pages (512
+    # blocks, no top-k) is one chunk whatever the batch
     assert B.select_workspace_bytes(1, 1) == 0
+    assert B.select_workspace_bytes(1, 4) == 0 and B.select_workspace_bytes(4096, 3) == 0
+    assert B.select_workspace_bytes(1, 5) > 0
     big = B.select_workspace_bytes(128, 256)
     # 32-page chunks: 8 chunks per row, 512 candidates (key + block) each
     assert big >= 128 * 8 * 512 * 8
@@ -118,6 +121,16 @@ def call_attn(a, ws, ws_bytes, scale=0.0625):
                                ctypes.byref(a["out"]), ctypes.c_void_p(ws), ws_bytes, None)
 
 
+def test_descriptor_bytes():
+    """The packed descriptor matches qsa_tensor field by field; more than 4
+    dims keep ndim with the first 4 extents (the library rejects them)."""
+    d = B.descriptor(0x1234560, B.I64, (3, 5), (5, 1))
+    assert (d.data, d.dtype, d.ndim) == (0x1234560, B.I64, 2)
+    assert list(d.shape) == [3, 5, 0, 0] and list(d.stride) == [5, 1, 0, 0]
+    d5 = B.descriptor(256, B.F16, (1, 2, 3, 4, 5), (120, 60, 20, 5, 1))
+    assert d5.ndim == 5 and list(d5.shape) == [1, 2, 3, 4] and list(d5.stride) == [120, 60, 20, 5]
+
+
 def test_select_zero_rows_is_noop():
     f, a, ws, wsb = select_args(R=0)
     assert call_select(a, 0, 0) == OK
@@ -127,6 +140,7 @@ SELECT_CASES = {
     "q_dtype": (lambda f, a: a.__setitem__("q", mk(f, 0, (4, 4, 128), 4)), DTYPE),
     "q_heads": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 3, 128), 2)), SHAPE),
     "q_rank": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 512), 2)), SHAPE),
+    "q_rank5": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (1, 2, 2, 4, 128), 2)), SHAPE),
     "q_strided": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 4, 128), 2, stride=(1024, 256, 1))), LAYOUT),
     "q_misaligned": (lambda f, a: a.__setitem__("q", mk(f, B.F16, (4, 4, 128), 2, ptr=f.alloc(8192) + 2)), LAYOUT),
     "kcache_bf16": (lambda f, a: a.__setitem__("kcache", mk(f, 0, (8, 128, 1, 128), 2)), DTYPE),

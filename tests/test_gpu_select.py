@@ -41,10 +41,12 @@ def test_ties_and_edges_bit_exact():
     assert np.array_equal(got, want)
 
 
-# Plans: (rows, table width) pick the chunk size (1..16 pages); these cover
-# chunks below and above 512 blocks, one-chunk rows, and multi-chunk merges
-# with ragged last chunks.
+# Plans: (rows, table width) pick the chunk size (1..16 pages, or the whole
+# table up to 4 pages); these cover chunks below and above 512 blocks,
+# one-chunk rows, and multi-chunk merges with ragged last chunks.
 PLAN_CASES = [
+    (5, 4, [0, 1, 515, 2048, 2047]),  # tables of <= 4 pages: one chunk per row
+    (3, 3, [1536, 9, 1100]),
     (1, 20, [9215]),
     (3, 40, [0, 20000, 517]),
     (8, 64, [1, 2, 3, 512, 515, 516, 2049, 32768]),
