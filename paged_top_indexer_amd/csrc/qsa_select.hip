@@ -991,8 +991,14 @@ enum : int { kSrcF16 = 0, kSrcE4M3 = 1, kSrcLogits = 2 };
 // 1 when p.group is 1, else kMaxGroup); rows of the group that share a
 // request are scored in one pass over its keys (a group that spans several
 // requests takes one pass per request).
+//
+// Compiled for 4 waves per SIMD (128 VGPRs; the 40 KiB of LDS allow 4
+// workgroups per CU), except the e4m3 scorer over groups of rows: 4 rows x
+// 4 heads of queries plus a page of codes in flight need ~148 VGPRs, so it
+// runs at 3 waves per SIMD rather than spill to scratch.
 template <int kSrc, bool kLogitsOut, int kGroup>
-__global__ __launch_bounds__(kChunkThreads, 4) void qsa_select_chunk_kernel(SelectParams p) {
+__global__ __launch_bounds__(kChunkThreads, (kSrc == kSrcE4M3 && kGroup > 1) ? 3 : 4) void
+qsa_select_chunk_kernel(SelectParams p) {
   __shared__ ChunkSmem sm;
   const int tid = threadIdx.x;
   const RowCol id = row_col_of_block(blockIdx.x, p.chunks_per_row);  // XCD-aware placement
