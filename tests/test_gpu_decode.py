@@ -78,3 +78,41 @@ def test_multi_token_rows():
     assert same.size > w.rows // 2
     want = orc().sparse_attn(w.q_attn[same], w.kv, want_idx[same], SCALE)
     check_attn(out[same], want, "multi-token rows with identical selection")
+
+
+@pytest.mark.parametrize("rows,lo,hi", [(4096, 0, 1500), (800, 4000, 12000)],
+                         ids=["R4096_short", "R800_mid"])
+def test_large_batches(rows, lo, hi):
+    """Large batches: 4096 short rows (tables of <= 3 pages: one chunk per
+    row, no merge) and 800 rows of 4000-12000 tokens (16-page chunks, so the
+    rows past 8192 tokens take two and a merge; attention at one split per
+    row, no combine).  Integer keys and queries over a shared 2048-page
+    cache: the selection bit-exact on every row; the decode step's attention
+    against the oracle on sampled rows."""
+    rng = np.random.default_rng(rows + lo)
+    lengths = rng.integers(lo, hi + 1, size=rows)
+    width = max(wl.pages_needed(int(L)) for L in lengths)
+    P = 2048
+    # integers in [-4, 4] drawn as int8 (a fraction of the int64 draw's time)
+    kcache = rng.integers(-4, 5, size=(P, 128, 1, 128), dtype=np.int8).astype(np.float16)
+    bt = wl.block_table_per_row(rng, lengths, P, width=width)
+    q = wl.int_f16(rng, -4, 4, (rows, 4, 128))
+    t2r, sl, qp = wl.decode_rows(lengths)
+    kv_pages = -(-int(lengths.max()) // 512) + 1
+    kv = wl.normal_f16(rng, (kv_pages, 512, 512))
+    q_attn = wl.normal_f16(rng, (rows, 3, 256))
+    assert width <= 4 if hi <= 1500 else qsa.select_workspace_bytes(rows, width) > 0
+    banner(f"decode large batch R={rows} L=[{lo},{hi}] W={width} "
+           f"select ws={qsa.select_workspace_bytes(rows, width)} "
+           f"attn ws={qsa.sparse_attn_workspace_bytes(rows)}")
+    k, v = qsa.kv_views(dev(kv))
+    idx, out = qsa.qsa_decode_step(dev(q), dev(kcache), dev(bt), dev(t2r), dev(sl), dev(qp),
+                                   dev(q_attn), k, v, SCALE)
+    torch.cuda.synchronize()
+    got, out = idx.cpu().numpy(), out.cpu().numpy()
+    want = orc().select(q, kcache, bt, t2r, sl, qp)
+    bad = np.flatnonzero(~np.all(got == want, axis=1))
+    assert bad.size == 0, f"rows differ: {bad[:10]}"
+    rows_s = sorted(set(rng.choice(rows, size=12, replace=False).tolist()) | {0, rows - 1})
+    check_attn(out[rows_s], orc().sparse_attn(q_attn[rows_s], kv, want[rows_s], SCALE),
+               "large batch")
