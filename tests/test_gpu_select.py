@@ -6,7 +6,8 @@ import torch
 
 from paged_top_indexer_amd import workloads as wl
 import paged_top_indexer_amd as qsa
-from gpu_util import (banner, check_select_band, dev, orc, select_gpu, subset_rows)
+from gpu_util import (banner, check_select_band, dev, orc, select_gpu, select_gpu_fp8,
+                      subset_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +85,36 @@ def test_very_long_rows_bit_exact(palette):
     got = select_gpu(*inputs)
     want = orc().select(*inputs)
     assert np.array_equal(got, want)
+
+
+def test_invalid_page_ids_read_as_zero_keys():
+    """Table entries outside [0, P) for visible blocks (an unmet device-side
+    precondition): the kernels stay in bounds and read such a page as
+    all-zero keys (score 0), so the result equals the oracle's with those
+    entries pointed at an appended all-zero page -- fp16 and e4m3 caches."""
+    rng = np.random.default_rng(31)
+    P = 48
+    kcache = wl.int_f16(rng, -4, 4, (P, 128, 1, 128))
+    lengths = [9000, 20000, 3000]
+    bt = wl.block_table_per_row(rng, lengths, P, width=40)
+    bad = [(0, 3, -1), (1, 0, P), (1, 17, P + 1000), (2, 5, -7)]
+    bt_gpu, bt_orc = bt.copy(), bt.copy()
+    for i, j, val in bad:
+        assert bt[i, j] >= 0  # a visible block's entry
+        bt_gpu[i, j] = val
+        bt_orc[i, j] = P
+    q = wl.int_f16(rng, -4, 4, (3, 4, 128))
+    t2r, sl, qp = wl.decode_rows(lengths)
+    banner("select with table entries outside [0, P)")
+    got = select_gpu(q, kcache, bt_gpu, t2r, sl, qp)
+    kz = np.concatenate([kcache, np.zeros((1, 128, 1, 128), np.float16)])
+    want = orc().select(q, kz, bt_orc, t2r, sl, qp)
+    assert np.array_equal(got, want)
+    codes, scales = wl.fp8_integer_keys(rng, kcache)
+    got8 = select_gpu_fp8(q, codes, scales, bt_gpu, t2r, sl, qp)
+    cz = np.concatenate([codes, np.zeros((1, 128, 1, 128), np.uint8)])
+    sz = np.concatenate([scales, np.ones((1, 128), np.float32)])
+    assert np.array_equal(got8, orc().select_fp8(q, cz, sz, bt_orc, t2r, sl, qp))
 
 
 def test_multirow_requests_and_padding():
