@@ -30,7 +30,8 @@ Workloads (``--workload``):
 Inputs are seeded synthetic data, resident in HBM before timing starts.
 
 One step = one qsa_decode_step call (selection then attention on one
-stream, no host sync); K steps are timed with HIP events at both ends.  The
+stream, no host sync); K steps (200 by default) are timed with HIP events at
+both ends.  The
 steps rotate over distinct KV caches, as consecutive layers would.  A second
 pass runs the two stages through qsa_select and qsa_sparse_attn with events
 between them for the per-stage times and the roofline.  Prints one JSON line.
@@ -223,6 +224,32 @@ def r1_latencies(torch, qsa, wl, dev, calls: int = 64) -> dict:
     return out
 
 
+def units_protocol(torch, stream, decode_call, attn_call, warmup_units: int = 5,
+                   samples: int = 10) -> dict:
+    """The pages' own timing protocol: warmup_units excluded units, then
+    `samples` timed units of 64 decode-step calls and of 128 attention calls
+    (events around each unit); mean, median and min of the per-call time."""
+    def stats(call, per_unit):
+        for u in range(warmup_units):
+            for i in range(per_unit):
+                call(u * per_unit + i)
+        times = []
+        for u in range(samples):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for i in range(per_unit):
+                call(u * per_unit + i)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(ev[0].elapsed_time(ev[1]) / per_unit)
+        return {"mean": round(float(np.mean(times)), 4), "median": round(float(np.median(times)), 4),
+                "min": round(float(np.min(times)), 4)}
+
+    return {"warmup_units": warmup_units, "samples": samples,
+            "decode_step_ms_per_call": {"calls_per_unit": 64, **stats(decode_call, 64)},
+            "attention_ms_per_call": {"calls_per_unit": 128, **stats(attn_call, 128)}}
+
+
 def batched_step(torch, qsa, wl, dev, steps: int = 20) -> dict:
     """The batched configuration (64 rows, lengths uniform in [512, 32768],
     requests 2i and 2i+1 sharing their first pages): mean decode-step time
@@ -375,7 +402,10 @@ def workload_config(w, kv_copies: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # 200 by default: a timed region carries a fixed ~0.14 ms start cost
+    # (measured: 0.2382 / 0.2340 / 0.2321 ms per step at K = 20 / 64 / 200),
+    # which a short region would spread over its few steps
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
@@ -633,6 +663,10 @@ def main() -> int:
     traffic = stored_traffic(w.name)
     ceiling = None if args.no_context else read_ceiling(torch, qsa, dev)
     context = None if args.no_context else r1_latencies(torch, qsa, wl, dev)
+    units = None if args.no_context else units_protocol(
+        torch, stream, step,
+        lambda i: qsa.qsa_sparse_attn(q_attn, *kv_views[i % len(kv_views)], idx, scale, out=out,
+                                      workspace=att_ws))
     batched = None if args.no_context else batched_step(torch, qsa, wl, dev)
     if ceiling:
         log(f"read ceiling {ceiling:.0f} GB/s; single-row latencies {context}")
@@ -689,6 +723,7 @@ def main() -> int:
     if context is not None:
         result["single_row_latency"] = context
         result["batched_64_rows"] = batched
+        result["units_protocol"] = units
         result["gpu_clocks_after_timing"] = clocks
     if not args.no_cpu_baseline:
         base = cpu_baseline(w, scale, fp8=fp8, weights=head_w)
