@@ -77,7 +77,8 @@ def test_very_long_rows_bit_exact(palette):
     """Rows of 2^20 and 1000003 tokens (262144 and 250000 blocks, 2048 table
     entries): two rows get 4-page chunks, 512 per row, so each row's merge
     takes up to 262144 candidates in 32 batches; with a 3-key palette almost
-    every score ties and block order decides."""
+    every score ties and block order decides.  The same rows also through
+    the e4m3 cache and with signed integer head weights."""
     lengths = [1 << 20, 1000003]
     inputs = integer_inputs(77 if palette is None else 78, lengths, 2048, 2048, palette=palette,
                             q_range=4 if palette is None else 1)
@@ -85,6 +86,18 @@ def test_very_long_rows_bit_exact(palette):
     got = select_gpu(*inputs)
     want = orc().select(*inputs)
     assert np.array_equal(got, want)
+    # the same rows through the e4m3 cache (integer keys re-encoded exactly)
+    # and with signed integer head weights
+    q, kcache, bt, t2r, sl, qp = inputs
+    rng = np.random.default_rng(79)
+    codes, scales = wl.fp8_integer_keys(rng, kcache)
+    assert np.array_equal(select_gpu_fp8(q, codes, scales, bt, t2r, sl, qp), want)
+    w = wl.head_weights(rng, len(lengths), integer=True)
+    got_w = qsa.qsa_select_weighted(dev(q), dev(w), dev(kcache), dev(bt), dev(t2r), dev(sl),
+                                    dev(qp))
+    torch.cuda.synchronize()
+    want_w = orc().select_weighted(q, w, bt, t2r, sl, qp, kcache=kcache)
+    assert np.array_equal(got_w.cpu().numpy(), want_w)
 
 
 def test_invalid_page_ids_read_as_zero_keys():
