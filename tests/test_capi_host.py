@@ -519,3 +519,22 @@ def test_read_probe_checks():
     assert lib.qsa_read_probe(ctypes.c_void_p(d), 1 << 20, ctypes.c_void_p(k), 2, None) == WORKSPACE
     assert lib.qsa_read_probe(ctypes.c_void_p(d), 1 << 20, ctypes.c_void_p(d + 64), 4, None) == ALIAS
     assert lib.qsa_read_probe(ctypes.c_void_p(d), 0, ctypes.c_void_p(k), 4, None) == OK
+
+
+@pytest.mark.parametrize("lang", ["c99", "c++17"])
+def test_header_compiles_standalone(lang, tmp_path):
+    """include/qsa.h needs no HIP header and compiles on its own as C99 and
+    as C++17 (a C caller includes it as is)."""
+    import shutil
+    import subprocess
+
+    compiler = "gcc" if lang == "c99" else "g++"
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not found")
+    src = tmp_path / ("use.c" if lang == "c99" else "use.cpp")
+    src.write_text('#include "qsa.h"\nint main(void) { int32_t w; qsa_constants(0, 0, &w, 0); '
+                   'return w == QSA_OUT_WIDTH ? 0 : 1; }\n')
+    res = subprocess.run([compiler, f"-std={lang}", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                          "-fsyntax-only", f"-I{os.path.join(ROOT, 'include')}", str(src)],
+                         capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
