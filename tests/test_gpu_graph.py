@@ -12,23 +12,31 @@ import torch
 
 from paged_top_indexer_amd import workloads as wl
 import paged_top_indexer_amd as qsa
-from gpu_util import DEV, banner, check_attn, dev, orc
+from gpu_util import DEV, banner, check_attn, dev, dev_e4m3, orc
 
 pytestmark = pytest.mark.gpu
 SCALE = wl.SOFTMAX_SCALE
 
 
-@pytest.mark.parametrize("case", ["multi_token_runs_integer", "batched_normal"])
+@pytest.mark.parametrize("case", ["multi_token_runs_integer", "batched_normal", "batched_e4m3"])
 def test_decode_step_graph_replays(case):
     integer = case.endswith("integer")
+    fp8 = case.endswith("e4m3")
     w = wl.multi_token_rows(0, integer=True) if integer else wl.batched_shared(0)
+    if fp8:
+        w = wl.with_fp8_keys(w, integer=False)
     run = 4 if integer else 1
     R = w.rows
-    banner(f"decode step graph replays: {w.name} R={R} rows_per_run={run}")
+    banner(f"decode step graph replays: {w.name} R={R} rows_per_run={run} e4m3={fp8}")
     qd = dev(w.q_sel)
     qv = qd.view(R // run, run, 4, 128) if run > 1 else qd
-    kc, bt, t2r, sl, qp = (dev(a) for a in (w.kcache, w.block_table, w.token_to_req, w.seq_lens,
-                                            w.query_pos))
+    bt, t2r, sl, qp = (dev(a) for a in (w.block_table, w.token_to_req, w.seq_lens, w.query_pos))
+    if fp8:
+        keys = (dev_e4m3(w.kcodes), dev(w.kscale))
+        decode = qsa.qsa_decode_step_fp8
+    else:
+        keys = (dev(w.kcache),)
+        decode = qsa.qsa_decode_step
     k, v = qsa.kv_views(dev(w.kv))
     qa = dev(w.q_attn)
     ws_bytes = max(1, qsa.decode_step_workspace_bytes(R, w.block_table.shape[1]))
@@ -38,8 +46,8 @@ def test_decode_step_graph_replays(case):
     out_g = torch.empty((R, 3, 256), dtype=torch.float16, device=DEV)
 
     def step():
-        qsa.qsa_decode_step(qv, kc, bt, t2r, sl, qp, qa, k, v, SCALE, indices=idx_g, out=out_g,
-                            workspace=ws_g)
+        decode(qv, *keys, bt, t2r, sl, qp, qa, k, v, SCALE, indices=idx_g, out=out_g,
+               workspace=ws_g)
 
     step()  # warm-up outside the capture
     torch.cuda.synchronize()
@@ -60,7 +68,7 @@ def test_decode_step_graph_replays(case):
         torch.cuda.synchronize()
         gi, go = idx_g.cpu().numpy(), out_g.cpu().numpy()
         # eager: the same inputs into buffers of its own
-        ei, eo = qsa.qsa_decode_step(qv, kc, bt, t2r, sl, qp, qa, k, v, SCALE, workspace=ws_e)
+        ei, eo = decode(qv, *keys, bt, t2r, sl, qp, qa, k, v, SCALE, workspace=ws_e)
         torch.cuda.synchronize()
         assert np.array_equal(gi, ei.cpu().numpy()), f"replay {rep}: indices differ from eager"
         assert np.array_equal(go, eo.cpu().numpy()), f"replay {rep}: output differs from eager"
