@@ -34,8 +34,9 @@
 namespace qsa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = kAttnThreads;
 constexpr int kWaves = kThreads / 64;
+static_assert(kCombineThreads == kThreads, "the combine kernel's thread e owns dim e");
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
 // One workgroup per (row, head): wave 0 turns the splits' (max, sum) into
 // weights 2^(m_s - M) and the total sum; then thread e sums the weighted
 // partials of dim e (independent loads, one per split), normalises, rounds.
-constexpr int kMaxSplits = 64;
+constexpr int kMaxSplits = kCombineMaxSplits;  // >= every plan's splits (qsa_launch.h)
 
 __global__ __launch_bounds__(kThreads) void qsa_attn_combine_kernel(AttnParams p) {
   __shared__ float weight[kMaxSplits];

@@ -304,13 +304,29 @@ int check_workspace(void* ws, size_t have, size_t need, Span guarded[], int ngua
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// A launch of `cols` workgroups per row over `rows` rows must fit one grid.
-int check_grid(const char* what, int64_t rows, int64_t cols) {
-  if (qsa::padded_rows(rows) > qsa::kMaxGrid / (cols > 0 ? cols : 1)) {
+// A launch of `cols` workgroups of `threads` threads per row over `rows`
+// rows (padded to whole XCD groups) must stay under 2^32 work-items, the
+// limit of one dispatch.
+int check_grid(const char* what, int64_t rows, int64_t cols, int threads) {
+  const int64_t per_row = (cols > 0 ? cols : 1) * (int64_t)threads;
+  if (qsa::padded_rows(rows) > qsa::kMaxWorkItems / per_row) {
     return fail(QSA_ERR_SHAPE, "%s: %lld rows x %lld workgroups per row exceed one launch", what,
                 (long long)rows, (long long)cols);
   }
   return QSA_OK;
+}
+
+// Both kernels of the selection (chunks over the row groups; the merge,
+// one workgroup per row of the padded groups).
+int check_select_grid(const char* what, const qsa::SelectPlan& plan, int64_t groups) {
+  QSA_TRY(check_grid(what, groups, plan.chunks_per_row, qsa::kChunkThreads));
+  return check_grid(what, qsa::padded_rows(groups) * plan.group, 1, qsa::kMergeThreads);
+}
+
+// Both kernels of the attention (splits; combine, one workgroup per head).
+int check_attn_grid(int64_t rows, const qsa::AttnPlan& plan) {
+  QSA_TRY(check_grid("attention", rows, plan.splits, qsa::kAttnThreads));
+  return check_grid("attention", rows, qsa::kAttHeads, qsa::kCombineThreads);
 }
 
 // Grid rows of the chunk kernel: one per group of plan.group query rows.
@@ -330,11 +346,12 @@ namespace qsa {
 AttnPlan plan_attn(int64_t rows) {
   AttnPlan p;
   constexpr int64_t kResident = 768;
-  constexpr int64_t kMaxSplits = (kOutWidth + 63) / 64;
   const int64_t want =
-      rows > 0 ? std::min(kMaxSplits, std::max<int64_t>(1, (kResident + rows - 1) / rows)) : 1;
+      rows > 0 ? std::min<int64_t>(kMaxAttnSplits, std::max<int64_t>(1, (kResident + rows - 1) / rows))
+               : 1;
   p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
   p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
+  // (at most kMaxAttnSplits: the combine kernel holds every split's weight)
   if (rows == 0) return p;
   size_t off = 0;
   p.partial_off = off;
@@ -387,7 +404,7 @@ int select_impl(const qsa_tensor* q, const qsa_tensor* weights, const qsa_tensor
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
   const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width, v.group);
-  QSA_TRY(check_grid("selection", plan_groups(plan, v.rows), plan.chunks_per_row));
+  QSA_TRY(check_select_grid("selection", plan, plan_groups(plan, v.rows)));
   Span guarded[9] = {span_of(q),        span_of(kcache),   span_of(block_table),
                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
                      span_of(out),      e4m3 ? span_of(kscale) : Span(),
@@ -428,8 +445,8 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   if (sv.rows == 0) return QSA_OK;
   const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width, sv.group);
   const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
-  QSA_TRY(check_grid("selection", plan_groups(splan, sv.rows), splan.chunks_per_row));
-  QSA_TRY(check_grid("attention", av.rows, aplan.splits));
+  QSA_TRY(check_select_grid("selection", splan, plan_groups(splan, sv.rows)));
+  QSA_TRY(check_attn_grid(av.rows, aplan));
   const size_t sel_bytes = align256(splan.bytes);
   const size_t need = sel_bytes + aplan.bytes;
   qsa_tensor whole = *k;
@@ -560,7 +577,8 @@ QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
   const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width, v.group);
-  QSA_TRY(check_grid("paged logits", plan_groups(plan, v.rows), plan.chunks_per_row));
+  QSA_TRY(check_grid("paged logits", plan_groups(plan, v.rows), plan.chunks_per_row,
+                     qsa::kChunkThreads));
   qsa::SelectArgs a;
   fill_select_args(a, q, weights, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
                    query_pos, nullptr, nullptr, v);
@@ -606,7 +624,7 @@ QSA_API int qsa_topk_per_row(const qsa_tensor* logits, const qsa_tensor* token_t
   const int64_t width = logits->shape[1];
   const int64_t pages = (width + QSA_PAGE_SLOTS - 1) / QSA_PAGE_SLOTS;
   const qsa::SelectPlan plan = qsa::plan_select(R, pages);
-  QSA_TRY(check_grid("top-k", R, plan.chunks_per_row));
+  QSA_TRY(check_select_grid("top-k", plan, R));
   Span guarded[5] = {span_of(logits), span_of(token_to_req), span_of(seq_lens),
                      span_of(query_pos), span_of(out)};
   QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 5));
@@ -636,7 +654,7 @@ QSA_API int qsa_sparse_attn(const qsa_tensor* q, const qsa_tensor* k, const qsa_
   QSA_TRY(validate_attn(q, k, v, indices, softmax_scale, out, false, &view));
   if (view.rows == 0) return QSA_OK;
   const qsa::AttnPlan plan = qsa::plan_attn(view.rows);
-  QSA_TRY(check_grid("attention", view.rows, plan.splits));
+  QSA_TRY(check_attn_grid(view.rows, plan));
   qsa_tensor whole = *k;
   whole.ndim = 1;
   whole.shape[0] = view.tokens * 2 * QSA_ATT_DIM;

@@ -21,11 +21,24 @@ constexpr int kKvRow = 512;
 constexpr int kKvPageTokens = 512;
 
 // Row-indexed grids are padded to whole groups of kRowGroup rows on each of
-// the kXcds XCDs (see qsa_device.h); a launch holds at most kMaxGrid
-// workgroups.
+// the kXcds XCDs (see qsa_device.h).  A dispatch holds fewer than 2^32
+// work-items (workgroups x threads per workgroup).
 constexpr int kXcds = 8;
 constexpr int kRowGroup = 4;
-constexpr int64_t kMaxGrid = 0x7FFFFFFF;
+constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
+
+// Threads per workgroup of each kernel (the host checks grid sizes with
+// them).
+constexpr int kChunkThreads = 256;
+constexpr int kMergeThreads = 512;
+constexpr int kAttnThreads = 256;
+constexpr int kCombineThreads = 256;
+
+// Attention splits per row: plan_attn never plans more than kMaxAttnSplits,
+// and the combine kernel keeps one weight per split in LDS.
+constexpr int kMaxAttnSplits = (kOutWidth + 63) / 64;  // 33 splits of 64 positions
+constexpr int kCombineMaxSplits = 64;
+static_assert(kMaxAttnSplits <= kCombineMaxSplits, "combine holds every split's weight");
 
 constexpr int64_t padded_rows(int64_t rows) {
   return (rows + kXcds * kRowGroup - 1) / (kXcds * kRowGroup) * (kXcds * kRowGroup);

@@ -65,8 +65,8 @@
 namespace qsa {
 namespace {
 
-constexpr int kChunkThreads = 256;
-constexpr int kMergeThreads = 512;  // 2 waves per SIMD hide part of the LDS latency
+// (kChunkThreads = 256; kMergeThreads = 512: 2 waves per SIMD hide part of
+// the merge's LDS latency -- both in qsa_launch.h)
 constexpr int kMaxChunkPages = 32;
 constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
 constexpr int kBins = 2048;       // radix digit of up to 11 bits

@@ -503,6 +503,17 @@ def test_launch_size_limits():
     f, a, ws, wsb = select_args(R=(1 << 30), W=(1 << 22))
     assert call_select(a, ws, 1 << 62) == SHAPE
     assert b"exceed one launch" in B.library().qsa_last_error()
+    # 2^22 rows x 8 chunks of 256 threads = 2^33 work-items: more than one
+    # dispatch holds, although far fewer than 2^31 workgroups
+    f, a, ws, wsb = select_args(R=(1 << 22), W=256)
+    assert call_select(a, ws, 1 << 62) == SHAPE
+    assert b"exceed one launch" in B.library().qsa_last_error()
+    f, a, ws, wsb = select_args(R=(1 << 20), W=256)
+    assert call_select(a, 0, 0) == WORKSPACE  # fits one launch; only the workspace is missing
+    # attention at one split per row: 2^25 rows x 256 threads = 2^33 work-items
+    g, at, aws, awsb, _ = attn_args(R=(1 << 25))
+    assert call_attn(at, 0, 0) == SHAPE
+    assert b"exceed one launch" in B.library().qsa_last_error()
     # attention: a batch this large runs one split per row (no partials, so
     # no workspace), whose grid of padded rows always fits one launch
     assert B.sparse_attn_workspace_bytes(1 << 30) == 0

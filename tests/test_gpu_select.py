@@ -6,8 +6,8 @@ import torch
 
 from paged_top_indexer_amd import workloads as wl
 import paged_top_indexer_amd as qsa
-from gpu_util import (banner, check_select_band, dev, orc, select_gpu, select_gpu_fp8,
-                      subset_rows)
+from gpu_util import (banner, check_select_band, dev, oracle_select, orc, select_gpu,
+                      select_gpu_fp8, subset_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,15 +190,15 @@ def long_context():
 
 def test_long_context_full_size(long_context):
     """The full R=128, L=131072 batch in the bench's launch configuration:
-    every row checked structurally, 6 sampled rows against the oracle."""
+    every row against the oracle (band rule), plus the structure of every
+    row."""
     w = long_context
     inputs = w.select_inputs()
     banner("select long_context R=128 L=131072 (full size)")
     got = select_gpu(*inputs)
-    rows = [0, 1, 37, 64, 101, 127]
-    want = orc().select(*subset_rows(inputs, rows))
-    sub = subset_rows(inputs, rows)
-    check_select_band(got[rows], want, orc(), sub, range(len(rows)))
+    want = oracle_select(orc(), inputs)
+    check_select_band(got, want, orc(), inputs, range(w.rows))
+    banner(f"rows identical to the oracle: {int(np.all(got == want, axis=1).sum())}/{w.rows}")
     for r in range(w.rows):
         g = got[r]
         assert np.all(g[2048:] == -1)  # L % 4 == 0: no tail

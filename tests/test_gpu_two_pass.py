@@ -9,6 +9,7 @@ import torch
 from paged_top_indexer_amd import workloads as wl
 import paged_top_indexer_amd as qsa
 from gpu_util import banner, check_select_band, dev, dev_e4m3, orc, subset_rows
+from oracle.acceptance import map_rows
 from test_gpu_select import PLAN_CASES, integer_inputs
 
 pytestmark = pytest.mark.gpu
@@ -145,7 +146,8 @@ def test_two_pass_equals_fused_full_size():
     """At the long-context shape (R=128, 32768 blocks per row) with head
     weights: paged logits then top-k per row give exactly the fused
     weighted selection (the same scorer computes the same fp32 values), and
-    sampled rows satisfy the band rule against the oracle."""
+    every row satisfies the band rule against the oracle's weighted
+    selection."""
     w_ = wl.long_context(0)
     inputs = w_.select_inputs()
     q, kcache, bt, t2r, sl, qp = inputs
@@ -159,15 +161,20 @@ def test_two_pass_equals_fused_full_size():
     torch.cuda.synchronize()
     fused, two, lgh = fused.cpu().numpy(), two.cpu().numpy(), lg.cpu().numpy()
     assert np.array_equal(fused, two)
+    R = w_.rows
+
+    def sub(rs):
+        return subset_rows(inputs, rs)
+
+    want = map_rows(lambda rs: orc().select_weighted(sub(rs)[0], w[rs], *sub(rs)[2:],
+                                                     kcache=kcache), range(R))
+    wl_or = map_rows(lambda rs: orc().paged_logits(sub(rs)[0], w[rs], *sub(rs)[2:], 32768,
+                                                   kcache=kcache), range(R))
+    check_select_band(two, want, orc(), inputs, range(R), row_scores=lambda i: wl_or[i])
+    assert np.allclose(lgh, wl_or, rtol=1e-4, atol=1e-3)
+    # the top-k of the oracle's own logits is the oracle's weighted selection
     rows = [0, 77, 127]
-    sub = subset_rows(inputs, rows)
-    want = orc().select_weighted(sub[0], w[rows], *sub[2:], kcache=kcache)
-    wl_or = orc().paged_logits(sub[0], w[rows], *sub[2:], 32768, kcache=kcache)
-    check_select_band(two[rows], want, orc(), sub, range(len(rows)),
-                      row_scores=lambda i: wl_or[i])
-    assert np.allclose(lgh[rows], wl_or, rtol=1e-4, atol=1e-3)
-    # the top-k of the oracle's own logits of those rows is the oracle selection
-    assert np.array_equal(orc().topk_per_row(wl_or, *sub[3:]), want)
+    assert np.array_equal(orc().topk_per_row(wl_or[rows], *sub(rows)[3:]), want[rows])
 
 
 def test_fail_closed_through_binding():
