@@ -326,6 +326,34 @@ QSA_API int qsa_decode_step_fp8(const qsa_tensor* q_sel, const qsa_tensor* kcach
                                 const qsa_tensor* indices, const qsa_tensor* out, void* workspace,
                                 size_t workspace_bytes, qsa_stream stream);
 
+/*
+ * qsa_decode_step_noalloc -- qsa_decode_step for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * qsa_decode_step (the caller still passes every input and output), but no
+ * workspace: the kernels use a fixed scratch array inside the library,
+ * QSA_STATIC_SCRATCH_BYTES (32 MiB) per GPU, which each GPU the library runs
+ * on holds from the first call until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *
+ * Limit: a call whose decode-step workspace (qsa_decode_step_workspace_bytes
+ * for the grouping q implies) exceeds QSA_STATIC_SCRATCH_BYTES fails with
+ * QSA_ERR_WORKSPACE before anything is launched -- e.g. 128 rows over a
+ * 256-page block table need about 6.6 MB and fit.  Every call on one GPU
+ * shares that GPU's scratch: calls that may overlap on one GPU (different
+ * streams, no ordering between them) race and must not be made; calls in
+ * order on one stream are fine (nothing in the scratch needs clearing:
+ * every byte read was written earlier in the same call).
+ */
+#define QSA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+QSA_API int qsa_decode_step_noalloc(const qsa_tensor* q_sel, const qsa_tensor* kcache,
+                                    const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                                    const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                                    const qsa_tensor* q_attn, const qsa_tensor* k,
+                                    const qsa_tensor* v, float softmax_scale,
+                                    const qsa_tensor* indices, const qsa_tensor* out,
+                                    qsa_stream stream);
+
 /* Workspace bytes qsa_build_metadata needs for num_reqs requests when
  * k_work_metadata is given (0 otherwise). */
 QSA_API size_t qsa_build_metadata_workspace_bytes(int64_t num_reqs);

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     qsa_build_metadata,
     qsa_decode_step,
     qsa_decode_step_fp8,
+    qsa_decode_step_noalloc,
     qsa_paged_logits,
     qsa_read_probe,
     qsa_select,

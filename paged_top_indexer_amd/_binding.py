@@ -87,6 +87,8 @@ def library() -> ctypes.CDLL:
             lib.qsa_select_fp8.restype = ctypes.c_int
             lib.qsa_decode_step_fp8.argtypes = [_P] * 10 + [f32, _P, _P, vp, sz, vp]
             lib.qsa_decode_step_fp8.restype = ctypes.c_int
+            lib.qsa_decode_step_noalloc.argtypes = [_P] * 9 + [f32, _P, _P, vp]
+            lib.qsa_decode_step_noalloc.restype = ctypes.c_int
             lib.qsa_select_weighted.argtypes = [_P] * 9 + [vp, sz, vp]
             lib.qsa_select_weighted.restype = ctypes.c_int
             lib.qsa_paged_logits.argtypes = [_P] * 9 + [vp]
@@ -359,6 +361,23 @@ def qsa_decode_step_fp8(q_sel, kcache, kscale, block_table, token_to_req, seq_le
     check(lib.qsa_decode_step_fp8(*[ctypes.byref(d) for d in first], ctypes.c_float(softmax_scale),
                                   ctypes.byref(idd), ctypes.byref(od), ws, ws_bytes,
                                   ctypes.c_void_p(sh)))
+    return indices, out
+
+
+def qsa_decode_step_noalloc(q_sel, kcache, block_table, token_to_req, seq_lens, query_pos, q_attn,
+                            k, v, softmax_scale: float, indices, out, stream=None):
+    """qsa_decode_step without a workspace: the library's fixed per-GPU
+    scratch stands in (for callers that cannot allocate; calls that overlap
+    on one GPU race).  indices ([R,2051] int32) and out ([R,3,256] fp16) are
+    the caller's; returns (indices, out)."""
+    lib = library()
+    sh = _stream(stream, q_sel.device)
+    first = [tensor_desc(t) for t in (q_sel, kcache, block_table, token_to_req, seq_lens,
+                                      query_pos, q_attn, k, v)]
+    idd, od = tensor_desc(indices), tensor_desc(out)
+    check(lib.qsa_decode_step_noalloc(*[ctypes.byref(d) for d in first],
+                                      ctypes.c_float(softmax_scale), ctypes.byref(idd),
+                                      ctypes.byref(od), ctypes.c_void_p(sh)))
     return indices, out
 
 

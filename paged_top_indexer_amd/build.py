@@ -20,7 +20,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["qsa_select.hip", "qsa_attn.hip", "qsa_metadata.hip", "qsa_probe.hip"]
+HIP_SOURCES = ["qsa_select.hip", "qsa_attn.hip", "qsa_metadata.hip", "qsa_noalloc.hip",
+               "qsa_probe.hip"]
 HOST_SOURCES = ["qsa_capi.cpp", "qsa_select_plan.cpp"]
 
 HIP_FLAGS = [

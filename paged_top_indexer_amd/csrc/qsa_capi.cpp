@@ -16,6 +16,9 @@
 #include "../../include/qsa.h"
 #include "qsa_launch.h"
 
+static_assert(QSA_STATIC_SCRATCH_BYTES == qsa::kStaticScratchBytes,
+              "the header states the fixed scratch's size");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -418,12 +421,15 @@ int select_impl(const qsa_tensor* q, const qsa_tensor* weights, const qsa_tensor
   return QSA_OK;
 }
 
+// static_ws: the workspace is the library's fixed device scratch (the
+// no-allocation entry point; `workspace` is ignored), looked up only after
+// every check has passed, including that the call fits in it.
 int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_tensor* kscale,
                 bool e4m3, const qsa_tensor* block_table, const qsa_tensor* token_to_req,
                 const qsa_tensor* seq_lens, const qsa_tensor* query_pos, const qsa_tensor* q_attn,
                 const qsa_tensor* k, const qsa_tensor* v, float softmax_scale,
                 const qsa_tensor* indices, const qsa_tensor* out, void* workspace,
-                size_t workspace_bytes, qsa_stream stream) {
+                size_t workspace_bytes, qsa_stream stream, bool static_ws = false) {
   g_last_error[0] = '\0';
   SelectView sv;
   QSA_TRY(validate_select_inputs(q_sel, nullptr, kcache, kscale, e4m3, block_table,
@@ -449,6 +455,21 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   QSA_TRY(check_attn_grid(av.rows, aplan));
   const size_t sel_bytes = align256(splan.bytes);
   const size_t need = sel_bytes + aplan.bytes;
+  if (static_ws) {
+    if (need > qsa::kStaticScratchBytes) {
+      return fail(QSA_ERR_WORKSPACE,
+                  "%lld rows with a %lld-page block table need %zu bytes of scratch; the fixed "
+                  "scratch holds %zu (use qsa_decode_step with a workspace)",
+                  (long long)sv.rows, (long long)sv.width, need, qsa::kStaticScratchBytes);
+    }
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      const int err = qsa::static_scratch(&workspace);
+      if (err) return fail(QSA_ERR_LAUNCH, "fixed scratch lookup failed (hipError %d)", err);
+      workspace_bytes = qsa::kStaticScratchBytes;
+    }
+  }
   qsa_tensor whole = *k;
   whole.ndim = 1;
   whole.shape[0] = av.tokens * 2 * QSA_ATT_DIM;
@@ -695,6 +716,18 @@ QSA_API int qsa_decode_step_fp8(const qsa_tensor* q_sel, const qsa_tensor* kcach
                                 size_t workspace_bytes, qsa_stream stream) {
   return decode_impl(q_sel, kcache, kscale, true, block_table, token_to_req, seq_lens, query_pos,
                      q_attn, k, v, softmax_scale, indices, out, workspace, workspace_bytes, stream);
+}
+
+QSA_API int qsa_decode_step_noalloc(const qsa_tensor* q_sel, const qsa_tensor* kcache,
+                                    const qsa_tensor* block_table, const qsa_tensor* token_to_req,
+                                    const qsa_tensor* seq_lens, const qsa_tensor* query_pos,
+                                    const qsa_tensor* q_attn, const qsa_tensor* k,
+                                    const qsa_tensor* v, float softmax_scale,
+                                    const qsa_tensor* indices, const qsa_tensor* out,
+                                    qsa_stream stream) {
+  return decode_impl(q_sel, kcache, nullptr, false, block_table, token_to_req, seq_lens,
+                     query_pos, q_attn, k, v, softmax_scale, indices, out, nullptr, 0, stream,
+                     true);
 }
 
 QSA_API size_t qsa_build_metadata_workspace_bytes(int64_t num_reqs) {

@@ -40,6 +40,10 @@ constexpr int kMaxAttnSplits = (kOutWidth + 63) / 64;  // 33 splits of 64 positi
 constexpr int kCombineMaxSplits = 64;
 static_assert(kMaxAttnSplits <= kCombineMaxSplits, "combine holds every split's weight");
 
+// Bytes of the fixed device scratch of the no-allocation decode step (one
+// copy per GPU, held until the process ends).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+
 constexpr int64_t padded_rows(int64_t rows) {
   return (rows + kXcds * kRowGroup - 1) / (kXcds * kRowGroup) * (kXcds * kRowGroup);
 }
@@ -139,5 +143,10 @@ int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_metadata(const MetaArgs& a, void* stream);
 int launch_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
+
+// Device address of the calling thread's current device's fixed scratch
+// (kStaticScratchBytes, 256-byte aligned); looked up once per device.
+// Returns the hipError_t (0 = success).
+int static_scratch(void** ptr);
 
 }  // namespace qsa

@@ -245,6 +245,33 @@ def test_decode_step_checks():
         ctypes.byref(s["out"]), ctypes.byref(a["out"]), ctypes.c_void_p(ws), wsb - 256, None) == WORKSPACE
 
 
+def test_decode_step_noalloc_checks():
+    """The no-allocation decode step validates like qsa_decode_step and
+    refuses a call whose workspace would exceed the fixed scratch, before it
+    looks the scratch up or launches anything (no GPU needed to see that)."""
+    lib = B.library()
+    f, s, _, _ = select_args(R=2, W=40)
+    g, a, _, _, base = attn_args(R=2)
+
+    def call(sel, att, idx=None):
+        return lib.qsa_decode_step_noalloc(
+            ctypes.byref(sel["q"]), ctypes.byref(sel["kcache"]), ctypes.byref(sel["bt"]),
+            ctypes.byref(sel["t2r"]), ctypes.byref(sel["sl"]), ctypes.byref(sel["qp"]),
+            ctypes.byref(att["q"]), ctypes.byref(att["k"]), ctypes.byref(att["v"]),
+            ctypes.c_float(0.0625), ctypes.byref(idx or sel["out"]), ctypes.byref(att["out"]),
+            None)
+
+    assert call(s, a, idx=mk(g, B.I32, (2, 2051), 4, ptr=base)) == ALIAS
+    assert call(s, a, idx=mk(g, B.I32, (3, 2051), 4)) == SHAPE
+    # 4096 rows over a 256-page table: ~64 MiB of candidates > the 32 MiB scratch
+    R, W = 4096, 256
+    f2, big, _, _ = select_args(R=R, N=R, W=W)
+    g2, att2, _, _, _ = attn_args(R=R)
+    assert B.decode_step_workspace_bytes(R, W) > 32 << 20
+    assert call(big, att2) == WORKSPACE
+    assert b"fixed scratch holds 33554432" in lib.qsa_last_error()
+
+
 def test_torch_descriptor_dtype_refused():
     """A float32 query is refused by the library; the binding turns the
     status into RuntimeError."""
