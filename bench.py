@@ -1,13 +1,20 @@
 """Decode-step throughput of the QSA select + sparse-attention path on one
 MI355X.
 
-Workloads (``--workload``):
+Workloads (``--workload``), one per configuration of the decode batch:
 
-* long_context (default): the long-context decode batch -- R=128 query rows,
-  each of a 131072-token request (32768 compressed blocks), a 32768-page
-  fp16 N(0,1) compressed-key cache (1 GiB) behind random permuted block
-  tables, and full-width [128,2051] sparse attention over a 131072-token
-  packed fp16 KV cache (128 MiB).
+* tiny: one decode row of 519 tokens (129 visible blocks, a 3-token tail)
+  over an 8-page cache of integer-valued keys with forced exact ties.
+* saturated: one decode row of 9215 tokens (2303 blocks) over an 8192-page
+  N(0,1) cache: the top-512 fills the 2051-wide output.
+* batched: 64 decode rows, lengths uniform in [512, 32768], requests 2i and
+  2i+1 sharing their first pages, a 16384-page N(0,1) cache.
+* ties_edges: 32 rows over edge lengths (0, 1-3, one page, page crossings,
+  65536) with keys from a 64-vector integer palette (massive ties).
+* long_context (default): R=128 query rows, each of a 131072-token request
+  (32768 compressed blocks), a 32768-page fp16 N(0,1) compressed-key cache
+  (1 GiB) behind random permuted block tables, and full-width [128,2051]
+  sparse attention over a 131072-token packed fp16 KV cache (128 MiB).
 * long_context_fp8: the long-context batch with its compressed keys
   absmax-quantized to an e4m3 cache (128 B of codes + one fp32 scale per
   key, 528 MiB), timed through qsa_decode_step_fp8.
@@ -35,6 +42,9 @@ both ends.  The
 steps rotate over distinct KV caches, as consecutive layers would.  A second
 pass runs the two stages through qsa_select and qsa_sparse_attn with events
 between them for the per-stage times and the roofline.  Prints one JSON line.
+The oracle then checks every row of the timed configuration's output (the
+band rule on N(0,1) inputs, bit-exact selection on integer inputs, attention
+within 2e-3 and one fp16 ulp); the exit status is 1 when any row fails.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline]
@@ -57,8 +67,25 @@ if ROOT not in sys.path:
 
 METRIC = "select+sparse-attn decode rows/sec and achieved HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# the sources that fix the kernels' memory traffic (a counter summary is
+# used only while their hash matches the one it was taken on)
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
-                  for f in ("qsa_select.hip", "qsa_device.h", "qsa_launch.h", "qsa_select_plan.cpp")]
+                  for f in ("qsa_select.hip", "qsa_attn.hip", "qsa_device.h", "qsa_launch.h",
+                            "qsa_select_plan.cpp", "qsa_capi.cpp")]
+
+# --workload name -> (builder, integer inputs: the selection is checked
+# bit-exact; else by the band rule)
+WORKLOADS = {
+    "tiny": ("tiny_integer", True),
+    "saturated": ("saturated_row", False),
+    "batched": ("batched_shared", False),
+    "ties_edges": ("ties_and_edges", True),
+    "long_context": ("long_context", False),
+    "long_context_fp8": ("long_context", False),
+    "long_context_two_pass": ("long_context", False),
+    "multi_token": ("multi_token_rows", False),
+    "multi_token_metadata": ("multi_token_rows", False),
+}
 
 
 def log(msg: str) -> None:
@@ -103,13 +130,18 @@ def logits_algorithmic_bytes(seq_lens, query_pos, token_to_req, width: int) -> i
     return total
 
 
-def attn_algorithmic_bytes(indices: np.ndarray) -> int:
-    """Per row: 1 KiB per distinct valid token (K and V halves), the 8204 B
-    index row, the 1.5 KiB query and the 1.5 KiB output."""
-    total = 0
-    for row in indices:
-        total += 1024 * len(np.unique(row[row >= 0])) + 8204 + 1536 + 1536
-    return total
+def attn_algorithmic_bytes(indices: np.ndarray) -> tuple[int, int]:
+    """(HBM bytes, gather bytes) the attention must move per launch.  Every
+    row of a launch indexes the same packed KV cache, so HBM must supply each
+    distinct valid token of the launch once: 1 KiB (K and V halves) per
+    token of the union over all rows.  Gather bytes count 1 KiB per distinct
+    valid token of each row, i.e. what the rows read, repeats across rows
+    included (those come from the caches when they hit).  Both add, per row,
+    the 8204 B index row, the 1.5 KiB query and the 1.5 KiB output."""
+    per_row = (8204 + 1536 + 1536) * indices.shape[0]
+    union = 1024 * len(np.unique(indices[indices >= 0]))
+    gather = sum(1024 * len(np.unique(row[row >= 0])) for row in indices)
+    return union + per_row, gather + per_row
 
 
 def kernel_source_hash() -> str:
@@ -120,10 +152,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per select launch from the committed counter summary of this
-    workload (profiles/select_<workload>_counters.json), if it was taken on
-    the current kernel source; else None."""
+def stored_counters(workload: str):
+    """The committed counter summary of this workload
+    (profiles/select_<workload>_counters.json) if it was taken on the
+    current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", f"select_{workload}_counters.json")
     if not os.path.exists(path):
         return None
@@ -131,7 +163,7 @@ def stored_traffic(workload: str):
         rec = json.load(f)
     if rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
 
 
 def read_ceiling(torch, qsa, dev, gib: int = 2, reps: int = 5) -> float:
@@ -250,40 +282,6 @@ def units_protocol(torch, stream, decode_call, attn_call, warmup_units: int = 5,
             "attention_ms_per_call": {"calls_per_unit": 128, **stats(attn_call, 128)}}
 
 
-def batched_step(torch, qsa, wl, dev, steps: int = 20) -> dict:
-    """The batched configuration (64 rows, lengths uniform in [512, 32768],
-    requests 2i and 2i+1 sharing their first pages): mean decode-step time
-    and the selection stage's algorithmic rate; context only."""
-    w = wl.batched_shared(0)
-    d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
-    sel = [d(a) for a in w.select_inputs()]
-    kvd = d(w.kv)
-    k, v = qsa.kv_views(kvd)
-    q = d(w.q_attn)
-    idx = torch.empty((w.rows, 2051), dtype=torch.int32, device=dev)
-    out = torch.empty((w.rows, 3, 256), dtype=torch.float16, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def mean_ms(fn):
-        for _ in range(5):
-            fn()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(steps):
-            fn()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / steps
-
-    step = mean_ms(lambda: qsa.qsa_decode_step(*sel, q, k, v, wl.SOFTMAX_SCALE, indices=idx,
-                                               out=out))
-    select = mean_ms(lambda: qsa.qsa_select(*sel, out=idx))
-    sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req)
-    return {"workload": w.name, "rows": int(w.rows), "step_ms": round(step, 4),
-            "rows_per_s": round(w.rows / step * 1e3, 1), "select_ms": round(select, 4),
-            "select_algorithmic_gbs": round(sel_bytes / select / 1e6, 1)}
-
-
 def host_cpu() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -296,8 +294,9 @@ def host_cpu() -> str:
 
 
 def host_threads() -> int:
-    """The CPU threads this process may run on, at most 16 (the host share of
-    one GPU on a shared node, whatever the machine's own count)."""
+    """Threads for the oracle: the CPUs this process may run on, at most 16
+    (the host share of one GPU on a shared node, whatever the machine's own
+    count)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -305,65 +304,148 @@ def host_threads() -> int:
     return max(1, min(n, 16))
 
 
-def cpu_baseline(w, scale: float, fp8: bool = False, weights=None,
-                 max_seconds: float = 20.0, threaded_seconds: float = 8.0) -> dict:
-    """The CPU oracle (plain C, unmodified) on the host cores: the whole decode
-    step of the first rows of the same workload, single-threaded until all
-    rows are done or max_seconds of work have been spent; then the same
-    per-row calls with the rows dealt to host_threads() threads (the C calls
-    release the interpreter lock and keep no shared state) for about
-    threaded_seconds, cycling over the rows."""
-    import itertools
-    from concurrent.futures import ThreadPoolExecutor
+def _pin(cpu: int):
+    """Pin the calling thread to one CPU; returns the previous set."""
+    before = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {cpu})
+    return before
 
+
+def oracle_rows_fn(w, scale: float, kind: str, weights=None, batch: int = 4):
+    """(per-batch inputs prepared up front, fn(batch inputs) running the whole
+    decode step of those rows through the oracle).  Slicing and copying the
+    rows' inputs happens here, outside any timed region; a call then only
+    hands the arrays to the C oracle (a few microseconds against ~50 ms per
+    row at the long-context shape)."""
     import oracle
 
     orc = oracle.default()
     q, kc, bt, t2r, sl, qp = w.select_inputs()
+    R = w.rows
+    batches = []
+    for i in range(0, R, batch):
+        rs = np.arange(i, min(R, i + batch))
+        batches.append(dict(q=np.ascontiguousarray(q[rs]), t2r=np.ascontiguousarray(t2r[rs]),
+                            qp=np.ascontiguousarray(qp[rs]),
+                            qa=np.ascontiguousarray(w.q_attn[rs]),
+                            wt=None if weights is None else np.ascontiguousarray(weights[rs]),
+                            rows=len(rs)))
 
-    def one_row(i: int):
-        r = np.array([i])
-        if fp8:
-            sel = orc.select_fp8(q[r], w.kcodes, w.kscale, bt, t2r[r], sl, qp[r])
-        elif weights is not None:
-            lg = orc.paged_logits(q[r], weights[r], bt, t2r[r], sl, qp[r], bt.shape[1] * 128,
+    def run(b):
+        if kind == "fp8":
+            sel = orc.select_fp8(b["q"], w.kcodes, w.kscale, bt, b["t2r"], sl, b["qp"])
+        elif kind == "two_pass":
+            lg = orc.paged_logits(b["q"], b["wt"], bt, b["t2r"], sl, b["qp"], bt.shape[1] * 128,
                                   kcache=kc)
-            sel = orc.topk_per_row(lg, t2r[r], sl, qp[r])
+            sel = orc.topk_per_row(lg, b["t2r"], sl, b["qp"])
         else:
-            sel = orc.select(q[r], kc, bt, t2r[r], sl, qp[r])
-        return sel, orc.sparse_attn(w.q_attn[r], w.kv, sel, scale)
+            sel = orc.select(b["q"], kc, bt, b["t2r"], sl, b["qp"])
+        orc.sparse_attn(b["qa"], w.kv, sel, scale)
+        return b["rows"]
 
-    done = 0
-    t0 = time.perf_counter()
-    outs = []
-    while done < w.rows and time.perf_counter() - t0 < max_seconds:
-        outs.append(one_row(done))
-        done += 1
-    dt = time.perf_counter() - t0
+    return batches, run
+
+
+def cpu_baseline(w, scale: float, kind: str, weights=None, min_seconds: float = 10.0,
+                 max_seconds: float = 25.0, threaded_seconds: float = 6.0) -> dict:
+    """The CPU oracle (plain C, unmodified) on the host cores, over the same
+    workload: the whole decode step (selection then attention) of batches of
+    4 rows, cycling over the rows.  Single-threaded leg: the calling thread
+    pinned to one CPU, until every row is done once and at least min_seconds
+    have passed (at most max_seconds).  Threaded leg: host_threads() threads,
+    each pinned to its own CPU, taking batches from a shared counter for
+    about threaded_seconds (the C calls release the interpreter lock and
+    keep no shared state)."""
+    import itertools
+    from concurrent.futures import ThreadPoolExecutor
+
+    batches, run = oracle_rows_fn(w, scale, kind, weights)
+    cpus = sorted(os.sched_getaffinity(0))
+    before = _pin(cpus[0])
+    try:
+        run(batches[0])  # warm-up (page-in of the oracle and the inputs)
+        done, k = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            dt = time.perf_counter() - t0
+            if dt >= max_seconds or (dt >= min_seconds and done >= w.rows):
+                break
+            done += run(batches[k % len(batches)])
+            k += 1
+        dt = time.perf_counter() - t0
+    finally:
+        os.sched_setaffinity(0, before)
 
     threads = host_threads()
     ticket = itertools.count()  # next() on a count is atomic under the interpreter lock
     t1 = time.perf_counter()
     stop = t1 + threaded_seconds
 
-    def worker(_):
+    def worker(i):
+        os.sched_setaffinity(0, {cpus[i % len(cpus)]})
         n = 0
         while time.perf_counter() < stop:
-            one_row(next(ticket) % w.rows)
-            n += 1
+            n += run(batches[next(ticket) % len(batches)])
         return n
 
     with ThreadPoolExecutor(threads) as ex:
         done_t = sum(ex.map(worker, range(threads)))
     dt_t = time.perf_counter() - t1
     return {"value": done / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {w.rows} rows of the same workload, select + attention "
-                      f"per row, {dt:.1f} s single-threaded",
-            "host_cpu": host_cpu(), "host_threads": threads,
+            "sample": f"{done} rows ({w.rows} distinct, batches of 4 cycled) of the same "
+                      f"workload, selection + attention per row, {dt:.1f} s on one pinned CPU "
+                      f"(inputs sliced before the clock starts)",
+            "host_cpu": host_cpu(), "nproc": os.cpu_count(), "affinity_cpus": len(cpus),
             "threaded": {"value": done_t / dt_t, "unit": "rows/s", "cores": threads,
-                         "sample": f"{done_t} rows (row i mod {w.rows}) dealt to {threads} "
-                                   f"threads, {dt_t:.1f} s"},
-            "_outs": outs}
+                         "sample": f"{done_t} rows dealt in batches of 4 to {threads} threads "
+                                   f"pinned to distinct CPUs, {dt_t:.1f} s"}}
+
+
+def parity_all_rows(w, kind: str, exact: bool, got_idx, got_out, scale: float,
+                    weights=None) -> dict:
+    """The timed configuration's output against the oracle on every row:
+    the selection bit-exact (integer inputs) or within the band rule
+    (N(0,1) inputs), and the attention over the GPU's own index rows within
+    2e-3 and one fp16 ulp of the float64 oracle.  Rows are dealt to host
+    threads."""
+    import oracle
+    from oracle import acceptance as acc
+
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    inputs = w.select_inputs()
+    row_scores = None
+    if kind == "fp8":
+        inputs = w.select_inputs_fp8()
+        ref = acc.oracle_select(orc, inputs)
+    elif kind == "two_pass":
+        q, kc, bt, t2r, sl, qp = inputs
+        width = bt.shape[1] * 128
+        ref = acc.map_rows(lambda rs: orc.select_weighted(q[rs], weights[rs], bt, t2r[rs], sl,
+                                                          qp[rs], kcache=kc), range(w.rows))
+
+        def row_scores(r):
+            return orc.paged_logits(q[r:r + 1], weights[r:r + 1], bt, t2r[r:r + 1], sl,
+                                    qp[r:r + 1], width, kcache=kc)[0]
+    else:
+        ref = acc.oracle_select(orc, inputs)
+    identical = int(np.all(got_idx == ref, axis=1).sum())
+    if exact:
+        problems = {int(r): "differs" for r in np.flatnonzero(~np.all(got_idx == ref, axis=1))}
+    else:
+        problems = acc.band_problems(orc, got_idx, ref, inputs, row_scores=row_scores)
+    want = acc.oracle_attn(orc, w.q_attn, w.kv, got_idx, scale)
+    err, over = acc.attn_error(got_out, want)
+    ok = not problems and err <= acc.ATTN_TOL and over == 0
+    return {"rows_checked": int(w.rows),
+            "selection_rule": "bit-exact" if exact else "band 1e-3 * max(|s_n|, 1)",
+            "selection_identical": identical,
+            "selection_within_rule": int(w.rows - len(problems)),
+            "selection_failures": {str(k): v for k, v in list(problems.items())[:5]},
+            "attention_rows_checked": int(w.rows), "attention_index_rows": "the GPU's own",
+            "attention_max_abs_err": err, "attention_over_1ulp": over,
+            "attention_tol": acc.ATTN_TOL, "ok": bool(ok),
+            "check_s": round(time.perf_counter() - t0, 1)}
 
 
 def gpu_clocks():
@@ -407,14 +489,13 @@ def main() -> int:
     # which a short region would spread over its few steps
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle: no CPU baseline and no parity check")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the read-ceiling probe and the single-row latencies")
+                    help="skip the read-ceiling probe, the single-row latencies and the pages' "
+                         "unit protocol")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", choices=["long_context", "long_context_fp8",
-                                           "long_context_two_pass", "multi_token",
-                                           "multi_token_metadata"],
-                    default="long_context")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="long_context")
     ap.add_argument("--rows-per-run", type=int, default=0,
                     help="pass the selection queries as [R/n, n, 4, 128] (runs of n rows of "
                          "one request); default 4 for the multi_token workloads, else 1")
@@ -444,21 +525,21 @@ def main() -> int:
         return 0
 
     t0 = time.perf_counter()
+    builder, exact = WORKLOADS[args.workload]
     fp8 = args.workload == "long_context_fp8"
     two_pass = args.workload == "long_context_two_pass"
     meta = args.workload == "multi_token_metadata"
+    multi = args.workload in ("multi_token", "multi_token_metadata")
+    kind = "fp8" if fp8 else "two_pass" if two_pass else "f16"
     head_w = None
-    if args.workload in ("multi_token", "multi_token_metadata"):
-        w = wl.multi_token_rows(args.seed)
-        if meta:
-            w.name = w.name + "_metadata"
-    else:
-        w = wl.long_context(args.seed)
-        if fp8:
-            w = wl.with_fp8_keys(w, integer=False)
-        if two_pass:
-            head_w = wl.head_weights(np.random.default_rng(args.seed + 555), w.rows)
-            w.name = w.name + "_two_pass"
+    w = getattr(wl, builder)(args.seed)
+    if fp8:
+        w = wl.with_fp8_keys(w, integer=False)
+    if two_pass:
+        head_w = wl.head_weights(np.random.default_rng(args.seed + 555), w.rows)
+        w.name = w.name + "_two_pass"
+    if meta:
+        w.name = w.name + "_metadata"
     log(f"generated {w.name} in {time.perf_counter() - t0:.1f} s")
     dev = torch.device("cuda:0")
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -469,16 +550,16 @@ def main() -> int:
     else:
         sel_in = [d(a) for a in w.select_inputs()]
         select_fn, decode_fn = qsa.qsa_select, qsa.qsa_decode_step
-    multi = args.workload in ("multi_token", "multi_token_metadata")
     run = args.rows_per_run or (4 if multi else 1)
     q_rows = sel_in[0]
     if run > 1:
         assert w.rows % run == 0, "rows must split into whole runs"
         sel_in[0] = q_rows.view(w.rows // run, run, 4, 128)
     # Consecutive decode steps of a model read different layers' caches.  The
-    # steps here rotate over distinct KV caches (8 x 128 MiB by default, four
-    # times the 256 MB Infinity Cache) so that no step finds its KV in the
-    # last-level cache because an earlier step read it.
+    # steps here rotate over distinct KV caches (8 x 128 MiB by default at the
+    # long-context shape, four times the 256 MB Infinity Cache) so that no
+    # step finds its KV in the last-level cache because an earlier step read
+    # it.
     kv_sets = [d(w.kv)]
     for i in range(1, args.kv_copies):
         kv_sets.append(d(wl.normal_f16(np.random.default_rng(args.seed + 1000 + i), w.kv.shape)))
@@ -562,8 +643,8 @@ def main() -> int:
     ms_per_step = t_ev[0].elapsed_time(t_ev[1]) / args.steps
     clocks = None if args.no_context else gpu_clocks()
 
-    # Per-stage times for the roofline: the same two stages through their own
-    # entry points, with events recorded on the launch stream around each.
+    # Per-stage times: the same two stages through their own entry points,
+    # with events recorded on the launch stream around each.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         k, v = kv_views[i % len(kv_views)]
@@ -623,56 +704,84 @@ def main() -> int:
     got_out = out.cpu().numpy()
     sel_bytes = select_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
                                          key_bytes=132 if fp8 else 256)
-    att_bytes = attn_algorithmic_bytes(got_idx)
+    att_bytes, att_gather = attn_algorithmic_bytes(got_idx)
     # kernel launches of one timed step at these shapes (the committed kernel
     # traces show one call of each per step)
+    plan_chunks = qsa.select_workspace_bytes(R, w.block_table.shape[1]) > 0
     kernels_per_step = (["qsa_metadata_kernel"] if meta else []) + (
         ["qsa_select_chunk_kernel (paged logits)", "qsa_select_chunk_kernel (top-k per row)"]
-        if two_pass else ["qsa_select_chunk_kernel"]) + [
-        "qsa_select_merge_kernel", "qsa_attn_kernel", "qsa_attn_combine_kernel"]
+        if two_pass else ["qsa_select_chunk_kernel"]) + (
+        ["qsa_select_merge_kernel"] if plan_chunks else []) + ["qsa_attn_kernel"] + (
+        ["qsa_attn_combine_kernel"] if qsa.sparse_attn_workspace_bytes(R) > 0 else [])
     sel_avg_s = float(np.mean(sel_ms)) / 1e3
     att_avg_s = float(np.mean(att_ms)) / 1e3
 
     def back_to_back_ms(fn) -> float:
         """Average duration of fn's launches: K calls back to back on the
         launch stream between two events (no events between the kernels)."""
-        fn()
+        fn(0)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for _ in range(args.steps):
-            fn()
+        for i in range(args.steps):
+            fn(i)
         ev[1].record(stream)
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / args.steps
 
+    # Roofline of each stage: algorithmic bytes per launch / the launch's
+    # average duration back to back; the stage that takes longer is the
+    # dominant one (the selection at every shape with long rows).
     if two_pass:
-        # the dominant kernel of the two-pass step is the paged-logits pass
-        roof_bytes = logits_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
-                                              logits_width)
-        roof_ms = back_to_back_ms(lambda: qsa.qsa_paged_logits(*sel_in, weights=wt, logits=logits))
-        roof_kernel = "qsa_paged_logits (qsa_select_chunk_kernel, logits out)"
+        sel_roof_bytes = logits_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
+                                                  logits_width)
+        sel_roof_ms = back_to_back_ms(
+            lambda i: qsa.qsa_paged_logits(*sel_in, weights=wt, logits=logits))
+        sel_kernel = "qsa_paged_logits (qsa_select_chunk_kernel, logits out)"
     else:
-        roof_bytes = sel_bytes
-        roof_ms = back_to_back_ms(lambda: select_fn(*(built_in if meta else sel_in), out=idx,
-                                                    workspace=sel_ws))
-        roof_kernel = (("qsa_select_fp8" if fp8 else "qsa_select") +
-                       " (qsa_select_chunk_kernel + qsa_select_merge_kernel)")
-    roof_s = roof_ms / 1e3
-    log(f"roofline launches back to back: {roof_ms:.4f} ms each")
-    achieved = roof_bytes / roof_s / 1e9
-    traffic = stored_traffic(w.name)
+        sel_roof_bytes = sel_bytes
+        sel_roof_ms = back_to_back_ms(lambda i: select_fn(*(built_in if meta else sel_in), out=idx,
+                                                          workspace=sel_ws))
+        sel_kernel = (("qsa_select_fp8" if fp8 else "qsa_select") + " (qsa_select_chunk_kernel" +
+                      (" + qsa_select_merge_kernel)" if plan_chunks else ")"))
+    att_roof_ms = back_to_back_ms(
+        lambda i: qsa.qsa_sparse_attn(q_attn, *kv_views[i % len(kv_views)], idx, scale, out=out,
+                                      workspace=att_ws))
+    att_kernel = "qsa_sparse_attn (qsa_attn_kernel" + (
+        " + qsa_attn_combine_kernel)" if qsa.sparse_attn_workspace_bytes(R) > 0 else ")")
+    log(f"back to back: selection {sel_roof_ms:.4f} ms, attention {att_roof_ms:.4f} ms per launch")
+    counters = stored_counters(w.name)
     ceiling = None if args.no_context else read_ceiling(torch, qsa, dev)
+
+    def roof(nbytes, ms, kernel, traffic):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kernel,
+                "ceiling": None if ceiling is None else round(ceiling, 1),
+                "frac_of_ceiling": None if ceiling is None else round(gbs / ceiling, 4),
+                "bytes_per_launch": int(nbytes), "avg_launch_ms": round(ms, 4)}
+
+    sel_roof = roof(sel_roof_bytes, sel_roof_ms, sel_kernel,
+                    counters.get("hbm_bytes_per_launch") if counters else None)
+    att_roof = roof(att_bytes, att_roof_ms, att_kernel,
+                    counters.get("attn_hbm_bytes_per_launch") if counters else None)
+    dominant, other = (sel_roof, att_roof) if sel_roof_ms >= att_roof_ms else (att_roof, sel_roof)
     context = None if args.no_context else r1_latencies(torch, qsa, wl, dev)
     units = None if args.no_context else units_protocol(
         torch, stream, step,
         lambda i: qsa.qsa_sparse_attn(q_attn, *kv_views[i % len(kv_views)], idx, scale, out=out,
                                       workspace=att_ws))
-    batched = None if args.no_context else batched_step(torch, qsa, wl, dev)
     if ceiling:
         log(f"read ceiling {ceiling:.0f} GB/s; single-row latencies {context}")
     rows_per_s = R / (ms_per_step / 1e3)
     step_bytes = sel_bytes + att_bytes + (R * logits_width * 8 if two_pass else 0)
     step_gbs = step_bytes / (ms_per_step / 1e3) / 1e9
+    data = ("synthetic (seeded N(0,1) keys absmax-quantized to e4m3 with one fp32 scale per "
+            "key; N(0,1) fp16 queries/KV; random permuted block tables)" if fp8 else
+            "synthetic (seeded N(0,1) fp16 keys/queries/KV, per-head weights U[-0.5, 1.5], "
+            "random permuted block tables)" if two_pass else
+            "synthetic (seeded integer-valued fp16 keys/queries with exact ties; N(0,1) fp16 KV)"
+            if exact else
+            "synthetic (seeded N(0,1) fp16 keys/queries/KV, random block tables)")
 
     result = {
         "metric": METRIC,
@@ -686,18 +795,9 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "e4m3 keys x f16 queries, f16 attention" if fp8 else "f16",
-        "data": ("synthetic (seeded N(0,1) keys absmax-quantized to e4m3 with one fp32 scale per "
-                 "key; N(0,1) fp16 queries/KV; random permuted block tables)" if fp8 else
-                 "synthetic (seeded N(0,1) fp16 keys/queries/KV, per-head weights U[-0.5, 1.5], "
-                 "random permuted block tables)" if two_pass else
-                 "synthetic (seeded N(0,1) fp16 keys/queries/KV, random permuted block tables)"),
+        "data": data,
         "config": {**workload_config(w, len(kv_sets)), "rows_per_run": run},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": roof_kernel,
-                     "ceiling": None if ceiling is None else round(ceiling, 1),
-                     "frac_of_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
-                     "bytes_per_launch": roof_bytes, "avg_launch_ms": round(roof_s * 1e3, 4)},
+        "roofline": dominant,
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
                    # per-step event times of the instrumented pass (K samples each)
                    "select_ms_median": round(float(np.median(sel_ms)), 4),
@@ -705,8 +805,15 @@ def main() -> int:
                    "attention_ms_median": round(float(np.median(att_ms)), 4),
                    "attention_ms_min": round(float(np.min(att_ms)), 4),
                    "kernels_per_step": kernels_per_step,
+                   "other_stage_roofline": other,
                    "attention_bytes": att_bytes,
-                   "attention_gbs": round(att_bytes / att_avg_s / 1e9, 1),
+                   "attention_gather_bytes": att_gather,
+                   "attention_gbs": round(att_bytes / (att_roof_ms / 1e3) / 1e9, 1),
+                   "attention_gather_gbs": round(att_gather / (att_roof_ms / 1e3) / 1e9, 1),
+                   "attention_fetch_bytes_measured": (counters.get("attn_fetch_bytes_per_launch")
+                                                      if counters else None),
+                   "select_bytes": sel_bytes,
+                   "step_bytes": step_bytes,
                    "step_gbs": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
                    "step_frac_of_ceiling": round(step_gbs / ceiling, 4) if ceiling else None,
@@ -715,30 +822,32 @@ def main() -> int:
                                          "qsa_build_metadata + qsa_decode_step" if meta else
                                          "qsa_decode_step_fp8" if fp8 else "qsa_decode_step"),
                    **extra,
-                   "stage_timing": "separate pass: qsa_select and qsa_sparse_attn with events "
-                                   "between them (the records add a few us per stage); "
-                                   "roofline.avg_launch_ms: the roofline call K times back "
-                                   "to back between two events"},
+                   "stage_timing": "select_ms / attention_ms: a separate pass through "
+                                   "qsa_select and qsa_sparse_attn with events between them "
+                                   "(the records add a few us per stage); roofline "
+                                   "avg_launch_ms: each stage's call K times back to back "
+                                   "between two events (attention rotating the KV caches)"},
     }
     if context is not None:
         result["single_row_latency"] = context
-        result["batched_64_rows"] = batched
         result["units_protocol"] = units
         result["gpu_clocks_after_timing"] = clocks
+    status = 0
     if not args.no_cpu_baseline:
-        base = cpu_baseline(w, scale, fp8=fp8, weights=head_w)
-        outs = base.pop("_outs")
-        # the timed configuration's output on the rows the oracle finished
-        same = sum(np.array_equal(sel[0], got_idx[i]) for i, (sel, _) in enumerate(outs))
-        errs = [float(np.max(np.abs(got_out[i].astype(np.float64) - a)))
-                for i, (sel, a) in enumerate(outs) if np.array_equal(sel[0], got_idx[i])]
-        result["cpu_baseline"] = base
-        result["parity"] = {"rows_checked": len(outs), "selection_identical": int(same),
-                            "attention_max_abs_err": max(errs) if errs else None}
-        log(f"oracle: {base['value']:.2f} rows/s, {base['threaded']['value']:.2f} rows/s on "
-            f"{base['host_threads']} threads; identical selections {same}/{len(outs)}")
+        result["cpu_baseline"] = cpu_baseline(w, scale, kind, weights=head_w)
+        base = result["cpu_baseline"]
+        log(f"oracle: {base['value']:.2f} rows/s on one pinned CPU, "
+            f"{base['threaded']['value']:.2f} rows/s on {base['threaded']['cores']} threads")
+        par = parity_all_rows(w, kind, exact, got_idx, got_out, scale, weights=head_w)
+        result["parity"] = par
+        log(f"parity: selection {par['selection_within_rule']}/{par['rows_checked']} within "
+            f"the rule ({par['selection_identical']} identical), attention max abs err "
+            f"{par['attention_max_abs_err']:.2e} over {par['attention_rows_checked']} rows, "
+            f"{par['attention_over_1ulp']} elements over 1 ulp")
+        if not par["ok"]:
+            status = 1
     print(json.dumps(result), flush=True)
-    return 0
+    return status
 
 
 if __name__ == "__main__":

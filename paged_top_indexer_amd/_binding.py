@@ -48,63 +48,70 @@ def descriptor(data_ptr: int, dtype: int, shape, stride) -> QsaTensor:
     return QsaTensor.from_buffer_copy(raw)
 
 
-_lib = None
+_libs: dict = {}
+_current = LIBRARY
 _lock = threading.Lock()
 
 _P = ctypes.POINTER(QsaTensor)
 
 
+def _configure(lib: ctypes.CDLL) -> None:
+    """Argument and result types of every entry point the library exports
+    (a library built from an older revision may lack some)."""
+    sz, i64, vp, f32, i = ctypes.c_size_t, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    sigs = {
+        "qsa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "qsa_last_error": ([], ctypes.c_char_p),
+        "qsa_constants": ([ctypes.POINTER(ctypes.c_int32)] * 4, None),
+        "qsa_select_workspace_bytes": ([i64, i64], sz),
+        "qsa_sparse_attn_workspace_bytes": ([i64], sz),
+        "qsa_decode_step_workspace_bytes": ([i64, i64], sz),
+        "qsa_select": ([_P] * 7 + [vp, sz, vp], i),
+        "qsa_sparse_attn": ([_P] * 4 + [f32, _P, vp, sz, vp], i),
+        "qsa_decode_step": ([_P] * 9 + [f32, _P, _P, vp, sz, vp], i),
+        "qsa_select_fp8": ([_P] * 8 + [vp, sz, vp], i),
+        "qsa_decode_step_fp8": ([_P] * 10 + [f32, _P, _P, vp, sz, vp], i),
+        "qsa_decode_step_noalloc": ([_P] * 9 + [f32, _P, _P, vp], i),
+        "qsa_select_weighted": ([_P] * 9 + [vp, sz, vp], i),
+        "qsa_paged_logits": ([_P] * 9 + [vp], i),
+        "qsa_topk_per_row_workspace_bytes": ([i64, i64], sz),
+        "qsa_topk_per_row": ([_P] * 5 + [vp, sz, vp], i),
+        "qsa_build_metadata_workspace_bytes": ([i64], sz),
+        "qsa_build_metadata": ([_P] * 4 + [i64, i64, i64] + [_P] * 5 + [vp, sz, vp], i),
+        "qsa_read_probe": ([vp, sz, vp, sz, vp], i),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name, None)
+        if fn is not None:
+            fn.argtypes = args
+            fn.restype = res
+
+
 def library() -> ctypes.CDLL:
-    """Load libqsa_amd.so (built by paged_top_indexer_amd.build)."""
-    global _lib
+    """The library the entry points call: libqsa_amd.so (built by
+    paged_top_indexer_amd.build), or the one use_library() selected."""
     with _lock:
-        if _lib is None:
-            if not os.path.exists(LIBRARY):
+        lib = _libs.get(_current)
+        if lib is None:
+            if not os.path.exists(_current):
                 raise RuntimeError(
-                    f"{LIBRARY} is missing: build it with `python -m paged_top_indexer_amd.build` "
+                    f"{_current} is missing: build it with `python -m paged_top_indexer_amd.build` "
                     "(there is no fallback implementation)")
-            lib = ctypes.CDLL(LIBRARY)
-            sz, i64, vp, f32 = ctypes.c_size_t, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
-            lib.qsa_status_string.argtypes = [ctypes.c_int]
-            lib.qsa_status_string.restype = ctypes.c_char_p
-            lib.qsa_last_error.argtypes = []
-            lib.qsa_last_error.restype = ctypes.c_char_p
-            lib.qsa_constants.argtypes = [ctypes.POINTER(ctypes.c_int32)] * 4
-            lib.qsa_constants.restype = None
-            lib.qsa_select_workspace_bytes.argtypes = [i64, i64]
-            lib.qsa_select_workspace_bytes.restype = sz
-            lib.qsa_sparse_attn_workspace_bytes.argtypes = [i64]
-            lib.qsa_sparse_attn_workspace_bytes.restype = sz
-            lib.qsa_decode_step_workspace_bytes.argtypes = [i64, i64]
-            lib.qsa_decode_step_workspace_bytes.restype = sz
-            lib.qsa_select.argtypes = [_P] * 7 + [vp, sz, vp]
-            lib.qsa_select.restype = ctypes.c_int
-            lib.qsa_sparse_attn.argtypes = [_P] * 4 + [f32, _P, vp, sz, vp]
-            lib.qsa_sparse_attn.restype = ctypes.c_int
-            lib.qsa_decode_step.argtypes = [_P] * 9 + [f32, _P, _P, vp, sz, vp]
-            lib.qsa_decode_step.restype = ctypes.c_int
-            lib.qsa_select_fp8.argtypes = [_P] * 8 + [vp, sz, vp]
-            lib.qsa_select_fp8.restype = ctypes.c_int
-            lib.qsa_decode_step_fp8.argtypes = [_P] * 10 + [f32, _P, _P, vp, sz, vp]
-            lib.qsa_decode_step_fp8.restype = ctypes.c_int
-            lib.qsa_decode_step_noalloc.argtypes = [_P] * 9 + [f32, _P, _P, vp]
-            lib.qsa_decode_step_noalloc.restype = ctypes.c_int
-            lib.qsa_select_weighted.argtypes = [_P] * 9 + [vp, sz, vp]
-            lib.qsa_select_weighted.restype = ctypes.c_int
-            lib.qsa_paged_logits.argtypes = [_P] * 9 + [vp]
-            lib.qsa_paged_logits.restype = ctypes.c_int
-            lib.qsa_topk_per_row_workspace_bytes.argtypes = [i64, i64]
-            lib.qsa_topk_per_row_workspace_bytes.restype = sz
-            lib.qsa_topk_per_row.argtypes = [_P] * 5 + [vp, sz, vp]
-            lib.qsa_topk_per_row.restype = ctypes.c_int
-            lib.qsa_build_metadata_workspace_bytes.argtypes = [i64]
-            lib.qsa_build_metadata_workspace_bytes.restype = sz
-            lib.qsa_build_metadata.argtypes = [_P] * 4 + [i64, i64, i64] + [_P] * 5 + [vp, sz, vp]
-            lib.qsa_build_metadata.restype = ctypes.c_int
-            lib.qsa_read_probe.argtypes = [vp, sz, vp, sz, vp]
-            lib.qsa_read_probe.restype = ctypes.c_int
-            _lib = lib
-        return _lib
+            lib = ctypes.CDLL(_current)
+            _configure(lib)
+            _libs[_current] = lib
+        return lib
+
+
+def use_library(path: str | None = None) -> str:
+    """Route the entry points to another build of the library (e.g. the
+    baseline of an A/B comparison; None: back to libqsa_amd.so).  Returns
+    the previous path."""
+    global _current
+    prev = _current
+    _current = os.path.abspath(path) if path else LIBRARY
+    library()
+    return prev
 
 
 def check(status: int) -> None:

@@ -15,13 +15,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PROFILES = os.path.join(ROOT, "profiles")
 WORKLOADS = ["long_context_R128_L131072", "long_context_R128_L131072_fp8",
              "long_context_R128_L131072_two_pass", "multi_token_R256_next4_prefill16",
-             "multi_token_R256_next4_prefill16_metadata"]
+             "multi_token_R256_next4_prefill16_metadata", "batched_R64_shared_pages",
+             "tiny_integer_R1_L519", "saturated_R1_L9215_P8192", "ties_edges_R32_palette64"]
 
 
-def trace_calls(workload: str) -> tuple[dict, int, int]:
+def trace_calls(workload: str) -> tuple[dict, int, int, int]:
     """Kernel name -> calls from the summary table, the number of steps the
-    run made (the sum of the counts in its 'Calls = ...' line) and the number
-    of back-to-back roofline calls after them."""
+    run made (the sum of the counts in its 'Calls = ...' line), and the
+    back-to-back selection and attention calls after them."""
     with open(os.path.join(PROFILES, f"kernel_trace_decode_step_{workload}.md")) as f:
         text = f.read()
     calls = {}
@@ -30,9 +31,10 @@ def trace_calls(workload: str) -> tuple[dict, int, int]:
     protocol = re.search(r"Calls = (\d+) warm-up \+ (\d+) timed .*? \+ (\d+) instrumented "
                          r"steps .*?\+ (\d+) parity step", text, re.S)
     assert protocol, f"{workload}: no call protocol line"
-    roof = re.search(r"plus (\d+) back-to-back roofline calls", text)
-    assert roof, f"{workload}: no roofline calls in the protocol line"
-    return calls, sum(int(g) for g in protocol.groups()), int(roof.group(1))
+    roof = re.search(r"plus (\d+) back-to-back roofline calls \(selection\) and (\d+) "
+                     r"back-to-back attention calls", text)
+    assert roof, f"{workload}: no back-to-back calls in the protocol line"
+    return calls, sum(int(g) for g in protocol.groups()), int(roof.group(1)), int(roof.group(2))
 
 
 @pytest.mark.parametrize("workload", WORKLOADS)
@@ -42,18 +44,26 @@ def test_counters_taken_on_current_sources(workload):
     assert rec["workload"] == workload
     assert rec["source_hash"] == bench.kernel_source_hash(), \
         "kernel sources changed since the counters were taken: profile again"
-    assert bench.stored_traffic(workload) == rec["hbm_bytes_per_launch"] > 0
+    got = bench.stored_counters(workload)
+    assert got is not None and got["hbm_bytes_per_launch"] == rec["hbm_bytes_per_launch"] > 0
+    assert rec["attn_fetch_bytes_per_launch"] > 0
+    cal = rec["copy_calibration"]
+    assert abs(cal["fetch_factor"] - 2.0) < 0.01 and abs(cal["write_factor"] - 1.0) < 0.01
 
 
 @pytest.mark.parametrize("workload", WORKLOADS)
 def test_one_dispatch_per_step(workload):
-    calls, steps, roof = trace_calls(workload)
-    assert calls["qsa_attn_kernel"] == calls["qsa_attn_combine_kernel"] == steps
+    calls, steps, roof, attn_b2b = trace_calls(workload)
+    assert calls["qsa_attn_kernel"] == steps + attn_b2b
+    if "qsa_attn_combine_kernel" in calls:
+        assert calls["qsa_attn_combine_kernel"] == steps + attn_b2b
     chunk = {k: v for k, v in calls.items() if k.startswith("qsa_select_chunk_kernel<")}
-    # a selection is one chunk launch and one merge launch; the paged-logits
-    # form (second template argument true) writes the matrix and has no merge
+    # a selection over several chunks per row is one chunk launch and one
+    # merge launch; the paged-logits form (second template argument true)
+    # writes the matrix and has no merge
     selecting = sum(v for k, v in chunk.items() if k.split(",")[1].strip() == "false")
-    assert calls["qsa_select_merge_kernel"] == selecting
+    if "qsa_select_merge_kernel" in calls:
+        assert calls["qsa_select_merge_kernel"] == selecting
     if workload.endswith("_two_pass"):
         assert chunk["qsa_select_chunk_kernel<0, true, 1>"] == steps + roof
         assert chunk["qsa_select_chunk_kernel<2, false, 1>"] == steps
