@@ -71,7 +71,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # used only while their hash matches the one it was taken on)
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
                   for f in ("qsa_select.hip", "qsa_attn.hip", "qsa_device.h", "qsa_launch.h",
-                            "qsa_select_plan.cpp", "qsa_capi.cpp")]
+                            "qsa_plan.cpp")]
 
 # --workload name -> (builder, integer inputs: the selection is checked
 # bit-exact; else by the band rule)
@@ -167,16 +167,33 @@ def stored_counters(workload: str):
 
 
 def read_ceiling(torch, qsa, dev, gib: int = 2, reps: int = 5) -> float:
-    """The box's practical HBM read ceiling (GB/s): qsa_read_probe streaming
-    `gib` GiB with nontemporal loads, `reps` times between HIP events."""
+    """The box's practical HBM read ceiling (GB/s): qsa_read_probe of
+    libqsa_probe.so (include/qsa_probe.h, a measurement aid built apart from
+    the method's library) streaming `gib` GiB with nontemporal loads, `reps`
+    times between HIP events."""
+    import ctypes
+
+    from paged_top_indexer_amd import build
+
+    lib = ctypes.CDLL(build.PROBE_LIBRARY)
+    lib.qsa_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
+    lib.qsa_read_probe.restype = ctypes.c_int
     buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    qsa.qsa_read_probe(buf, sink)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     stream = torch.cuda.current_stream(dev)
+
+    def probe():
+        rc = lib.qsa_read_probe(buf.data_ptr(), buf.numel(), sink.data_ptr(), 4,
+                                stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"qsa_read_probe failed with status {rc}")
+
+    probe()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
     for _ in range(reps):
-        qsa.qsa_read_probe(buf, sink)
+        probe()
     ev[1].record(stream)
     torch.cuda.synchronize()
     gbs = (gib << 30) * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9

@@ -411,17 +411,6 @@ QSA_API int qsa_build_metadata(const qsa_tensor* query_start_loc, const qsa_tens
                                const qsa_tensor* k_work_metadata, void* workspace,
                                size_t workspace_bytes, qsa_stream stream);
 
-/*
- * qsa_read_probe -- a measurement aid, not part of the method: one plain
- * streaming read of `bytes` bytes at `data` (device memory, 16-byte
- * aligned, a multiple of 16 bytes) with coalesced nontemporal loads, the
- * practical HBM read ceiling the bench reports beside the 8 TB/s peak.
- * `sink` (device, >= 4 aligned bytes, not overlapping `data`) may receive
- * one word.  Asynchronous on `stream`; errors as for the other entry points.
- */
-QSA_API int qsa_read_probe(const void* data, size_t bytes, void* sink, size_t sink_bytes,
-                           qsa_stream stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,6 @@ from ._binding import (  # noqa: F401
     qsa_decode_step_fp8,
     qsa_decode_step_noalloc,
     qsa_paged_logits,
-    qsa_read_probe,
     qsa_select,
     qsa_select_fp8,
     qsa_select_weighted,

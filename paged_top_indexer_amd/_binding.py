@@ -78,7 +78,6 @@ def _configure(lib: ctypes.CDLL) -> None:
         "qsa_topk_per_row": ([_P] * 5 + [vp, sz, vp], i),
         "qsa_build_metadata_workspace_bytes": ([i64], sz),
         "qsa_build_metadata": ([_P] * 4 + [i64, i64, i64] + [_P] * 5 + [vp, sz, vp], i),
-        "qsa_read_probe": ([vp, sz, vp, sz, vp], i),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name, None)
@@ -424,14 +423,3 @@ def qsa_build_metadata(query_start_loc, seq_lens, block_table, num_tokens: int,
                                  _opt(o.get("slot_mapping")), _opt(o.get("k_work")), ws, ws_bytes,
                                  ctypes.c_void_p(sh)))
     return o
-
-
-def qsa_read_probe(data, sink, stream=None) -> None:
-    """One streaming read of the device tensor ``data`` (the practical HBM
-    read ceiling; a measurement aid).  ``sink``: a device tensor of >= 4
-    bytes."""
-    lib = library()
-    sh = _stream(stream, data.device)
-    check(lib.qsa_read_probe(ctypes.c_void_p(data.data_ptr()), data.numel() * data.element_size(),
-                             ctypes.c_void_p(sink.data_ptr()), sink.numel() * sink.element_size(),
-                             ctypes.c_void_p(sh)))

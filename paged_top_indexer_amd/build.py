@@ -20,13 +20,15 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIBRARY = os.path.join(HERE, "libqsa_amd.so")
+# the read-ceiling probe, a measurement aid built apart from the method
+PROBE_LIBRARY = os.path.join(HERE, "libqsa_probe.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["qsa_select.hip", "qsa_attn.hip", "qsa_metadata.hip", "qsa_noalloc.hip",
-               "qsa_probe.hip"]
-HOST_SOURCES = ["qsa_capi.cpp", "qsa_select_plan.cpp"]
+HIP_SOURCES = ["qsa_select.hip", "qsa_attn.hip", "qsa_metadata.hip", "qsa_noalloc.hip"]
+PROBE_SOURCE = "qsa_probe.hip"
+HOST_SOURCES = ["qsa_capi.cpp", "qsa_plan.cpp"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -61,9 +63,14 @@ def build(verbose: bool = False, csrc: str = CSRC, include: str | None = None,
     inc = [f"-I{include}"] if include else []
     if csrc == CSRC:
         hip, host = HIP_SOURCES, HOST_SOURCES
+        probe = os.path.join(build_dir, PROBE_SOURCE + ".o")
+        _run([HIPCC, *HIP_FLAGS, "-c", os.path.join(csrc, PROBE_SOURCE), "-o", probe], verbose)
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", PROBE_LIBRARY + ".tmp",
+              probe], verbose)
+        os.replace(PROBE_LIBRARY + ".tmp", PROBE_LIBRARY)
     else:  # another revision's tree: whatever sources it has
         names = sorted(os.listdir(csrc))
-        hip = [n for n in names if n.endswith(".hip")]
+        hip = [n for n in names if n.endswith(".hip") and n != PROBE_SOURCE]
         host = [n for n in names if n.endswith(".cpp")]
     jobs = []
     objs = []

@@ -339,33 +339,6 @@ int64_t plan_groups(const qsa::SelectPlan& plan, int64_t rows) {
 
 }  // namespace
 
-namespace qsa {
-
-
-// Split length: enough splits for about one resident round of attention
-// workgroups over the batch (3 per CU on 256 CUs), in multiples of 64 index
-// positions (each wave loads its indices 64 at a time), at most 33 splits of
-// 64 positions; a batch of 768 rows or more gets one split per row.
-AttnPlan plan_attn(int64_t rows) {
-  AttnPlan p;
-  constexpr int64_t kResident = 768;
-  const int64_t want =
-      rows > 0 ? std::min<int64_t>(kMaxAttnSplits, std::max<int64_t>(1, (kResident + rows - 1) / rows))
-               : 1;
-  p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
-  p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
-  // (at most kMaxAttnSplits: the combine kernel holds every split's weight)
-  if (rows == 0) return p;
-  size_t off = 0;
-  p.partial_off = off;
-  off = align256(off + (size_t)rows * p.splits * kAttHeads * kAttDim * sizeof(float));
-  p.stats_off = off;
-  off = align256(off + (size_t)rows * p.splits * kAttHeads * 2 * sizeof(float));
-  p.bytes = p.splits > 1 ? off : 0;
-  return p;
-}
-
-}  // namespace qsa
 
 namespace {
 
@@ -842,28 +815,6 @@ QSA_API int qsa_build_metadata(const qsa_tensor* query_start_loc, const qsa_tens
   a.circular_buffer_size = circular_buffer_size;
   const int err = qsa::launch_metadata(a, stream);
   if (err) return fail(QSA_ERR_LAUNCH, "metadata launch failed (hipError %d)", err);
-  return QSA_OK;
-}
-
-QSA_API int qsa_read_probe(const void* data, size_t bytes, void* sink, size_t sink_bytes,
-                           qsa_stream stream) {
-  g_last_error[0] = '\0';
-  if (!data || !sink) return fail(QSA_ERR_NULL, "read probe: data and sink must be non-NULL");
-  if (reinterpret_cast<uintptr_t>(data) % 16 || bytes % 16) {
-    return fail(QSA_ERR_LAYOUT, "read probe: data must be 16-byte aligned and a multiple of 16 bytes");
-  }
-  if (reinterpret_cast<uintptr_t>(sink) % 4 || sink_bytes < 4) {
-    return fail(QSA_ERR_WORKSPACE, "read probe: sink needs 4 aligned bytes");
-  }
-  Span d, k;
-  d.lo = reinterpret_cast<uintptr_t>(data);
-  d.hi = d.lo + bytes;
-  k.lo = reinterpret_cast<uintptr_t>(sink);
-  k.hi = k.lo + 4;
-  if (overlaps(d, k)) return fail(QSA_ERR_ALIAS, "read probe: sink overlaps data");
-  if (bytes == 0) return QSA_OK;
-  const int err = qsa::launch_read_probe(data, (int64_t)bytes, static_cast<uint32_t*>(sink), stream);
-  if (err) return fail(QSA_ERR_LAUNCH, "read probe launch failed (hipError %d)", err);
   return QSA_OK;
 }
 

@@ -141,7 +141,6 @@ struct MetaArgs {
 int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_metadata(const MetaArgs& a, void* stream);
-int launch_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
 
 // Device address of the calling thread's current device's fixed scratch

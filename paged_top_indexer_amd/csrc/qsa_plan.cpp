@@ -1,7 +1,7 @@
-// qsa_select_plan.cpp -- launch plan of the selection (host-only C++):
-// chunk size, grid shape and the candidate area of the workspace.  Kept
-// apart from the validation code because it fixes the selection kernels'
-// memory traffic.
+// qsa_plan.cpp -- launch plans of the two stages (host-only C++): the
+// selection's chunk size, grid shape and candidate area, and the attention's
+// split length and partials.  Kept apart from the validation code because
+// they fix the kernels' memory traffic.
 #include <algorithm>
 #include <cstddef>
 #include <cstdint>
@@ -46,6 +46,30 @@ SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
   p.blocks_off = off;
   off = align256(off + cands * sizeof(uint32_t));
   p.bytes = off;
+  return p;
+}
+
+// Split length: enough splits for about one resident round of attention
+// workgroups over the batch (3 per CU on 256 CUs), in multiples of 64 index
+// positions (each wave loads its indices 64 at a time), at most 33 splits of
+// 64 positions; a batch of 768 rows or more gets one split per row.
+AttnPlan plan_attn(int64_t rows) {
+  AttnPlan p;
+  constexpr int64_t kResident = 768;
+  const int64_t want =
+      rows > 0 ? std::min<int64_t>(kMaxAttnSplits,
+                                   std::max<int64_t>(1, (kResident + rows - 1) / rows))
+               : 1;
+  p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
+  p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
+  // (at most kMaxAttnSplits: the combine kernel holds every split's weight)
+  if (rows == 0) return p;
+  size_t off = 0;
+  p.partial_off = off;
+  off = align256(off + (size_t)rows * p.splits * kAttHeads * kAttDim * sizeof(float));
+  p.stats_off = off;
+  off = align256(off + (size_t)rows * p.splits * kAttHeads * 2 * sizeof(float));
+  p.bytes = p.splits > 1 ? off : 0;
   return p;
 }
 

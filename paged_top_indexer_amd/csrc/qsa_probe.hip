@@ -1,6 +1,7 @@
-// qsa_probe.hip -- a plain streaming-read kernel: the practical HBM read
-// ceiling of the box, measured beside the path's own kernels.  Not part of
-// the method; it gives the roofline a second, measured denominator.
+// qsa_probe.hip -- libqsa_probe.so (include/qsa_probe.h): a plain
+// streaming-read kernel, the practical HBM read ceiling of the box, measured
+// beside the path's own kernels.  Not part of the method and not linked into
+// its library; it gives the roofline a second, measured denominator.
 //
 // Each workgroup streams a contiguous span with nontemporal 16-byte loads
 // (each load instruction reads 1 KiB contiguous per wave, eight in flight
@@ -11,9 +12,8 @@
 
 #include <cstdint>
 
-#include "qsa_launch.h"
+#include "../../include/qsa_probe.h"
 
-namespace qsa {
 namespace {
 
 constexpr int kProbeThreads = 256;
@@ -46,11 +46,16 @@ __global__ __launch_bounds__(kProbeThreads) void qsa_read_probe_kernel(const u32
 
 }  // namespace
 
-int launch_read_probe(const void* data, int64_t bytes, uint32_t* sink, void* stream) {
+extern "C" QSA_API int qsa_read_probe(const void* data, size_t bytes, void* sink,
+                                      size_t sink_bytes, qsa_stream stream) {
+  const uintptr_t d = reinterpret_cast<uintptr_t>(data), k = reinterpret_cast<uintptr_t>(sink);
+  if (!data || !sink) return QSA_ERR_NULL;
+  if (d % 16 || bytes % 16) return QSA_ERR_LAYOUT;
+  if (k % 4 || sink_bytes < 4) return QSA_ERR_WORKSPACE;
+  if (k < d + bytes && d < k + 4) return QSA_ERR_ALIAS;
+  if (bytes == 0) return QSA_OK;
   hipLaunchKernelGGL(qsa_read_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(data),
-                     bytes / 16, sink);
-  return (int)hipGetLastError();
+                     (int64_t)(bytes / 16), static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH;
 }
-
-}  // namespace qsa

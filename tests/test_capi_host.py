@@ -547,8 +547,29 @@ def test_launch_size_limits():
     assert B.sparse_attn_workspace_bytes(767) > 0 and B.sparse_attn_workspace_bytes(768) == 0
 
 
+def probe_library():
+    from paged_top_indexer_amd import build
+
+    lib = ctypes.CDLL(build.PROBE_LIBRARY)
+    lib.qsa_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_size_t, ctypes.c_void_p]
+    lib.qsa_read_probe.restype = ctypes.c_int
+    return lib
+
+
+def test_read_probe_is_apart_from_the_method():
+    """The read-ceiling probe is a measurement aid: exported by
+    libqsa_probe.so as include/qsa_probe.h declares, absent from the method's
+    library and header."""
+    assert not hasattr(B.library(), "qsa_read_probe")
+    assert "qsa_read_probe" not in declared_symbols()
+    text = open(os.path.join(ROOT, "include", "qsa_probe.h")).read()
+    assert re.findall(r"QSA_API\s+[\w\s\*]+?\b(qsa_\w+)\s*\(", text) == ["qsa_read_probe"]
+    assert hasattr(probe_library(), "qsa_read_probe")
+
+
 def test_read_probe_checks():
-    lib = B.library()
+    lib = probe_library()
     f = Fake()
     d, k = f.alloc(1 << 20), f.alloc(64)
     assert lib.qsa_read_probe(None, 1 << 20, ctypes.c_void_p(k), 4, None) == NULL
@@ -561,8 +582,9 @@ def test_read_probe_checks():
 
 @pytest.mark.parametrize("lang", ["c99", "c++17"])
 def test_header_compiles_standalone(lang, tmp_path):
-    """include/qsa.h needs no HIP header and compiles on its own as C99 and
-    as C++17 (a C caller includes it as is)."""
+    """include/qsa.h (and the probe's qsa_probe.h) need no HIP header and
+    compile on their own as C99 and as C++17 (a C caller includes them as
+    they are)."""
     import shutil
     import subprocess
 
@@ -570,8 +592,10 @@ def test_header_compiles_standalone(lang, tmp_path):
     if shutil.which(compiler) is None:
         pytest.skip(f"{compiler} not found")
     src = tmp_path / ("use.c" if lang == "c99" else "use.cpp")
-    src.write_text('#include "qsa.h"\nint main(void) { int32_t w; qsa_constants(0, 0, &w, 0); '
-                   'return w == QSA_OUT_WIDTH ? 0 : 1; }\n')
+    src.write_text('#include "qsa.h"\n#include "qsa_probe.h"\n'
+                   'int main(void) { int32_t w; qsa_constants(0, 0, &w, 0); '
+                   'int (*probe)(const void*, size_t, void*, size_t, qsa_stream) = qsa_read_probe; '
+                   '(void)probe; return w == QSA_OUT_WIDTH ? 0 : 1; }\n')
     res = subprocess.run([compiler, f"-std={lang}", "-Wall", "-Wextra", "-Werror", "-pedantic",
                           "-fsyntax-only", f"-I{os.path.join(ROOT, 'include')}", str(src)],
                          capture_output=True, text=True)

@@ -1,4 +1,4 @@
-"""Each planted mistake in the oracle must be caught by at least one pin.
+"""Each planted mistake in the oracle must be caught by at least two pins.
 
 The oracle source carries twenty compile-time mutants (a dropped term, a wrong
 sign, an off-by-one, a transposed operand, ...).  Building each one and
@@ -43,7 +43,8 @@ def test_mutant_is_caught(tmp_path, mutant):
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(orc)
-        except (AssertionError, ValueError) as e:
+        except (AssertionError, ValueError):
             caught.append(pin.__name__)
-            break
-    assert caught, f"no pin catches mutant {mutant} ({MUTANTS[mutant]})"
+            if len(caught) == 2:
+                break
+    assert len(caught) >= 2, f"mutant {mutant} ({MUTANTS[mutant]}) caught only by {caught}"
