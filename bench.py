@@ -645,19 +645,32 @@ def main() -> int:
             k, v = kv_views[i % len(kv_views)]
             decode_fn(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
 
+    def timed_steps(lead_in: bool) -> float:
+        """ms per step over exactly K decode steps between two events, after a
+        synchronisation.  lead_in: a ~0.2 ms device sleep is queued between
+        the synchronisation and the start event, so the timed region opens
+        with the first step already queued -- otherwise it also holds the
+        host's first launch (marshalling, the launch path) on an idle GPU, a
+        fixed ~0.1 ms that a short region spreads over its few steps."""
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        if lead_in:
+            torch.cuda._sleep(500_000)  # GPU clock cycles (~0.2 ms)
+        ev[0].record(stream)
+        for i in range(args.steps):
+            step(i)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / args.steps
+
     # warm-up, then exactly K timed decode steps (events only at the ends)
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    t_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     t_start = time.perf_counter()
-    t_ev[0].record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_ev[1].record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed_steps(lead_in=True)
     wall = time.perf_counter() - t_start
-    ms_per_step = t_ev[0].elapsed_time(t_ev[1]) / args.steps
+    # the same K steps with the region opening on an idle GPU, for reference
+    ms_per_step_cold = timed_steps(lead_in=False)
     clocks = None if args.no_context else gpu_clocks()
 
     # Per-stage times: the same two stages through their own entry points,
@@ -710,7 +723,8 @@ def main() -> int:
         torch.cuda.synchronize()
         extra["select_row_by_row_ms"] = round(flat_ev[0].elapsed_time(flat_ev[1]) / args.steps, 4)
         log(f"selection row by row {extra['select_row_by_row_ms']:.4f} ms")
-    log(f"step {ms_per_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms); stages: select "
+    log(f"step {ms_per_step:.4f} ms (cold start {ms_per_step_cold:.4f} ms; wall "
+        f"{wall * 1e3 / args.steps:.4f} ms); stages: select "
         f"{np.mean(sel_ms):.4f} ms (min {np.min(sel_ms):.4f}), attention {np.mean(att_ms):.4f} ms")
 
     # one more step on the first KV cache (the oracle's) for the parity check
@@ -834,6 +848,7 @@ def main() -> int:
                    "step_gbs": round(step_gbs, 1),
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
                    "step_frac_of_ceiling": round(step_gbs / ceiling, 4) if ceiling else None,
+                   "ms_per_step_cold_start": round(ms_per_step_cold, 4),
                    "timed_entry_point": ("qsa_paged_logits + qsa_topk_per_row + qsa_sparse_attn"
                                          if two_pass else
                                          "qsa_build_metadata + qsa_decode_step" if meta else

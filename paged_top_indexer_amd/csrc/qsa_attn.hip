@@ -34,9 +34,8 @@
 namespace qsa {
 namespace {
 
-constexpr int kThreads = kAttnThreads;
-constexpr int kWaves = kThreads / 64;
-static_assert(kCombineThreads == kThreads, "the combine kernel's thread e owns dim e");
+constexpr int kThreads = kAttnThreads;  // the split kernel's 4 waves, and the combine's threads
+static_assert(kCombineThreads == kAttnThreads, "the combine kernel's thread e owns dim e");
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -55,6 +54,7 @@ struct AttnParams {
   int split_positions;
 };
 
+template <int kWaves>
 struct Smem {
   float o[kWaves][kAttHeads][kAttDim];
   float m[kWaves][kAttHeads];
@@ -67,8 +67,11 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
-  __shared__ Smem sm;
+// kWaves waves per workgroup: 4 for splits of a row (kAttnThreads), or
+// kAttnRowWaves when one workgroup takes a whole row (no combine).
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void qsa_attn_kernel(AttnParams p) {
+  __shared__ Smem<kWaves> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -201,10 +204,10 @@ __global__ __launch_bounds__(kThreads) void qsa_attn_kernel(AttnParams p) {
     for (int e = 0; e < 4; ++e) sm.o[wave][h][4 * lane + e] = o[h][e];
   __syncthreads();
 
-  // merge the 4 waves: thread tid owns dim tid of every head
-  const int e = tid;
+  // merge the waves: thread t owns (head, dim) pairs t, t + 64 kWaves, ...
 #pragma unroll
-  for (int h = 0; h < kAttHeads; ++h) {
+  for (int he = tid; he < kAttHeads * kAttDim; he += 64 * kWaves) {
+    const int h = he / kAttDim, e = he % kAttDim;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][h]);
@@ -293,8 +296,15 @@ int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
   p.splits = plan.splits;
   p.split_positions = plan.split_positions;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(qsa_attn_kernel, dim3((unsigned)(padded_rows(a.rows) * plan.splits)),
-                     dim3(kThreads), 0, s, p);
+  if (plan.waves == kAttnRowWaves) {
+    hipLaunchKernelGGL(qsa_attn_kernel<kAttnRowWaves>,
+                       dim3((unsigned)(padded_rows(a.rows) * plan.splits)),
+                       dim3(64 * kAttnRowWaves), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(qsa_attn_kernel<kAttnThreads / 64>,
+                       dim3((unsigned)(padded_rows(a.rows) * plan.splits)), dim3(kAttnThreads),
+                       0, s, p);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return (int)err;
   hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)(padded_rows(a.rows) * kAttHeads)),

@@ -38,6 +38,9 @@ constexpr int kCombineThreads = 256;
 // and the combine kernel keeps one weight per split in LDS.
 constexpr int kMaxAttnSplits = (kOutWidth + 63) / 64;  // 33 splits of 64 positions
 constexpr int kCombineMaxSplits = 64;
+// Waves of a workgroup that takes a whole row of index positions (3 per
+// SIMD, the split kernel's occupancy).
+constexpr int kAttnRowWaves = 12;
 static_assert(kMaxAttnSplits <= kCombineMaxSplits, "combine holds every split's weight");
 
 // Bytes of the fixed device scratch of the no-allocation decode step (one
@@ -77,10 +80,13 @@ struct SelectPlan {
 SelectPlan plan_select(int64_t rows, int64_t table_width, int group = 1);
 
 // Launch plan of the attention kernel: `splits` workgroups per row, each
-// covering `split_positions` index positions (4 waves x tiles of 16).
+// covering `split_positions` index positions with `waves` waves (tiles of
+// 16 positions): 4 waves per split, or kAttnRowWaves when one workgroup
+// takes a whole row.
 struct AttnPlan {
   int split_positions = 128;
   int splits = 1;
+  int waves = 4;
   size_t partial_off = 0;  // [rows][splits][3][256] fp32 unnormalised outputs
   size_t stats_off = 0;    // [rows][splits][3][2] fp32 (running max, sum)
   size_t bytes = 0;

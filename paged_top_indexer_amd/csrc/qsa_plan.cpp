@@ -62,6 +62,16 @@ AttnPlan plan_attn(int64_t rows) {
                : 1;
   p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
   p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
+  if (rows >= 64 && rows <= 256) {
+    // 64-256 rows: about one workgroup of kAttnRowWaves waves per CU
+    // (splits = 256 / rows), each wave a whole number of 16-position tiles;
+    // 256 rows take one workgroup per row and need no combine
+    constexpr int kUnit = 16 * kAttnRowWaves;
+    const int splits = (int)std::max<int64_t>(1, 256 / rows);
+    p.waves = kAttnRowWaves;
+    p.split_positions = kUnit * ((kOutWidth + splits * kUnit - 1) / (splits * kUnit));
+    p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
+  }
   // (at most kMaxAttnSplits: the combine kernel holds every split's weight)
   if (rows == 0) return p;
   size_t off = 0;

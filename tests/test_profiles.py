@@ -54,7 +54,9 @@ def test_counters_taken_on_current_sources(workload):
 @pytest.mark.parametrize("workload", WORKLOADS)
 def test_one_dispatch_per_step(workload):
     calls, steps, roof, attn_b2b = trace_calls(workload)
-    assert calls["qsa_attn_kernel"] == steps + attn_b2b
+    # the attention kernel runs as one instantiation (<4> or <12> waves) per shape
+    attn = [v for k, v in calls.items() if k.startswith("qsa_attn_kernel<")]
+    assert attn == [steps + attn_b2b]
     if "qsa_attn_combine_kernel" in calls:
         assert calls["qsa_attn_combine_kernel"] == steps + attn_b2b
     chunk = {k: v for k, v in calls.items() if k.startswith("qsa_select_chunk_kernel<")}
