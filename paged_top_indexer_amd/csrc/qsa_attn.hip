@@ -30,6 +30,7 @@
 
 #include "qsa_device.h"
 #include "qsa_launch.h"
+#include "qsa_topk.h"
 
 namespace qsa {
 namespace {
@@ -44,7 +45,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 struct AttnParams {
   const uint16_t* q;
   const uint16_t* kv;
-  const int32_t* indices;
+  int32_t* indices;  // read; written for multi-chunk rows by the fused path
   uint16_t* out;
   float* partial;  // [rows][splits][3][256]
   float* stats;    // [rows][splits][3][2]
@@ -52,14 +53,133 @@ struct AttnParams {
   float scale_log2;
   int splits;
   int split_positions;
+  FusedSelect sel;  // the fused path's selection inputs
 };
 
 template <int kWaves>
-struct Smem {
+struct AttnPart {
   float o[kWaves][kAttHeads][kAttDim];
   float m[kWaves][kAttHeads];
   float l[kWaves][kAttHeads];
 };
+
+// The selection prologue's LDS (the merge kernel's work for one row).
+template <int NT>
+struct SelPart {
+  uint32_t keys[kFusedCands];
+  uint32_t blocks[kFusedCands];
+  uint64_t sorted[kTopKBlocks];
+  alignas(16) uint32_t hist0[kBins];
+  alignas(16) uint32_t hist1[kBins];
+  uint32_t red_and[NT / 64], red_or[NT / 64];
+  Scratch s;
+};
+
+template <int kWaves, bool kSelect>
+struct Smem {
+  AttnPart<kWaves> att;
+  __device__ AttnPart<kWaves>& part() { return att; }
+};
+
+template <int kWaves>
+struct Smem<kWaves, true> {
+  union {
+    AttnPart<kWaves> att;
+    SelPart<64 * kWaves> sel;
+  } u;
+  int32_t idx[kOutWidth + 1];  // the row's selected index list
+  __device__ AttnPart<kWaves>& part() { return u.att; }
+};
+
+// The index row of a multi-chunk row, selected from the chunk kernel's
+// candidates exactly as the merge kernel selects it: the top
+// min(512, V) (score descending, block ascending) of the chunks' best keys,
+// expanded to tokens with the tail and -1 padding, into idx (LDS).  The
+// candidates' shared leading key bits are shifted out before the radix
+// select (same order, same ties).  All NT threads call; ends with a barrier.
+template <int NT>
+__device__ void select_row(const FusedSelect& f, int64_t r, const Row& row, SelPart<NT>& sm,
+                           int32_t* idx) {
+  const int tid = threadIdx.x;
+  const int last_n = (int)(row.visible - (row.nchunks - 1) * f.chunk_blocks);
+  const int m = (int)((row.nchunks - 1) * f.cand_cap) + min(f.cand_cap, last_n);
+  const int k = (int)min((int64_t)kTopKBlocks, row.visible);
+  const uint32_t* ckeys = f.cand_keys + r * f.chunks_per_row * f.cand_cap;
+  const uint32_t* cblocks = f.cand_blocks + r * f.chunks_per_row * f.cand_cap;
+  for (int i = tid; i < kBins; i += NT) sm.hist0[i] = 0;
+  // 16-byte loads (a row's list starts 256-byte aligned; cand_cap is a
+  // multiple of 4), two in flight per thread, with the AND and OR of the keys
+  uint32_t kand = 0xFFFFFFFFu, kor = 0;
+  constexpr int kLoadUnroll = 2;
+  const int m4 = m >> 2;
+  const uint4* k4 = reinterpret_cast<const uint4*>(ckeys);
+  const uint4* b4 = reinterpret_cast<const uint4*>(cblocks);
+  for (int j0 = tid; j0 < m4; j0 += NT * kLoadUnroll) {
+    uint4 kv[kLoadUnroll], bv[kLoadUnroll];
+#pragma unroll
+    for (int u = 0; u < kLoadUnroll; ++u) {
+      const int j = j0 + u * NT;
+      if (j < m4) {
+        kv[u] = k4[j];
+        bv[u] = b4[j];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kLoadUnroll; ++u) {
+      const int j = j0 + u * NT;
+      if (j < m4) {
+        const uint32_t xs[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+        const uint32_t bs[4] = {bv[u].x, bv[u].y, bv[u].z, bv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sm.keys[4 * j + e] = xs[e];
+          sm.blocks[4 * j + e] = bs[e];
+          kand &= xs[e];
+          kor |= xs[e];
+        }
+      }
+    }
+  }
+  for (int i = 4 * m4 + tid; i < m; i += NT) {
+    const uint32_t x = ckeys[i];
+    sm.keys[i] = x;
+    sm.blocks[i] = cblocks[i];
+    kand &= x;
+    kor |= x;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
+    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    sm.red_and[tid >> 6] = kand;
+    sm.red_or[tid >> 6] = kor;
+  }
+  __syncthreads();
+  uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    all_and &= sm.red_and[w];
+    all_or |= sm.red_or[w];
+  }
+  const uint32_t differ = all_and ^ all_or;
+  const int shift = differ ? __builtin_clz(differ) : 0;  // bits every key shares
+  auto lds_key = [&](int i) { return sm.keys[i] << shift; };
+  auto block_of = [&](int i) { return sm.blocks[i]; };
+  uint32_t T = 0, bcut = 0xFFFFFFFFu;
+  if (m > k) {
+    for (int i = tid; i < m; i += NT) atomicAdd(&sm.hist0[digit0(lds_key(i))], 1u);
+    __syncthreads();
+    topk_threshold<NT>(lds_key, block_of, m, k, sm.s, sm.hist0, sm.hist1, T, bcut);
+  }
+  compact_topk<NT>(
+      lds_key, block_of, m, T, bcut,
+      [&](uint32_t slot, int i, uint32_t) { sm.sorted[slot] = pack(sm.keys[i], sm.blocks[i]); },
+      sm.s);
+  sort_expand_write(sm.sorted, k, row.visible, row.tail, idx, sm.sorted);
+  __syncthreads();
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -68,10 +188,16 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
 }
 
 // kWaves waves per workgroup: 4 for splits of a row (kAttnThreads), or
-// kAttnRowWaves when one workgroup takes a whole row (no combine).
-template <int kWaves>
+// kAttnRowWaves for about one workgroup per CU.  kSelect (the fused decode
+// step): a multi-chunk row's index list is first selected here from the
+// chunk kernel's candidates (every split of the row computes the same
+// list; the row's last split also writes it out as the index row), then
+// the split attends over its positions of that list, exactly as over the
+// index row.
+template <int kWaves, bool kSelect>
 __global__ __launch_bounds__(64 * kWaves) void qsa_attn_kernel(AttnParams p) {
-  __shared__ Smem<kWaves> sm;
+  __shared__ Smem<kWaves, kSelect> sm;
+  AttnPart<kWaves>& att = sm.part();
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -93,10 +219,24 @@ __global__ __launch_bounds__(64 * kWaves) void qsa_attn_kernel(AttnParams p) {
     }
   }
 
+  const int32_t* idx_row = p.indices + r * kOutWidth;
+  if constexpr (kSelect) {
+    const Row row = row_extent(p.sel.token_to_req, p.sel.num_reqs, p.sel.seq_lens,
+                               p.sel.query_pos, p.sel.max_visible, p.sel.chunk_blocks, r);
+    if (row.nchunks > 1) {  // uniform: rows of one chunk were finished by the chunk kernel
+      select_row<64 * kWaves>(p.sel, r, row, sm.u.sel, sm.idx);
+      if (split == p.splits - 1) {
+        for (int i = tid; i < kOutWidth; i += 64 * kWaves) {
+          p.indices[r * kOutWidth + i] = sm.idx[i];
+        }
+      }
+      idx_row = sm.idx;
+    }
+  }
+
   const int wave_positions = p.split_positions / kWaves;
   const int pos_begin = split * p.split_positions + wave * wave_positions;
   const int pos_end = min(kOutWidth, pos_begin + wave_positions);
-  const int32_t* idx_row = p.indices + r * kOutWidth;
   // The wave's indices come 64 at a time, one per lane, the next 64 loaded
   // while the current ones are used: a tile's gathers wait only for their
   // own data.
@@ -195,13 +335,13 @@ __global__ __launch_bounds__(64 * kWaves) void qsa_attn_kernel(AttnParams p) {
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (lane < kAttHeads) {
-    sm.m[wave][lane] = m_run;
-    sm.l[wave][lane] = l_run;
+    att.m[wave][lane] = m_run;
+    att.l[wave][lane] = l_run;
   }
 #pragma unroll
   for (int h = 0; h < kAttHeads; ++h)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.o[wave][h][4 * lane + e] = o[h][e];
+    for (int e = 0; e < 4; ++e) att.o[wave][h][4 * lane + e] = o[h][e];
   __syncthreads();
 
   // merge the waves: thread t owns (head, dim) pairs t, t + 64 kWaves, ...
@@ -210,14 +350,14 @@ __global__ __launch_bounds__(64 * kWaves) void qsa_attn_kernel(AttnParams p) {
     const int h = he / kAttDim, e = he % kAttDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, att.m[w][h]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float f = exp2_fast(sm.m[w][h] - M);
-        L = fmaf(f, sm.l[w][h], L);
-        O = fmaf(f, sm.o[w][h][e], O);
+        const float f = exp2_fast(att.m[w][h] - M);
+        L = fmaf(f, att.l[w][h], L);
+        O = fmaf(f, att.o[w][h][e], O);
       }
     }
     if (p.splits == 1) {
@@ -285,7 +425,8 @@ int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
   AttnParams p;
   p.q = a.q;
   p.kv = a.kv;
-  p.indices = a.indices;
+  p.indices = const_cast<int32_t*>(a.indices);
+  if (a.fused) p.sel = *a.fused;
   p.out = a.out;
   char* ws = static_cast<char*>(a.workspace);
   p.partial = plan.bytes ? reinterpret_cast<float*>(ws + plan.partial_off) : nullptr;
@@ -296,12 +437,16 @@ int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
   p.splits = plan.splits;
   p.split_positions = plan.split_positions;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (plan.waves == kAttnRowWaves) {
-    hipLaunchKernelGGL(qsa_attn_kernel<kAttnRowWaves>,
+  if (plan.waves == kAttnRowWaves && a.fused) {
+    hipLaunchKernelGGL((qsa_attn_kernel<kAttnRowWaves, true>),
+                       dim3((unsigned)(padded_rows(a.rows) * plan.splits)),
+                       dim3(64 * kAttnRowWaves), 0, s, p);
+  } else if (plan.waves == kAttnRowWaves) {
+    hipLaunchKernelGGL((qsa_attn_kernel<kAttnRowWaves, false>),
                        dim3((unsigned)(padded_rows(a.rows) * plan.splits)),
                        dim3(64 * kAttnRowWaves), 0, s, p);
   } else {
-    hipLaunchKernelGGL(qsa_attn_kernel<kAttnThreads / 64>,
+    hipLaunchKernelGGL((qsa_attn_kernel<kAttnThreads / 64, false>),
                        dim3((unsigned)(padded_rows(a.rows) * plan.splits)), dim3(kAttnThreads),
                        0, s, p);
   }

@@ -456,7 +456,26 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   qsa::SelectArgs s;
   fill_select_args(s, q_sel, nullptr, kcache, kscale, e4m3, block_table, token_to_req, seq_lens,
                    query_pos, indices, workspace, sv);
-  int err = qsa::launch_select(s, splan, stream);
+  // Fused path: with whole-CU attention workgroups and rows whose
+  // candidates fit in LDS, the attention kernel selects each multi-chunk
+  // row itself instead of a merge launch.
+  const bool fused = aplan.waves == qsa::kAttnRowWaves && splan.chunks_per_row > 1 &&
+                     splan.chunks_per_row * splan.cand_cap <= qsa::kFusedCands;
+  qsa::FusedSelect fs;
+  if (fused) {
+    char* ws = static_cast<char*>(workspace);
+    fs.cand_keys = reinterpret_cast<const uint32_t*>(ws + splan.keys_off);
+    fs.cand_blocks = reinterpret_cast<const uint32_t*>(ws + splan.blocks_off);
+    fs.token_to_req = s.token_to_req;
+    fs.seq_lens = s.seq_lens;
+    fs.query_pos = s.query_pos;
+    fs.num_reqs = s.num_reqs;
+    fs.max_visible = s.max_visible;
+    fs.chunks_per_row = splan.chunks_per_row;
+    fs.chunk_blocks = splan.chunk_pages * QSA_PAGE_SLOTS;
+    fs.cand_cap = (int)splan.cand_cap;
+  }
+  int err = qsa::launch_select(s, splan, stream, !fused);
   if (err) return fail(QSA_ERR_LAUNCH, "selection launch failed (hipError %d)", err);
 
   qsa::AttnArgs a;
@@ -468,6 +487,7 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   a.rows = av.rows;
   a.num_tokens = av.tokens;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  a.fused = fused ? &fs : nullptr;
   err = qsa::launch_attn(a, aplan, stream);
   if (err) return fail(QSA_ERR_LAUNCH, "attention launch failed (hipError %d)", err);
   return QSA_OK;

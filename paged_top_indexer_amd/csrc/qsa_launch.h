@@ -116,10 +116,28 @@ struct SelectArgs {
   int64_t rows = 0, num_pages = 0, num_reqs = 0, table_width = 0, bt_stride = 0;
 };
 
+// The decode step's selection handed to the attention kernel (the fused
+// path): instead of a merge launch, every attention workgroup of a
+// multi-chunk row selects the row's top-k from the chunk kernel's
+// candidates itself, and the row's last split writes the index row.
+struct FusedSelect {
+  const uint32_t* cand_keys = nullptr;    // the chunk kernel's candidates
+  const uint32_t* cand_blocks = nullptr;
+  const int32_t* token_to_req = nullptr;
+  const int32_t* seq_lens = nullptr;
+  const int64_t* query_pos = nullptr;
+  int64_t num_reqs = 0, max_visible = 0, chunks_per_row = 0;
+  int chunk_blocks = 0, cand_cap = 0;
+};
+
+// A row's candidates the fused path holds in LDS (16 chunks of 512).
+constexpr int kFusedCands = 8192;
+
 struct AttnArgs {
   const uint16_t* q;       // [R,3,256] fp16
   const uint16_t* kv;      // packed rows of 512 fp16 (K at +0, V at +256)
-  const int32_t* indices;  // [R,2051]
+  const int32_t* indices;  // [R,2051] (written for multi-chunk rows when fused)
+  const FusedSelect* fused = nullptr;  // non-NULL: select inside the attention
   uint16_t* out;           // [R,3,256] fp16
   void* workspace;
   int64_t rows, num_tokens;
@@ -144,7 +162,9 @@ struct MetaArgs {
 };
 
 // Enqueue the kernels; return the hipError_t of the launch (0 = success).
-int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream);
+// merge false: launch the chunk kernel only (the fused decode step, whose
+// attention kernel does the merge's work).
+int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream, bool merge = true);
 int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
 int launch_metadata(const MetaArgs& a, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);

@@ -19,10 +19,11 @@ WORKLOADS = ["long_context_R128_L131072", "long_context_R128_L131072_fp8",
              "tiny_integer_R1_L519", "saturated_R1_L9215_P8192", "ties_edges_R32_palette64"]
 
 
-def trace_calls(workload: str) -> tuple[dict, int, int, int]:
+def trace_calls(workload: str) -> tuple[dict, int, int, int, int]:
     """Kernel name -> calls from the summary table, the number of steps the
-    run made (the sum of the counts in its 'Calls = ...' line), and the
-    back-to-back selection and attention calls after them."""
+    run made (the sum of the counts in its 'Calls = ...' line), the
+    back-to-back selection and attention calls after them, and how many of
+    the steps were decode-step calls (warm-up, timed and parity)."""
     with open(os.path.join(PROFILES, f"kernel_trace_decode_step_{workload}.md")) as f:
         text = f.read()
     calls = {}
@@ -34,7 +35,8 @@ def trace_calls(workload: str) -> tuple[dict, int, int, int]:
     roof = re.search(r"plus (\d+) back-to-back roofline calls \(selection\) and (\d+) "
                      r"back-to-back attention calls", text)
     assert roof, f"{workload}: no back-to-back calls in the protocol line"
-    return calls, sum(int(g) for g in protocol.groups()), int(roof.group(1)), int(roof.group(2))
+    g = [int(x) for x in protocol.groups()]
+    return calls, sum(g), int(roof.group(1)), int(roof.group(2)), g[0] + g[1] + g[3]
 
 
 @pytest.mark.parametrize("workload", WORKLOADS)
@@ -53,10 +55,13 @@ def test_counters_taken_on_current_sources(workload):
 
 @pytest.mark.parametrize("workload", WORKLOADS)
 def test_one_dispatch_per_step(workload):
-    calls, steps, roof, attn_b2b = trace_calls(workload)
-    # the attention kernel runs as one instantiation (<4> or <12> waves) per shape
-    attn = [v for k, v in calls.items() if k.startswith("qsa_attn_kernel<")]
-    assert attn == [steps + attn_b2b]
+    calls, steps, roof, attn_b2b, decode_steps = trace_calls(workload)
+    # one attention launch per step and per back-to-back call (<4> or <12>
+    # waves; <12, true> is the decode step's fused selection + attention)
+    attn = sum(v for k, v in calls.items() if k.startswith("qsa_attn_kernel<"))
+    assert attn == steps + attn_b2b
+    fused = calls.get("qsa_attn_kernel<12, true>", 0)
+    assert fused in (0, decode_steps)
     if "qsa_attn_combine_kernel" in calls:
         assert calls["qsa_attn_combine_kernel"] == steps + attn_b2b
     chunk = {k: v for k, v in calls.items() if k.startswith("qsa_select_chunk_kernel<")}
@@ -65,7 +70,8 @@ def test_one_dispatch_per_step(workload):
     # writes the matrix and has no merge
     selecting = sum(v for k, v in chunk.items() if k.split(",")[1].strip() == "false")
     if "qsa_select_merge_kernel" in calls:
-        assert calls["qsa_select_merge_kernel"] == selecting
+        # the fused decode steps launch no merge: their attention selects
+        assert calls["qsa_select_merge_kernel"] == selecting - (decode_steps if fused else 0)
     if workload.endswith("_two_pass"):
         assert chunk["qsa_select_chunk_kernel<0, true, 1>"] == steps + roof
         assert chunk["qsa_select_chunk_kernel<2, false, 1>"] == steps
