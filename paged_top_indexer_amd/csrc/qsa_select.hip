@@ -328,23 +328,32 @@ __device__ __forceinline__ float head_sum(const floatx4& acc, const HeadWeights&
   return sum;
 }
 
-// The physical pages of a chunk (at most 32): lane i holds the page of the
-// chunk's i-th logical page, or 0 when the table names a page outside
-// [0, P) (an unmet precondition: such a page reads as an all-zero key, see
-// the valid mask).  A tile's page is then a readlane away, so no load in
-// the scoring loop waits on another load.
-__device__ __forceinline__ int32_t chunk_pages(const SelectParams& p, int64_t req,
-                                               int64_t chunk_base, int nblk, int lane,
-                                               bool* valid) {
-  const int npages = (nblk + kPageSlots - 1) / kPageSlots;
-  int32_t page = 0;
-  *valid = false;
-  if (lane < npages) {
-    const int64_t pg = p.block_table[req * p.bt_stride + (chunk_base / kPageSlots) + lane];
-    *valid = pg >= 0 && pg < p.num_pages;
-    page = *valid ? (int32_t)pg : 0;
+// Lane i: the block table's entry for the chunk's i-th logical page of
+// request req (at most 32 pages), or -1 past the table's width or the
+// lanes, or for an invalid request.  It needs only the request id, so it
+// is loaded while the row's sequence length is still in flight (and
+// checked only where it is used, so that nothing waits for it early).
+__device__ __forceinline__ int32_t page_row(const SelectParams& p, int64_t req, int64_t chunk_base,
+                                            int lane) {
+  const int64_t col = chunk_base / kPageSlots + lane;
+  int32_t entry = -1;
+  if (req >= 0 && req < p.num_reqs && lane < kMaxChunkPages && col < p.table_width) {
+    entry = p.block_table[req * p.bt_stride + col];
   }
-  return page;
+  return entry;
+}
+
+// The physical pages of a chunk of nblk blocks, from its page_row: lane i
+// holds the page of the chunk's i-th logical page, or 0 where the valid
+// mask is clear -- past the chunk, or an entry outside [0, P) (an unmet
+// precondition: such a page reads as an all-zero key).  A tile's page is
+// then a readlane away, so no load in the scoring loop waits on another
+// load.
+__device__ __forceinline__ int32_t chunk_pages(const SelectParams& p, int32_t row_pages, int nblk,
+                                               int lane, bool* valid) {
+  const int npages = (nblk + kPageSlots - 1) / kPageSlots;
+  *valid = lane < npages && row_pages >= 0 && row_pages < p.num_pages;
+  return *valid ? row_pages : 0;
 }
 
 // Key loads go through a buffer resource spanning one cache page: an offset
@@ -375,8 +384,8 @@ __device__ __forceinline__ int tile_keys(int t, int tt, int ntiles, int nblk, ui
 // lane n + 16j.
 template <typename Sink>
 __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem& sm,
-                                                const PassRows& pr, int64_t req,
-                                                int64_t chunk_base, const Sink& sink) {
+                                                const PassRows& pr, int32_t row_pages,
+                                                const Sink& sink) {
   constexpr int kUnroll = 4;  // tiles in flight per wave (4 KiB each)
   constexpr int kPageBytes = kPageSlots * kSelDim * 2;
   const int lane = threadIdx.x & 63;
@@ -397,7 +406,7 @@ __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem
   const HeadWeights hw = head_weights(p, out_row ? pr.r0 + g : pr.r0);
   const int row_nblk = pick_row(pr.nblk, g);  // 0 for lanes of rows outside the pass
   bool page_valid;
-  const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
+  const int32_t pages = chunk_pages(p, row_pages, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
   const int ntiles = (nblk + 15) >> 4;
   if (wave >= ntiles) return;
@@ -493,8 +502,8 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
 // and a tile takes its keys' scales from them with a lane permute.
 template <typename Sink>
 __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm,
-                                                 const PassRows& pr, int64_t req,
-                                                 int64_t chunk_base, const Sink& sink) {
+                                                 const PassRows& pr, int32_t row_pages,
+                                                 const Sink& sink) {
   constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each): one page
   constexpr int kPageBytes = kPageSlots * kSelDim;
   constexpr int kScaleBytes = kPageSlots * 4;
@@ -517,7 +526,7 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
   const HeadWeights hw = head_weights(p, out_row ? pr.r0 + g : pr.r0);
   const int row_nblk = pick_row(pr.nblk, g);
   bool page_valid;
-  const int32_t pages = chunk_pages(p, req, chunk_base, nblk, lane, &page_valid);
+  const int32_t pages = chunk_pages(p, row_pages, nblk, lane, &page_valid);
   const uint64_t valid_mask = __ballot(page_valid);
   const int ntiles = (nblk + 15) >> 4;
   const int npages = (nblk + kPageSlots - 1) / kPageSlots;
@@ -662,23 +671,54 @@ qsa_select_chunk_kernel(SelectParams p) {
 
   // The group's rows (uniform values, constant indices): request, blocks of
   // this chunk, and which rows have work here (a selection's chunk past a
-  // row's last one has none; paged logits fill every column).
-  int64_t req[kMaxGroup];
+  // row's last one has none; paged logits fill every column).  Their inputs
+  // load in two rounds, each all at once: every row's request id and query
+  // position (a group past the batch's end re-reads the last row; unused),
+  // then the sequence lengths and the first request's block-table entries
+  // for this chunk.
+  int64_t req[kMaxGroup], qpos[kMaxGroup], seq[kMaxGroup];
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) {
+    req[j] = -1;
+    qpos[j] = 0;
+    seq[j] = 0;
+  }
+  // (lane j < kGroup loads row r0 + j's values: one vector load per array
+  // and round; per-row scalar loads were issued one after another)
+  int32_t pages0 = -1;  // page_row of req[0]
+  {
+    const int lane = tid & 63;
+    const int64_t rl = min(r0 + min(lane, kGroup - 1), p.rows - 1);
+    const int32_t req_l = p.token_to_req[rl];
+    const int64_t qpos_l = p.query_pos[rl];
+    const int64_t req_0 = __builtin_amdgcn_readfirstlane(req_l);
+    if constexpr (kSrc != kSrcLogits) pages0 = page_row(p, req_0, chunk_base, lane);
+    const int32_t seq_l = p.num_reqs > 0 ? seq_len_at(p.seq_lens, p.num_reqs, req_l) : 0;
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      req[j] = __builtin_amdgcn_readlane(req_l, j);
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)qpos_l, j);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)qpos_l >> 32), j);
+      qpos[j] = (int64_t)(((uint64_t)hi << 32) | lo);
+      seq[j] = __builtin_amdgcn_readlane(seq_l, j);
+    }
+  }
   int nblk[kMaxGroup];
   uint32_t live = 0;   // rows with work in this chunk
   uint32_t single = 0; // rows whose only chunk this is (finished here)
   Row row0;
 #pragma unroll
   for (int j = 0; j < kMaxGroup; ++j) {
-    req[j] = -1;
     nblk[j] = 0;
-    if (j < rows_here) {
-      const Row row = row_setup(p, r0 + j);
+    if (j < kGroup && j < rows_here) {
+      const Row row = row_from(req[j], qpos[j], seq[j], p.num_reqs, p.max_visible, p.chunk_blocks);
       if (j == 0) row0 = row;
-      req[j] = row.req;
+      req[j] = row.req;  // -1 for a request id outside [0, N)
       nblk[j] = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
       if (kLogitsOut || chunk < row.nchunks) live |= 1u << j;
       if (row.nchunks == 1) single |= 1u << j;
+    } else {
+      req[j] = -1;
     }
   }
   if (live == 0) return;
@@ -714,10 +754,12 @@ qsa_select_chunk_kernel(SelectParams p) {
         pr.nblk_max = max(pr.nblk_max, pr.nblk[j]);
       }
       todo &= ~pr.mask;
+      // (the first pass is req[0]'s, whose block-table entries are loaded)
+      const int32_t row_pages = rq == req[0] ? pages0 : page_row(p, rq, chunk_base, tid & 63);
       if constexpr (kSrc == kSrcE4M3) {
-        score_chunk_e4m3(p, sm, pr, rq, chunk_base, sink);
+        score_chunk_e4m3(p, sm, pr, row_pages, sink);
       } else {
-        score_chunk_f16(p, sm, pr, rq, chunk_base, sink);
+        score_chunk_f16(p, sm, pr, row_pages, sink);
       }
     }
   };

@@ -37,18 +37,15 @@ struct Row {
 };
 
 // Visible blocks V = max(0, min(floor((qp+1)/4), floor(L/4))) and tail
-// T = min(qp+1, L) - 4V of query row r.  A request id outside [0, N) makes
-// the row empty; V never exceeds what the block table can map (or, for a
-// logits source, the logits width).
-__device__ inline Row row_extent(const int32_t* token_to_req, int64_t num_reqs,
-                                 const int32_t* seq_lens, const int64_t* query_pos,
-                                 int64_t max_visible, int chunk_blocks, int64_t r) {
+// T = min(qp+1, L) - 4V of query row r, from its request id `req`, query
+// position `qpos` and the request's sequence length.  A request id outside
+// [0, N) makes the row empty; V never exceeds what the block table can map
+// (or, for a logits source, the logits width).
+__device__ inline Row row_from(int64_t req, int64_t qpos, int64_t seq_len, int64_t num_reqs,
+                               int64_t max_visible, int chunk_blocks) {
   Row row;
-  const int64_t req = token_to_req[r];
   if (req >= 0 && req < num_reqs) {
     row.req = req;
-    const int64_t seq_len = seq_lens[req];
-    const int64_t qpos = query_pos[r];
     const int64_t upto = qpos < INT64_MAX ? qpos + 1 : qpos;
     const int64_t a = upto >= 0 ? upto / kRatio : -1;
     const int64_t b = seq_len >= 0 ? seq_len / kRatio : -1;
@@ -59,6 +56,25 @@ __device__ inline Row row_extent(const int32_t* token_to_req, int64_t num_reqs,
   }
   row.nchunks = max((int64_t)1, (row.visible + chunk_blocks - 1) / chunk_blocks);
   return row;
+}
+
+// seq_lens[req], read at index 0 for a request id outside [0, N) so that
+// the load needs no branch (its value is then unused); N >= 1.
+__device__ __forceinline__ int64_t seq_len_at(const int32_t* seq_lens, int64_t num_reqs,
+                                              int64_t req) {
+  return seq_lens[(req >= 0 && req < num_reqs) ? req : 0];
+}
+
+// Row r's extent from the selection inputs: the request id and query
+// position are independent loads issued together, then the sequence
+// length (two dependent memory round trips, not three).
+__device__ inline Row row_extent(const int32_t* token_to_req, int64_t num_reqs,
+                                 const int32_t* seq_lens, const int64_t* query_pos,
+                                 int64_t max_visible, int chunk_blocks, int64_t r) {
+  const int64_t req = token_to_req[r];
+  const int64_t qpos = query_pos[r];
+  const int64_t seq_len = num_reqs > 0 ? seq_len_at(seq_lens, num_reqs, req) : 0;
+  return row_from(req, qpos, seq_len, num_reqs, max_visible, chunk_blocks);
 }
 
 // Radix digits of a 32-bit key, most significant first: 11, 11 and 10 bits.
