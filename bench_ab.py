@@ -8,7 +8,7 @@ unit i wins when it is faster than the mean of the baseline units around it
 once more on the same inputs and their outputs are compared.
 
     python bench_ab.py --baseline OLD.so [--candidate NEW.so] [--workload NAME]
-                       [--op decode_step|select|attention] [--pairs 10]
+                       [--op decode_step|select|attention] [--pairs 10] [--rows R]
 
 The candidate defaults to the tree's libqsa_amd.so; a baseline of an
 earlier revision is built with `python -m paged_top_indexer_amd.build --rev
@@ -45,6 +45,8 @@ def main() -> int:
     ap.add_argument("--pairs", type=int, default=10)
     ap.add_argument("--rows-per-run", type=int, default=0,
                     help="queries as [R/n, n, 4, 128]; default 4 for multi_token, else 1")
+    ap.add_argument("--rows", type=int, default=0,
+                    help="long_context only: its batch size (default 128)")
     ap.add_argument("--kv-copies", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
@@ -61,7 +63,11 @@ def main() -> int:
             print(f"{name} library {path} is missing", file=sys.stderr)
             return 2
     calls = args.calls or (128 if args.op == "attention" else 64)
-    w = getattr(wl, BUILDERS[args.workload])(args.seed)
+    if args.rows and args.workload != "long_context":
+        print("--rows applies to long_context only", file=sys.stderr)
+        return 2
+    w = (wl.long_context(args.seed, rows=args.rows) if args.rows else
+         getattr(wl, BUILDERS[args.workload])(args.seed))
     dev = torch.device("cuda:0")
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     sel = [d(a) for a in w.select_inputs()]
@@ -141,7 +147,7 @@ def main() -> int:
     same_idx = bool(np.array_equal(outs["baseline"][0], outs["candidate"][0]))
     diff_out = float(np.max(np.abs(outs["baseline"][1].astype(np.float64) -
                                    outs["candidate"][1].astype(np.float64))))
-    res = {"workload": w.name, "op": args.op, "calls_per_unit": calls,
+    res = {"workload": w.name, "rows": w.rows, "op": args.op, "calls_per_unit": calls,
            "warmup_units": args.warmup_units, "pairs": args.pairs,
            "baseline": {"lib": libs["baseline"], "mean_ms": round(float(np.mean(base)), 5),
                         "median_ms": round(float(np.median(base)), 5)},

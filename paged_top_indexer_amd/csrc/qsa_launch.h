@@ -130,7 +130,9 @@ struct FusedSelect {
   int chunk_blocks = 0, cand_cap = 0;
 };
 
-// A row's candidates the fused path holds in LDS (16 chunks of 512).
+// A row's candidates the fused path holds in LDS (16 chunks of 512), and
+// the merge kernel's batch: plan_select keeps a row within it where the
+// largest chunk allows.
 constexpr int kFusedCands = 8192;
 
 struct AttnArgs {

@@ -18,7 +18,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // Chunk size: the largest of 32/16/8/4/2/1 pages that still gives the chunk
 // kernel about 1024 workgroups (4 per compute unit on 256 CUs, its
 // occupancy), so long rows are split across the chip while short batches
-// keep chunks small.  A table of at most 4 pages (512 blocks: every visible
+// keep chunks small -- but no smaller than keeps a row's candidates
+// (chunks x min(512, chunk)) within one merge batch of kFusedCands, where
+// the largest chunk allows: every further batch of 8192 candidates costs
+// the merge a whole radix select, more than a few rows' longer chunks cost
+// the chunk kernel.  A table of at most 4 pages (512 blocks: every visible
 // block is selected, no top-k) is one chunk per row whatever the batch, so
 // short rows finish in the chunk kernel without a merge launch.
 SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
@@ -31,6 +35,10 @@ SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
     pages = (int)w;
   } else {
     while (pages > 1 && groups * ((w + pages - 1) / pages) < 1024) pages >>= 1;
+    auto row_cands = [&](int pg) {
+      return ((w + pg - 1) / pg) * std::min<int64_t>(kTopKBlocks, (int64_t)pg * kPageSlots);
+    };
+    while (pages < max_chunk_pages(p.group) && row_cands(pages) > kFusedCands) pages <<= 1;
   }
   p.chunk_pages = pages;
   p.chunks_per_row = (w + pages - 1) / pages;

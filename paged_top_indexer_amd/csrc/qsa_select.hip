@@ -70,7 +70,9 @@ namespace {
 // the merge's LDS latency -- both in qsa_launch.h)
 constexpr int kMaxChunkPages = 32;
 constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
-constexpr int kMergeList = 8192 + kTopKBlocks;  // LDS list of the merge
+// LDS list of the merge: the running best plus a batch of kFusedCands
+// candidates (the plans keep a row within one batch where they can)
+constexpr int kMergeList = kFusedCands + kTopKBlocks;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));

@@ -50,6 +50,14 @@ def test_workspace_sizes():
     assert big >= 128 * 8 * 512 * 8
     assert B.decode_step_workspace_bytes(128, 256) >= big + B.sparse_attn_workspace_bytes(128)
     assert B.sparse_attn_workspace_bytes(128) > 0
+    # few rows of a long table: 1024 workgroups would mean 1-page chunks
+    # (256 chunks x 128 candidates per row, 4 merge batches); the chunks grow
+    # until a row's candidates fit one merge batch of 8192 where the largest
+    # chunk allows -- 16 x 512 for single rows, and for row groups (largest
+    # chunk 8 pages) 32 x 512, which sizes the workspace: two uint32 arrays
+    assert B.select_workspace_bytes(4, 256) == 2 * (4 * 32 * 512 * 4)
+    # a row that fits one batch already keeps its 1024-workgroup chunks
+    assert B.select_workspace_bytes(4, 64) == 2 * (4 * 64 * 128 * 4)
 
 
 # ---------------------------------------------------------------------------

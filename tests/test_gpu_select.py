@@ -42,15 +42,18 @@ def test_ties_and_edges_bit_exact():
     assert np.array_equal(got, want)
 
 
-# Plans: (rows, table width) pick the chunk size (1..16 pages, or the whole
+# Plans: (rows, table width) pick the chunk size (1..32 pages, or the whole
 # table up to 4 pages); these cover chunks below and above 512 blocks,
-# one-chunk rows, and multi-chunk merges with ragged last chunks.
+# one-chunk rows, multi-chunk merges with ragged last chunks, and few rows
+# of a long table (chunks grown until a row's candidates fit one merge
+# batch: 16 pages for 5 rows of 256).
 PLAN_CASES = [
     (5, 4, [0, 1, 515, 2048, 2047]),  # tables of <= 4 pages: one chunk per row
     (3, 3, [1536, 9, 1100]),
     (1, 20, [9215]),
     (3, 40, [0, 20000, 517]),
     (8, 64, [1, 2, 3, 512, 515, 516, 2049, 32768]),
+    (5, 256, [131072, 131071, 70001, 131072, 99999]),
     (64, 256, [70001, 131072, 0, 3, 4096, 2051, 1027, 513] * 8),
     (130, 256, [131071, 65539, 9999, 600, 131072] * 26),
 ]
