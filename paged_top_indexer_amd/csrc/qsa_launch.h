@@ -81,8 +81,8 @@ SelectPlan plan_select(int64_t rows, int64_t table_width, int group = 1);
 
 // Launch plan of the attention kernel: `splits` workgroups per row, each
 // covering `split_positions` index positions with `waves` waves (tiles of
-// 16 positions): 4 waves per split, or kAttnRowWaves when one workgroup
-// takes a whole row.
+// 16 positions): 4 waves per split, or kAttnRowWaves (about one workgroup
+// per CU, for 24 to 256 rows).
 struct AttnPlan {
   int split_positions = 128;
   int splits = 1;
