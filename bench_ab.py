@@ -46,7 +46,9 @@ def main() -> int:
     ap.add_argument("--rows-per-run", type=int, default=0,
                     help="queries as [R/n, n, 4, 128]; default 4 for multi_token, else 1")
     ap.add_argument("--rows", type=int, default=0,
-                    help="long_context only: its batch size (default 128)")
+                    help="long_context: its batch size (<= 128); multi_token: its "
+                         "rows (4 prefill requests x 16 rows plus decode requests "
+                         "x 4 rows; default 256)")
     ap.add_argument("--kv-copies", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
@@ -63,11 +65,18 @@ def main() -> int:
             print(f"{name} library {path} is missing", file=sys.stderr)
             return 2
     calls = args.calls or (128 if args.op == "attention" else 64)
-    if args.rows and args.workload != "long_context":
-        print("--rows applies to long_context only", file=sys.stderr)
+    if args.rows and args.workload not in ("long_context", "multi_token"):
+        print("--rows applies to long_context and multi_token only", file=sys.stderr)
         return 2
-    w = (wl.long_context(args.seed, rows=args.rows) if args.rows else
-         getattr(wl, BUILDERS[args.workload])(args.seed))
+    if args.rows and args.workload == "long_context":
+        w = wl.long_context(args.seed, rows=args.rows)
+    elif args.rows:
+        if args.rows < 64 or args.rows % 4:
+            print("multi_token --rows: a multiple of 4, at least 64", file=sys.stderr)
+            return 2
+        w = wl.multi_token_rows(args.seed, decode_requests=(args.rows - 64) // 4)
+    else:
+        w = getattr(wl, BUILDERS[args.workload])(args.seed)
     dev = torch.device("cuda:0")
     d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     sel = [d(a) for a in w.select_inputs()]
