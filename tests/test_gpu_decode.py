@@ -74,6 +74,22 @@ def test_multi_token_rows():
     check_attn(out, oracle_attn(orc(), w.q_attn, w.kv, idx, SCALE), "multi-token, every row")
 
 
+@pytest.mark.parametrize("rows", [23, 24])
+def test_fused_boundary_rows(rows):
+    """The first rows of the long-context batch (128K-token rows, N(0,1)):
+    23 rows take 4-wave attention workgroups after a merge launch, 24 rows
+    the 12-wave plan with each row's selection folded into the attention
+    launch.  Every row's selection within the band, every row's attention
+    against the oracle over the GPU's own index row."""
+    w = wl.long_context(0, rows=rows)
+    inputs = w.select_inputs()
+    banner(f"decode long_context rows={rows}")
+    idx, out = decode_gpu(w)
+    want_idx = oracle_select(orc(), inputs)
+    check_select_band(idx, want_idx, orc(), inputs, range(rows))
+    check_attn(out, oracle_attn(orc(), w.q_attn, w.kv, idx, SCALE), f"rows={rows}, every row")
+
+
 @pytest.mark.parametrize("rows,lo,hi", [(4096, 0, 1500), (800, 4000, 12000)],
                          ids=["R4096_short", "R800_mid"])
 def test_large_batches(rows, lo, hi):
