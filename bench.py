@@ -737,13 +737,25 @@ def main() -> int:
                                          key_bytes=132 if fp8 else 256)
     att_bytes, att_gather = attn_algorithmic_bytes(got_idx)
     # kernel launches of one timed step at these shapes (the committed kernel
-    # traces show one call of each per step)
+    # traces show one call of each per step).  This mirrors the library's
+    # plans: rows of several chunks need a merge (a selection workspace),
+    # except in a decode step whose attention takes 12-wave workgroups
+    # (24-256 rows with at least two 16-position tiles per wave), which
+    # selects them itself; a top-k per row over at most 32768 columns is one
+    # kernel; several splits per row need a combine (an attention workspace).
     plan_chunks = qsa.select_workspace_bytes(R, w.block_table.shape[1]) > 0
-    kernels_per_step = (["qsa_metadata_kernel"] if meta else []) + (
-        ["qsa_select_chunk_kernel (paged logits)", "qsa_select_chunk_kernel (top-k per row)"]
-        if two_pass else ["qsa_select_chunk_kernel"]) + (
-        ["qsa_select_merge_kernel"] if plan_chunks else []) + ["qsa_attn_kernel"] + (
-        ["qsa_attn_combine_kernel"] if qsa.sparse_attn_workspace_bytes(R) > 0 else [])
+    row_waves = 0 < R <= 256 and (256 // R) * 16 * 12 < qsa.OUT_WIDTH
+    combine = ["qsa_attn_combine_kernel"] if qsa.sparse_attn_workspace_bytes(R) > 0 else []
+    if two_pass:
+        topk = (["qsa_topk_row_kernel"] if logits_width <= 32768 else
+                ["qsa_select_chunk_kernel (top-k per row)", "qsa_select_merge_kernel"])
+        kernels_per_step = ["qsa_select_chunk_kernel (paged logits)"] + topk + ["qsa_attn_kernel"]
+    else:
+        fused = plan_chunks and row_waves
+        kernels_per_step = (["qsa_metadata_kernel"] if meta else []) + ["qsa_select_chunk_kernel"] + (
+            ["qsa_select_merge_kernel"] if plan_chunks and not fused else []) + (
+            ["qsa_attn_kernel (selecting multi-chunk rows)"] if fused else ["qsa_attn_kernel"])
+    kernels_per_step += combine
     sel_avg_s = float(np.mean(sel_ms)) / 1e3
     att_avg_s = float(np.mean(att_ms)) / 1e3
 

@@ -605,7 +605,8 @@ QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
 }
 
 QSA_API size_t qsa_topk_per_row_workspace_bytes(int64_t rows, int64_t logits_width) {
-  if (rows <= 0) return 0;
+  // rows of at most kRowTopkMaxWidth columns: one workgroup per row, none
+  if (rows <= 0 || logits_width <= qsa::kRowTopkMaxWidth) return 0;
   return qsa::plan_select(rows, (logits_width + QSA_PAGE_SLOTS - 1) / QSA_PAGE_SLOTS).bytes;
 }
 
@@ -637,8 +638,15 @@ QSA_API int qsa_topk_per_row(const qsa_tensor* logits, const qsa_tensor* token_t
   if (R == 0) return QSA_OK;
   const int64_t width = logits->shape[1];
   const int64_t pages = (width + QSA_PAGE_SLOTS - 1) / QSA_PAGE_SLOTS;
-  const qsa::SelectPlan plan = qsa::plan_select(R, pages);
-  QSA_TRY(check_select_grid("top-k", plan, R));
+  // rows of at most kRowTopkMaxWidth columns: one workgroup per row holds
+  // the whole row; wider ones go through chunks and a merge
+  const bool whole_rows = width <= qsa::kRowTopkMaxWidth;
+  const qsa::SelectPlan plan = whole_rows ? qsa::SelectPlan{} : qsa::plan_select(R, pages);
+  if (whole_rows) {
+    QSA_TRY(check_grid("top-k", R, 1, qsa::kRowTopkThreads));
+  } else {
+    QSA_TRY(check_select_grid("top-k", plan, R));
+  }
   Span guarded[5] = {span_of(logits), span_of(token_to_req), span_of(seq_lens),
                      span_of(query_pos), span_of(out)};
   QSA_TRY(check_workspace(workspace, workspace_bytes, plan.bytes, guarded, 5));
@@ -655,7 +663,7 @@ QSA_API int qsa_topk_per_row(const qsa_tensor* logits, const qsa_tensor* token_t
   a.rows = R;
   a.num_reqs = N;
   a.table_width = pages;
-  const int err = qsa::launch_select(a, plan, stream);
+  const int err = whole_rows ? qsa::launch_topk_rows(a, stream) : qsa::launch_select(a, plan, stream);
   if (err) return fail(QSA_ERR_LAUNCH, "top-k launch failed (hipError %d)", err);
   return QSA_OK;
 }

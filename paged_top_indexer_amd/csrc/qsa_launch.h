@@ -135,6 +135,11 @@ struct FusedSelect {
 // largest chunk allows.
 constexpr int kFusedCands = 8192;
 
+// A logits row of at most this many columns is selected by one workgroup of
+// kRowTopkThreads holding the whole row in LDS (128 KiB of keys).
+constexpr int64_t kRowTopkMaxWidth = 32768;
+constexpr int kRowTopkThreads = 1024;
+
 struct AttnArgs {
   const uint16_t* q;       // [R,3,256] fp16
   const uint16_t* kv;      // packed rows of 512 fp16 (K at +0, V at +256)
@@ -168,6 +173,9 @@ struct MetaArgs {
 // attention kernel does the merge's work).
 int launch_select(const SelectArgs& a, const SelectPlan& p, void* stream, bool merge = true);
 int launch_paged_logits(const SelectArgs& a, const SelectPlan& p, void* stream);
+// Top-k per row over logits rows of at most kRowTopkMaxWidth columns: one
+// workgroup of kRowTopkThreads per row, no workspace.
+int launch_topk_rows(const SelectArgs& a, void* stream);
 int launch_metadata(const MetaArgs& a, void* stream);
 int launch_attn(const AttnArgs& a, const AttnPlan& p, void* stream);
 

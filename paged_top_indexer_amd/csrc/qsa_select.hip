@@ -1005,6 +1005,87 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
   sort_expand_write(sm.sorted, best_n, row.visible, row.tail, p.out + r * kOutWidth, sm.sorted);
 }
 
+// ---- top-k per row over a logits matrix, one workgroup per row -----------
+// A row of at most kRowTopkMaxWidth scores is held whole in LDS, so one
+// workgroup takes it from the logits to the written index row: no chunk
+// candidates, no merge launch.  The scores become order-preserving keys as
+// they load; the keys' shared leading bits are shifted out before the radix
+// select (same order, same ties; without it the first digit would put a
+// whole row in a few bins and the histogram's LDS atomics would serialise),
+// then threshold, compaction, sort and expansion as in the merge kernel.
+struct RowSmem {
+  uint32_t keys[kRowTopkMaxWidth];
+  alignas(16) uint32_t hist0[kBins];
+  alignas(16) uint32_t hist1[kBins];
+  uint64_t sorted[kTopKBlocks];
+  uint32_t red_and[kRowTopkThreads / 64], red_or[kRowTopkThreads / 64];
+  Scratch s;
+};
+
+__global__ __launch_bounds__(kRowTopkThreads) void qsa_topk_row_kernel(SelectParams p) {
+  __shared__ RowSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  if (r >= p.rows) return;
+  for (int i = tid; i < kBins; i += kRowTopkThreads) sm.hist0[i] = 0;
+  const Row row = row_setup(p, r);
+  const int n = (int)row.visible;  // <= logits_width <= kRowTopkMaxWidth
+  const int k = min(kTopKBlocks, n);
+  const float* src = p.logits_in + r * p.logits_stride;
+  // a whole row in flight at once: 32 loads per thread
+  constexpr int kUnroll = kRowTopkMaxWidth / kRowTopkThreads;
+  uint32_t kand = 0xFFFFFFFFu, kor = 0;
+  for (int i0 = tid; i0 < n; i0 += kRowTopkThreads * kUnroll) {
+    float v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kRowTopkThreads;
+      v[u] = i < n ? __builtin_nontemporal_load(src + i) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int i = i0 + u * kRowTopkThreads;
+      if (i < n) {
+        const uint32_t key = score_key(v[u]);
+        sm.keys[i] = key;
+        kand &= key;
+        kor |= key;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
+    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
+  }
+  if ((tid & 63) == 0) {
+    sm.red_and[tid >> 6] = kand;
+    sm.red_or[tid >> 6] = kor;
+  }
+  __syncthreads();
+  uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
+#pragma unroll
+  for (int w = 0; w < kRowTopkThreads / 64; ++w) {
+    all_and &= sm.red_and[w];
+    all_or |= sm.red_or[w];
+  }
+  const uint32_t differ = all_and ^ all_or;
+  const int shift = differ ? __builtin_clz(differ) : 0;  // bits every key shares
+  auto lds_key = [&](int i) { return sm.keys[i] << shift; };
+  auto block_of = [&](int i) { return (uint32_t)i; };
+  uint32_t T = 0, bcut = 0xFFFFFFFFu;  // k == n: every key is taken
+  if (n > k) {
+    for (int i = tid; i < n; i += kRowTopkThreads) atomicAdd(&sm.hist0[digit0(lds_key(i))], 1u);
+    __syncthreads();
+    topk_threshold<kRowTopkThreads>(lds_key, block_of, n, k, sm.s, sm.hist0, sm.hist1, T, bcut);
+  }
+  compact_topk<kRowTopkThreads>(
+      lds_key, block_of, n, T, bcut,
+      [&](uint32_t slot, int i, uint32_t) { sm.sorted[slot] = pack(sm.keys[i], (uint32_t)i); },
+      sm.s);
+  sort_expand_write(sm.sorted, k, row.visible, row.tail, p.out + r * kOutWidth, sm.sorted);
+}
+
 }  // namespace
 
 namespace {
@@ -1074,6 +1155,14 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream, boo
   const int64_t groups = (a.rows + p.group - 1) / p.group;
   hipLaunchKernelGGL(qsa_select_merge_kernel, dim3((unsigned)(padded_rows(groups) * p.group)),
                      dim3(kMergeThreads), 0, s, p);
+  return (int)hipGetLastError();
+}
+
+int launch_topk_rows(const SelectArgs& a, void* stream) {
+  if (a.rows == 0) return 0;
+  const SelectParams p = make_params(a, SelectPlan{});
+  hipLaunchKernelGGL(qsa_topk_row_kernel, dim3((unsigned)a.rows), dim3(kRowTopkThreads), 0,
+                     static_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 

@@ -10,6 +10,7 @@ namespace qsa {
 
 int launch_select(const SelectArgs&, const SelectPlan&, void*, bool) { std::abort(); }
 int launch_paged_logits(const SelectArgs&, const SelectPlan&, void*) { std::abort(); }
+int launch_topk_rows(const SelectArgs&, void*) { std::abort(); }
 int launch_metadata(const MetaArgs&, void*) { std::abort(); }
 int launch_attn(const AttnArgs&, const AttnPlan&, void*) { std::abort(); }
 int static_scratch(void**) { std::abort(); }

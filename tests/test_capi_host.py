@@ -431,7 +431,11 @@ def call_topk(lg, t2r, sl, qp, out, ws, ws_bytes):
 
 def test_topk_per_row_checks():
     f = Fake()
-    R, Wl = 4, 9000
+    # rows of at most 32768 columns are selected one workgroup per row,
+    # without workspace; wider rows go through chunks and a merge
+    assert B.topk_per_row_workspace_bytes(4, 32768) == 0
+    assert B.topk_per_row_workspace_bytes(4, 32769) > 0
+    R, Wl = 4, 40000
     lg = mk(f, B.F32, (R, Wl), 4)
     t2r, sl, qp = mk(f, B.I32, (R,), 4), mk(f, B.I32, (2,), 4), mk(f, B.I64, (R,), 8)
     out = mk(f, B.I32, (R, 2051), 4)

@@ -120,11 +120,13 @@ def random_logits(seed, rows, width):
     return lg
 
 
-@pytest.mark.parametrize("rows,width", [(1, 600), (7, 5000), (64, 33000), (130, 9000)])
+@pytest.mark.parametrize("rows,width", [(1, 600), (7, 5000), (3, 32768), (2, 32769),
+                                        (64, 33000), (130, 9000)])
 def test_topk_per_row_exact(rows, width):
     """Given logits, the selection is exact (no arithmetic): ties, signed
     zeros, -inf, junk past each row's visible blocks, rows shorter and longer
-    than 512 blocks, multi-row requests."""
+    than 512 blocks, multi-row requests.  Up to 32768 columns one workgroup
+    selects a whole row; wider rows go through chunks and a merge."""
     rng = np.random.default_rng(rows + width)
     lg = random_logits(rows * 3 + width, rows, width)
     nreq = max(1, rows // 2)
