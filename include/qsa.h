@@ -247,7 +247,8 @@ QSA_API int qsa_paged_logits(const qsa_tensor* q, const qsa_tensor* weights,
                              const qsa_tensor* logits, qsa_stream stream);
 
 /* Workspace bytes qsa_topk_per_row needs for `rows` rows of `logits_width`
- * columns.  0 when rows == 0. */
+ * columns.  0 when rows == 0 or logits_width <= 32768 (such rows are
+ * selected one workgroup per row). */
 QSA_API size_t qsa_topk_per_row_workspace_bytes(int64_t rows, int64_t logits_width);
 
 /*
