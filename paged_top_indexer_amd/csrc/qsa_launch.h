@@ -30,7 +30,7 @@ constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 // Threads per workgroup of each kernel (the host checks grid sizes with
 // them).
 constexpr int kChunkThreads = 256;
-constexpr int kMergeThreads = 512;
+constexpr int kMergeThreads = 768;
 constexpr int kAttnThreads = 256;
 constexpr int kCombineThreads = 256;
 

@@ -66,7 +66,7 @@
 namespace qsa {
 namespace {
 
-// (kChunkThreads = 256; kMergeThreads = 512: 2 waves per SIMD hide part of
+// (kChunkThreads = 256; kMergeThreads = 768: 3 waves per SIMD hide part of
 // the merge's LDS latency -- both in qsa_launch.h)
 constexpr int kMaxChunkPages = 32;
 constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
