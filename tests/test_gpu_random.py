@@ -11,7 +11,7 @@ import torch
 
 from paged_top_indexer_amd import workloads as wl
 import paged_top_indexer_amd as qsa
-from gpu_util import banner, dev, dev_e4m3, orc
+from gpu_util import banner, check_attn, dev, dev_e4m3, orc
 
 pytestmark = pytest.mark.gpu
 
@@ -82,3 +82,41 @@ def test_random_selection_bit_exact(seed):
     got = got.cpu().numpy()
     bad = np.flatnonzero(~np.all(got == want, axis=1))
     assert bad.size == 0, f"{c['desc']}: rows differ: {bad[:10]}"
+
+
+DECODE_CASES = 8
+
+
+@pytest.mark.parametrize("seed", range(DECODE_CASES))
+def test_random_decode_step(seed):
+    """The decode step over the same kind of random configurations (no head
+    weights: the decode step has none): its index rows bit-exact against the
+    oracle, its attention against the oracle's over those index rows.  Batch
+    sizes from 1 to ~300 rows cover both attention plans, and with them the
+    decode steps that select inside the attention launch and those that
+    launch a merge."""
+    c = random_case(100 + seed)
+    q, kcache, bt, t2r, sl, qp = c["q"], c["kcache"], c["bt"], c["t2r"], c["sl"], c["qp"]
+    R = q.shape[0]
+    rng = np.random.default_rng(5000 + seed)
+    kv_pages = -(-int(max(int(sl.max()), 1)) // 512) + 1
+    kv = wl.normal_f16(rng, (kv_pages, 512, 512))
+    q_attn = wl.normal_f16(rng, (R, 3, 256))
+    scale = wl.SOFTMAX_SCALE
+    banner(f"random decode step R={R} {c['desc']} kv_pages={kv_pages}")
+    want = orc().select(q, kcache, bt, t2r, sl, qp)
+    qd = dev(q)
+    if c["hint"] > 1:
+        qd = qd.view(R // c["hint"], c["hint"], 4, 128)
+    k, v = qsa.kv_views(dev(kv))
+    args = [dev(bt), dev(t2r), dev(sl), dev(qp), dev(q_attn), k, v, scale]
+    if c["fp8"]:
+        codes, scales = wl.fp8_integer_keys(c["rng"], kcache)
+        idx, out = qsa.qsa_decode_step_fp8(qd, dev_e4m3(codes), dev(scales), *args)
+    else:
+        idx, out = qsa.qsa_decode_step(qd, dev(kcache), *args)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    bad = np.flatnonzero(~np.all(idx == want, axis=1))
+    assert bad.size == 0, f"{c['desc']}: rows differ: {bad[:10]}"
+    check_attn(out.cpu().numpy(), orc().sparse_attn(q_attn, kv, idx, scale), c["desc"])
