@@ -39,7 +39,10 @@ Inputs are seeded synthetic data, resident in HBM before timing starts.
 One step = one qsa_decode_step call (selection then attention on one
 stream, no host sync); K steps (200 by default) are timed with HIP events at
 both ends.  The
-steps rotate over distinct KV caches, as consecutive layers would.  A second
+steps rotate over distinct KV caches and over block tables that map the
+rows through distinct page permutations of the key cache, as consecutive
+layers would read distinct caches (no step finds its data in the last-level
+cache because an earlier step read it).  A second
 pass runs the two stages through qsa_select and qsa_sparse_attn with events
 between them for the per-stage times and the roofline.  Prints one JSON line.
 The oracle then checks every row of the timed configuration's output (the
@@ -486,11 +489,12 @@ def gpu_clocks():
     return keep or None
 
 
-def workload_config(w, kv_copies: int) -> dict:
+def workload_config(w, kv_copies: int, key_tables: int) -> dict:
     lens = w.seq_lens[w.token_to_req].astype(np.int64)
     cfg = {"workload": w.name, "rows": int(w.rows), "requests": int(len(np.unique(w.token_to_req))),
            "cache_pages": int(w.kcache.shape[0]), "kv_tokens": int(w.kv.shape[0] * w.kv.shape[1]),
-           "top_blocks": 512, "index_width": 2051, "kv_caches_rotated": kv_copies}
+           "top_blocks": 512, "index_width": 2051, "kv_caches_rotated": kv_copies,
+           "key_tables_rotated": key_tables}
     if np.all(lens == lens[0]):
         cfg["seq_len"] = int(lens[0])
     else:
@@ -518,6 +522,9 @@ def main() -> int:
                          "one request); default 4 for the multi_token workloads, else 1")
     ap.add_argument("--kv-copies", type=int, default=8,
                     help="distinct KV caches the steps rotate over (one per simulated layer)")
+    ap.add_argument("--key-tables", type=int, default=8,
+                    help="block tables (page permutations of the key cache) the steps' "
+                         "selections rotate over (one per simulated layer)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the bench, run a plain device copy of MIB MiB three "
                          "times (reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -581,6 +588,21 @@ def main() -> int:
     for i in range(1, args.kv_copies):
         kv_sets.append(d(wl.normal_f16(np.random.default_rng(args.seed + 1000 + i), w.kv.shape)))
     kv_views = [qsa.kv_views(t) for t in kv_sets]
+    # Likewise the selection: a layer's compressed keys are read once per
+    # step, so the steps rotate over block tables that map the rows through
+    # distinct page permutations of the cache (table 0 is the workload's own;
+    # same rows, lengths and sharing, other physical pages).  No step then
+    # finds its keys in the last-level cache because an earlier step read
+    # them.
+    sel_sets = [sel_in]
+    perm_rng = np.random.default_rng(args.seed + 2000)
+    bt_at = 3 if fp8 else 2  # (e4m3 inputs carry the key scales before the table)
+    for i in range(1, args.key_tables):
+        perm = perm_rng.permutation(w.kcache.shape[0]).astype(np.int32)
+        bt = np.asarray(w.block_table).copy()
+        bt[bt >= 0] = perm[bt[bt >= 0]]
+        sel_sets.append(sel_in[:bt_at] + [d(bt)] + sel_in[bt_at + 1:])
+    sel_at = lambda i: sel_sets[i % len(sel_sets)]  # noqa: E731
     q_attn = d(w.q_attn)
     R = w.rows
     idx = torch.empty((R, 2051), dtype=torch.int32, device=dev)
@@ -604,21 +626,22 @@ def main() -> int:
                                           workspace=meta_ws)
         built_in = [sel_in[0], sel_in[1], sel_in[2], meta_out["token_to_req"], sel_in[4],
                     meta_out["logical_positions"]]
+        built_at = lambda i: [sel_at(i)[0], sel_at(i)[1], sel_at(i)[2]] + built_in[3:]  # noqa: E731
 
         def build_metadata():
             qsa.qsa_build_metadata(qsl, sel_in[4], sel_in[2], R, max_num_work=R, out=meta_out,
                                    workspace=meta_ws)
 
-        def select_stage(mark=None):
+        def select_stage(i, mark=None):
             build_metadata()
             if mark is not None:
                 mark.record(stream)
-            select_fn(*built_in, out=idx, workspace=sel_ws)
+            select_fn(*built_at(i), out=idx, workspace=sel_ws)
 
         def step(i):
             k, v = kv_views[i % len(kv_views)]
             build_metadata()
-            decode_fn(*built_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
+            decode_fn(*built_at(i), q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
     elif two_pass:
         wt = d(head_w)
         logits_width = w.block_table.shape[1] * 128
@@ -626,8 +649,8 @@ def main() -> int:
         topk_ws = torch.zeros(max(1, qsa.topk_per_row_workspace_bytes(R, logits_width)),
                               dtype=torch.uint8, device=dev)
 
-        def select_stage(mark=None):
-            qsa.qsa_paged_logits(*sel_in, weights=wt, logits=logits)
+        def select_stage(i, mark=None):
+            qsa.qsa_paged_logits(*sel_at(i), weights=wt, logits=logits)
             if mark is not None:
                 mark.record(stream)
             qsa.qsa_topk_per_row(logits, sel_in[3], sel_in[4], sel_in[5], out=idx,
@@ -635,15 +658,15 @@ def main() -> int:
 
         def step(i):
             k, v = kv_views[i % len(kv_views)]
-            select_stage()
+            select_stage(i)
             qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
     else:
-        def select_stage(mark=None):
-            select_fn(*sel_in, out=idx, workspace=sel_ws)
+        def select_stage(i, mark=None):
+            select_fn(*sel_at(i), out=idx, workspace=sel_ws)
 
         def step(i):
             k, v = kv_views[i % len(kv_views)]
-            decode_fn(*sel_in, q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
+            decode_fn(*sel_at(i), q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
 
     def timed_steps(lead_in: bool) -> float:
         """ms per step over exactly K decode steps between two events, after a
@@ -679,7 +702,7 @@ def main() -> int:
     for i in range(args.steps):
         k, v = kv_views[i % len(kv_views)]
         events[i][0].record(stream)
-        select_stage(mark=events[i][3] if (two_pass or meta) else None)
+        select_stage(i, mark=events[i][3] if (two_pass or meta) else None)
         events[i][1].record(stream)
         qsa.qsa_sparse_attn(q_attn, k, v, idx, scale, out=out, workspace=att_ws)
         events[i][2].record(stream)
@@ -701,8 +724,9 @@ def main() -> int:
         fused_idx = torch.empty_like(idx)
         qsa.qsa_select_weighted(sel_in[0], wt, *sel_in[1:], out=fused_idx, workspace=sel_ws)
         fused_ev[0].record(stream)
-        for _ in range(args.steps):
-            qsa.qsa_select_weighted(sel_in[0], wt, *sel_in[1:], out=fused_idx, workspace=sel_ws)
+        for i in range(args.steps):
+            qsa.qsa_select_weighted(sel_in[0], wt, *sel_at(i)[1:], out=fused_idx,
+                                    workspace=sel_ws)
         fused_ev[1].record(stream)
         torch.cuda.synchronize()
         extra = {"logits_ms": round(float(np.mean(logits_ms)), 4),
@@ -714,11 +738,10 @@ def main() -> int:
         # the same selection with the queries passed row by row, for comparison
         flat_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         flat_idx = torch.empty_like(idx)
-        flat_in = [q_rows] + sel_in[1:]
-        select_fn(*flat_in, out=flat_idx, workspace=sel_ws)
+        select_fn(q_rows, *sel_in[1:], out=flat_idx, workspace=sel_ws)
         flat_ev[0].record(stream)
-        for _ in range(args.steps):
-            select_fn(*flat_in, out=flat_idx, workspace=sel_ws)
+        for i in range(args.steps):
+            select_fn(q_rows, *sel_at(i)[1:], out=flat_idx, workspace=sel_ws)
         flat_ev[1].record(stream)
         torch.cuda.synchronize()
         extra["select_row_by_row_ms"] = round(flat_ev[0].elapsed_time(flat_ev[1]) / args.steps, 4)
@@ -778,12 +801,12 @@ def main() -> int:
         sel_roof_bytes = logits_algorithmic_bytes(w.seq_lens, w.query_pos, w.token_to_req,
                                                   logits_width)
         sel_roof_ms = back_to_back_ms(
-            lambda i: qsa.qsa_paged_logits(*sel_in, weights=wt, logits=logits))
+            lambda i: qsa.qsa_paged_logits(*sel_at(i), weights=wt, logits=logits))
         sel_kernel = "qsa_paged_logits (qsa_select_chunk_kernel, logits out)"
     else:
         sel_roof_bytes = sel_bytes
-        sel_roof_ms = back_to_back_ms(lambda i: select_fn(*(built_in if meta else sel_in), out=idx,
-                                                          workspace=sel_ws))
+        sel_roof_ms = back_to_back_ms(lambda i: select_fn(*(built_at(i) if meta else sel_at(i)),
+                                                          out=idx, workspace=sel_ws))
         sel_kernel = (("qsa_select_fp8" if fp8 else "qsa_select") + " (qsa_select_chunk_kernel" +
                       (" + qsa_select_merge_kernel)" if plan_chunks else ")"))
     att_roof_ms = back_to_back_ms(
@@ -839,7 +862,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "e4m3 keys x f16 queries, f16 attention" if fp8 else "f16",
         "data": data,
-        "config": {**workload_config(w, len(kv_sets)), "rows_per_run": run},
+        "config": {**workload_config(w, len(kv_sets), len(sel_sets)), "rows_per_run": run},
         "roofline": dominant,
         "stages": {"select_ms": round(sel_avg_s * 1e3, 4), "attention_ms": round(att_avg_s * 1e3, 4),
                    # per-step event times of the instrumented pass (K samples each)
