@@ -553,6 +553,15 @@ def test_launch_size_limits():
     g, at, aws, awsb, _ = attn_args(R=(1 << 25))
     assert call_attn(at, 0, 0) == SHAPE
     assert b"exceed one launch" in B.library().qsa_last_error()
+    # top-k per row, one 1024-thread workgroup per row of <= 32768 columns:
+    # 2^22 rows x 1024 threads = 2^32 work-items, one more than a launch holds
+    f = Fake()
+    R, Wl = 1 << 22, 100
+    lg = mk(f, B.F32, (R, Wl), 4)
+    t2r, sl, qp = mk(f, B.I32, (R,), 4), mk(f, B.I32, (2,), 4), mk(f, B.I64, (R,), 8)
+    out = mk(f, B.I32, (R, 2051), 4)
+    assert call_topk(lg, t2r, sl, qp, out, 0, 0) == SHAPE
+    assert b"exceed one launch" in B.library().qsa_last_error()
     # attention: a batch this large runs one split per row (no partials, so
     # no workspace), whose grid of padded rows always fits one launch
     assert B.sparse_attn_workspace_bytes(1 << 30) == 0
