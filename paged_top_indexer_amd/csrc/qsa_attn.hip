@@ -147,24 +147,7 @@ __device__ void select_row(const FusedSelect& f, int64_t r, const Row& row, SelP
     kand &= x;
     kor |= x;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
-    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
-  }
-  if ((tid & 63) == 0) {
-    sm.red_and[tid >> 6] = kand;
-    sm.red_or[tid >> 6] = kor;
-  }
-  __syncthreads();
-  uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    all_and &= sm.red_and[w];
-    all_or |= sm.red_or[w];
-  }
-  const uint32_t differ = all_and ^ all_or;
-  const int shift = differ ? __builtin_clz(differ) : 0;  // bits every key shares
+  const int shift = shared_lead_bits<NT>(kand, kor, sm.red_and, sm.red_or);
   auto lds_key = [&](int i) { return sm.keys[i] << shift; };
   auto block_of = [&](int i) { return sm.blocks[i]; };
   uint32_t T = 0, bcut = 0xFFFFFFFFu;

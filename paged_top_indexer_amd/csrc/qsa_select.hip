@@ -960,24 +960,7 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
       kand &= x;
       kor |= x;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
-      kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
-    }
-    if ((tid & 63) == 0) {
-      sm.red_and[tid >> 6] = kand;
-      sm.red_or[tid >> 6] = kor;
-    }
-    __syncthreads();
-    uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
-#pragma unroll
-    for (int w = 0; w < kMergeThreads / 64; ++w) {
-      all_and &= sm.red_and[w];
-      all_or |= sm.red_or[w];
-    }
-    const uint32_t differ = all_and ^ all_or;
-    const int shift = differ ? __builtin_clz(differ) : 0;  // bits every key shares
+    const int shift = shared_lead_bits<kMergeThreads>(kand, kor, sm.red_and, sm.red_or);
     const int n_list = best_n + nb;
     const int kk = min(k, n_list);
     auto lds_key = [&](int i) { return sm.keys[i] << shift; };
@@ -1053,24 +1036,7 @@ __global__ __launch_bounds__(kRowTopkThreads) void qsa_topk_row_kernel(SelectPar
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
-    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
-  }
-  if ((tid & 63) == 0) {
-    sm.red_and[tid >> 6] = kand;
-    sm.red_or[tid >> 6] = kor;
-  }
-  __syncthreads();
-  uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
-#pragma unroll
-  for (int w = 0; w < kRowTopkThreads / 64; ++w) {
-    all_and &= sm.red_and[w];
-    all_or |= sm.red_or[w];
-  }
-  const uint32_t differ = all_and ^ all_or;
-  const int shift = differ ? __builtin_clz(differ) : 0;  // bits every key shares
+  const int shift = shared_lead_bits<kRowTopkThreads>(kand, kor, sm.red_and, sm.red_or);
   auto lds_key = [&](int i) { return sm.keys[i] << shift; };
   auto block_of = [&](int i) { return (uint32_t)i; };
   uint32_t T = 0, bcut = 0xFFFFFFFFu;  // k == n: every key is taken

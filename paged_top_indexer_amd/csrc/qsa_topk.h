@@ -77,6 +77,36 @@ __device__ inline Row row_extent(const int32_t* token_to_req, int64_t num_reqs,
   return row_from(req, qpos, seq_len, num_reqs, max_visible, chunk_blocks);
 }
 
+// Block-wide: how many leading bits every key of a list shares, from each
+// thread's AND and OR of the keys it read (red_and, red_or: one LDS word per
+// wave).  Keys shifted left by it keep their order and their ties, and a
+// list of one row's best keys -- which share their sign and most of their
+// exponent -- spreads over the first radix digit instead of landing in a
+// few bins whose LDS atomics would serialise.  All NT threads call; ends
+// after a barrier.
+template <int NT>
+__device__ __forceinline__ int shared_lead_bits(uint32_t kand, uint32_t kor, uint32_t* red_and,
+                                                uint32_t* red_or) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
+    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red_and[threadIdx.x >> 6] = kand;
+    red_or[threadIdx.x >> 6] = kor;
+  }
+  __syncthreads();
+  uint32_t all_and = 0xFFFFFFFFu, all_or = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    all_and &= red_and[w];
+    all_or |= red_or[w];
+  }
+  const uint32_t differ = all_and ^ all_or;
+  return differ ? __builtin_clz(differ) : 0;
+}
+
 // Radix digits of a 32-bit key, most significant first: 11, 11 and 10 bits.
 __device__ __forceinline__ uint32_t digit0(uint32_t key) { return key >> 21; }
 
