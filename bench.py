@@ -762,12 +762,13 @@ def main() -> int:
     # kernel launches of one timed step at these shapes (the committed kernel
     # traces show one call of each per step).  This mirrors the library's
     # plans: rows of several chunks need a merge (a selection workspace),
-    # except in a decode step whose attention takes 12-wave workgroups
-    # (24-256 rows with at least two 16-position tiles per wave), which
-    # selects them itself; a top-k per row over at most 32768 columns is one
-    # kernel; several splits per row need a combine (an attention workspace).
+    # except in a decode step whose attention takes 12-wave workgroups (up
+    # to 256 rows), which selects them itself (every workload here keeps a
+    # row's candidates within the 8192 the attention workgroup holds); a
+    # top-k per row over at most 32768 columns is one kernel; several splits
+    # per row need a combine (an attention workspace).
     plan_chunks = qsa.select_workspace_bytes(R, w.block_table.shape[1]) > 0
-    row_waves = 0 < R <= 256 and (256 // R) * 16 * 12 < qsa.OUT_WIDTH
+    row_waves = 0 < R <= 256
     combine = ["qsa_attn_combine_kernel"] if qsa.sparse_attn_workspace_bytes(R) > 0 else []
     if two_pass:
         topk = (["qsa_topk_row_kernel"] if logits_width <= 32768 else

@@ -422,12 +422,12 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
     }
   }
   if (sv.rows == 0) return QSA_OK;
-  const qsa::SelectPlan splan = qsa::plan_select(sv.rows, sv.width, sv.group);
-  const qsa::AttnPlan aplan = qsa::plan_attn(av.rows);
+  const qsa::DecodePlan plan = qsa::plan_decode(sv.rows, sv.width, sv.group);
+  const qsa::SelectPlan& splan = plan.select;
+  const qsa::AttnPlan& aplan = plan.attn;
   QSA_TRY(check_select_grid("selection", splan, plan_groups(splan, sv.rows)));
   QSA_TRY(check_attn_grid(av.rows, aplan));
-  const size_t sel_bytes = align256(splan.bytes);
-  const size_t need = sel_bytes + aplan.bytes;
+  const size_t need = plan.bytes;
   if (static_ws) {
     if (need > qsa::kStaticScratchBytes) {
       return fail(QSA_ERR_WORKSPACE,
@@ -459,8 +459,7 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   // Fused path: with whole-CU attention workgroups and rows whose
   // candidates fit in LDS, the attention kernel selects each multi-chunk
   // row itself instead of a merge launch.
-  const bool fused = aplan.waves == qsa::kAttnRowWaves && splan.chunks_per_row > 1 &&
-                     splan.chunks_per_row * splan.cand_cap <= qsa::kFusedCands;
+  const bool fused = plan.fused;
   qsa::FusedSelect fs;
   if (fused) {
     char* ws = static_cast<char*>(workspace);
@@ -483,7 +482,7 @@ int decode_impl(const qsa_tensor* q_sel, const qsa_tensor* kcache, const qsa_ten
   a.kv = static_cast<const uint16_t*>(k->data);
   a.indices = static_cast<const int32_t*>(indices->data);
   a.out = static_cast<uint16_t*>(out->data);
-  a.workspace = aplan.bytes ? static_cast<char*>(workspace) + sel_bytes : nullptr;
+  a.workspace = aplan.bytes ? static_cast<char*>(workspace) + plan.attn_off : nullptr;
   a.rows = av.rows;
   a.num_tokens = av.tokens;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
@@ -539,8 +538,12 @@ QSA_API size_t qsa_sparse_attn_workspace_bytes(int64_t rows) {
 
 QSA_API size_t qsa_decode_step_workspace_bytes(int64_t rows, int64_t table_width) {
   if (rows <= 0) return 0;
-  return align256(qsa_select_workspace_bytes(rows, table_width)) +
-         qsa_sparse_attn_workspace_bytes(rows);
+  // enough for every row grouping
+  size_t bytes = 0;
+  for (int group = 1; group <= qsa::kMaxGroup; ++group) {
+    bytes = std::max(bytes, qsa::plan_decode(rows, table_width, group).bytes);
+  }
+  return bytes;
 }
 
 QSA_API int qsa_select(const qsa_tensor* q, const qsa_tensor* kcache, const qsa_tensor* block_table,

@@ -20,9 +20,9 @@ constexpr int kAttDim = 256;
 constexpr int kKvRow = 512;
 constexpr int kKvPageTokens = 512;
 
-// Row-indexed grids are padded to whole groups of kRowGroup rows on each of
-// the kXcds XCDs (see qsa_device.h).  A dispatch holds fewer than 2^32
-// work-items (workgroups x threads per workgroup).
+// Row-indexed grids place kRowGroup consecutive rows together on the kXcds
+// XCDs (see qsa_device.h).  A dispatch holds fewer than 2^32 work-items
+// (workgroups x threads per workgroup).
 constexpr int kXcds = 8;
 constexpr int kRowGroup = 4;
 constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
@@ -47,8 +47,25 @@ static_assert(kMaxAttnSplits <= kCombineMaxSplits, "combine holds every split's 
 // copy per GPU, held until the process ends).
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 
+// Whether a row-indexed grid over `units` rows (or, for the chunk kernel's
+// runs of a request's rows, runs of `group` rows) deals cells of kRowGroup
+// rows x one column to the XCDs (see qsa_device.h): every grid but a single
+// row and 32 or more runs, which are placed by XCD groups.
+constexpr bool deal_cells(int64_t units, int group) {
+  return units > 1 && (group == 1 || units < kXcds * kRowGroup);
+}
+
 constexpr int64_t padded_rows(int64_t rows) {
   return (rows + kXcds * kRowGroup - 1) / (kXcds * kRowGroup) * (kXcds * kRowGroup);
+}
+
+// Workgroups of a row-indexed grid of `cols` columns over `units` rows (or
+// runs of `group` rows): whole rounds of cells on all XCDs, or whole XCD
+// groups.  Never more than padded_rows(units) * cols.
+constexpr int64_t grid_blocks(int64_t units, int64_t cols, int group) {
+  if (!deal_cells(units, group)) return padded_rows(units) * cols;
+  const int64_t cells = (units + kRowGroup - 1) / kRowGroup * cols;
+  return (cells + kXcds - 1) / kXcds * (kXcds * kRowGroup);
 }
 
 // Query rows scored together against one key stream: 4 rows x 4 heads fill
@@ -81,8 +98,8 @@ SelectPlan plan_select(int64_t rows, int64_t table_width, int group = 1);
 
 // Launch plan of the attention kernel: `splits` workgroups per row, each
 // covering `split_positions` index positions with `waves` waves (tiles of
-// 16 positions): 4 waves per split, or kAttnRowWaves (about one workgroup
-// per CU, for 24 to 256 rows).
+// 16 positions): kAttnRowWaves (about one workgroup per CU) up to 256
+// rows, 4 waves per split above.
 struct AttnPlan {
   int split_positions = 128;
   int splits = 1;
@@ -93,6 +110,19 @@ struct AttnPlan {
 };
 
 AttnPlan plan_attn(int64_t rows);
+
+// Plans of the decode step: the selection's, the attention's, whether the
+// attention launch finishes the selection (no merge launch), and the
+// workspace (the selection's at 0, the attention's at attn_off).
+struct DecodePlan {
+  SelectPlan select;
+  AttnPlan attn;
+  bool fused = false;
+  size_t attn_off = 0;
+  size_t bytes = 0;
+};
+
+DecodePlan plan_decode(int64_t rows, int64_t table_width, int group);
 
 // Arguments of the selection family.  Scores come from fp16 keys (kcache),
 // e4m3 keys (kcodes + kscale) or a logits matrix (logits_in); they are

@@ -57,10 +57,11 @@ SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
   return p;
 }
 
-// Split length: enough splits for about one resident round of attention
-// workgroups over the batch (3 per CU on 256 CUs), in multiples of 64 index
-// positions (each wave loads its indices 64 at a time), at most 33 splits of
-// 64 positions; a batch of 768 rows or more gets one split per row.
+// Splits: up to 256 rows, whole-CU workgroups (below); above, 4-wave
+// workgroups, enough splits for about one resident round of them over the
+// batch (3 per CU on 256 CUs) in multiples of 64 index positions (each wave
+// loads its indices 64 at a time) -- a batch of 768 rows or more gets one
+// split per row.
 AttnPlan plan_attn(int64_t rows) {
   AttnPlan p;
   constexpr int64_t kResident = 768;
@@ -71,13 +72,11 @@ AttnPlan plan_attn(int64_t rows) {
   p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
   p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
   // Up to 256 rows: about one workgroup of kAttnRowWaves waves per CU
-  // (splits = 256 / rows), each wave a whole number of 16-position tiles;
-  // 256 rows take one workgroup per row and need no combine.  Only while
-  // that leaves each wave at least two tiles (24 rows or more): with one
-  // tile per wave the 4-wave plan is faster (20 rows: 9% on the decode
-  // step; 24-48 rows gain 5-9% over it).
+  // (splits = 256 / rows, at most 11 of 192 positions), each wave a whole
+  // number of 16-position tiles; 256 rows take one workgroup per row and
+  // need no combine.
   constexpr int kUnit = 16 * kAttnRowWaves;
-  if (rows > 0 && rows <= 256 && std::max<int64_t>(1, 256 / rows) * kUnit < kOutWidth) {
+  if (rows > 0 && rows <= 256) {
     const int splits = (int)std::max<int64_t>(1, 256 / rows);
     p.waves = kAttnRowWaves;
     p.split_positions = kUnit * ((kOutWidth + splits * kUnit - 1) / (splits * kUnit));
@@ -92,6 +91,21 @@ AttnPlan plan_attn(int64_t rows) {
   off = align256(off + (size_t)rows * p.splits * kAttHeads * 2 * sizeof(float));
   p.bytes = p.splits > 1 ? off : 0;
   return p;
+}
+
+// The selection runs inside the attention launch when every multi-chunk
+// row's candidates fit the attention workgroup's LDS (at most kFusedCands)
+// and the attention takes whole-CU workgroups (up to 256 rows).
+DecodePlan plan_decode(int64_t rows, int64_t table_width, int group) {
+  DecodePlan d;
+  d.select = plan_select(rows, table_width, group);
+  d.attn = plan_attn(rows);
+  d.fused = d.select.chunks_per_row > 1 &&
+            d.select.chunks_per_row * d.select.cand_cap <= kFusedCands &&
+            d.attn.waves == kAttnRowWaves;
+  d.attn_off = align256(d.select.bytes);
+  d.bytes = d.attn_off + d.attn.bytes;
+  return d;
 }
 
 }  // namespace qsa

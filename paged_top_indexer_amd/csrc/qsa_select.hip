@@ -663,8 +663,9 @@ __global__ __launch_bounds__(kChunkThreads, (kSrc == kSrcE4M3 && kGroup > 1) ? 3
 qsa_select_chunk_kernel(SelectParams p) {
   __shared__ ChunkSmem sm;
   const int tid = threadIdx.x;
-  const RowCol id = row_col_of_block(blockIdx.x, p.chunks_per_row);  // XCD-aware placement
   const int group = kGroup == 1 ? 1 : p.group;
+  const RowCol id =
+      row_col_of_block(blockIdx.x, p.chunks_per_row, (p.rows + group - 1) / group, group);
   const int64_t r0 = id.row * group;
   const int64_t chunk = id.col;
   if (r0 >= p.rows) return;
@@ -883,8 +884,9 @@ struct MergeSmem {
 __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectParams p) {
   __shared__ MergeSmem sm;
   const int tid = threadIdx.x;
-  // row s % group of the chunk kernel's (s / group)-th group on this XCD:
-  // a row is merged on the XCD that scored it
+  // rows by XCD groups: row s % group of the (s / group)-th run of rows on
+  // this XCD (where the chunk kernel places its runs so too, a row is merged
+  // on the XCD that scored it)
   const int64_t s = blockIdx.x / kXcds;
   const int64_t r = row_on_xcd(blockIdx.x % kXcds, s / p.group) * p.group + s % p.group;
   if (r >= p.rows) return;
@@ -1091,7 +1093,7 @@ SelectParams make_params(const SelectArgs& a, const SelectPlan& plan) {
 template <int kSrc, bool kLogitsOut>
 void launch_chunks(const SelectParams& p, hipStream_t s) {
   const int64_t groups = (p.rows + p.group - 1) / p.group;
-  const dim3 grid((unsigned)(p.chunks_per_row * padded_rows(groups)));
+  const dim3 grid((unsigned)grid_blocks(groups, p.chunks_per_row, p.group));
   if constexpr (kSrc != kSrcLogits) {  // (logits rows are never grouped)
     if (p.group > 1) {
       hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, kMaxGroup>), grid,

@@ -133,12 +133,13 @@ def test_inputs_unchanged_and_fail_closed():
     assert torch.all(out == 7.0)
 
 
-# Batch sizes across the split plans: 4-wave workgroups with 33 splits of
-# 64 positions for a single row and fewer, longer splits as rows grow (up
-# to 23 rows, and from 257 rows up: one split per row, no combine, from 768
-# rows); 12-wave workgroups from 24 to 256 rows (6 splits of 384 positions
-# at 24 rows, 4 at 64, one per row at 256).
-SPLIT_BATCHES = [1, 2, 5, 16, 23, 24, 33, 64, 100, 256, 300, 767, 768, 900]
+# Batch sizes across the split plans and workgroup placements: 12-wave
+# workgroups up to 256 rows (11 splits of 192 positions up to 23 rows, 6 of
+# 384 at 24 rows, 4 at 64, one per row at 256), one row on one XCD and
+# larger batches dealt over the XCDs in cells of 4 rows; 4-wave workgroups
+# from 257 rows up (fewer, longer splits as rows grow; one split per row,
+# no combine, from 768 rows).
+SPLIT_BATCHES = [1, 2, 3, 5, 16, 23, 24, 33, 64, 100, 256, 300, 767, 768, 900]
 
 
 @pytest.mark.parametrize("rows", SPLIT_BATCHES)

@@ -74,13 +74,15 @@ def test_multi_token_rows():
     check_attn(out, oracle_attn(orc(), w.q_attn, w.kv, idx, SCALE), "multi-token, every row")
 
 
-@pytest.mark.parametrize("rows", [23, 24])
-def test_fused_boundary_rows(rows):
-    """The first rows of the long-context batch (128K-token rows, N(0,1)):
-    23 rows take 4-wave attention workgroups after a merge launch, 24 rows
-    the 12-wave plan with each row's selection folded into the attention
-    launch.  Every row's selection within the band, every row's attention
-    against the oracle over the GPU's own index row."""
+@pytest.mark.parametrize("rows", [1, 2, 23, 24, 40])
+def test_small_and_uneven_batches(rows):
+    """The first rows of the long-context batch (128K-token rows, N(0,1)),
+    each row's selection folded into whole-CU attention workgroups: one row
+    (all its workgroups on one XCD, 11 splits of 192 positions), 2 to 23
+    rows dealt over the XCDs (11 splits each), 24 and 40 rows (6 splits of
+    384; 40 rows do not fill whole groups of 4 rows per XCD).  Every row's
+    selection within the band, every row's attention against the oracle
+    over the GPU's own index row."""
     w = wl.long_context(0, rows=rows)
     inputs = w.select_inputs()
     banner(f"decode long_context rows={rows}")
@@ -88,6 +90,29 @@ def test_fused_boundary_rows(rows):
     want_idx = oracle_select(orc(), inputs)
     check_select_band(idx, want_idx, orc(), inputs, range(rows))
     check_attn(out, oracle_attn(orc(), w.q_attn, w.kv, idx, SCALE), f"rows={rows}, every row")
+
+
+def test_small_batch_over_fused_candidates():
+    """Three rows of 262,656 tokens (513 pages each): 17 chunks of 32 pages
+    leave 8704 candidates per row, more than an attention workgroup holds,
+    so the merge launch selects (two batches of candidates) and 4-wave
+    attention workgroups follow, all dealt over the XCDs.  N(0,1) keys of
+    the long-context cache behind a seeded page permutation; every row's
+    selection within the band, the attention against the oracle."""
+    base = wl.long_context(0, rows=3)
+    rng = np.random.default_rng(11)
+    L, W = 262656, 513
+    bt = rng.permutation(base.kcache.shape[0])[:3 * W].astype(np.int32).reshape(3, W)
+    t2r, sl, qp = wl.decode_rows([L] * 3)
+    kv = wl.normal_f16(rng, (W, wl.TOKENS_PER_PAGE, wl.KV_ROW))
+    w = wl.Workload("long_rows_R3_L262656", 0, base.q_sel, base.kcache, bt, t2r, sl, qp,
+                    base.q_attn, kv)
+    inputs = w.select_inputs()
+    banner("decode 3 rows of 262656 tokens (8704 candidates per row)")
+    idx, out = decode_gpu(w)
+    want_idx = oracle_select(orc(), inputs)
+    check_select_band(idx, want_idx, orc(), inputs, range(3))
+    check_attn(out, oracle_attn(orc(), w.q_attn, w.kv, idx, SCALE), "long rows, every row")
 
 
 @pytest.mark.parametrize("rows,lo,hi", [(4096, 0, 1500), (800, 4000, 12000)],
