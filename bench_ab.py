@@ -9,6 +9,12 @@ once more on the same inputs and their outputs are compared.
 
     python bench_ab.py --baseline OLD.so [--candidate NEW.so] [--workload NAME]
                        [--op decode_step|select|attention] [--pairs 10] [--rows R]
+                       [--graph]
+
+With --graph each build's unit of calls is captured once in a HIP graph and
+every unit is one replay: device time only, for calls shorter than the
+host's ~12 us of argument marshalling per call from Python (a single
+row's attention), which eager units would time instead.
 
 The candidate defaults to the tree's libqsa_amd.so; a baseline of an
 earlier revision is built with `python -m paged_top_indexer_amd.build --rev
@@ -51,6 +57,8 @@ def main() -> int:
                          "x 4 rows; default 256)")
     ap.add_argument("--kv-copies", type=int, default=8)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="time each unit as one replay of a HIP graph of its calls")
     args = ap.parse_args()
 
     import torch
@@ -118,14 +126,29 @@ def main() -> int:
 
     stream = torch.cuda.current_stream(dev)
     counter = [0]
+    graphs = {}
+    if args.graph:
+        for name in libs:
+            _binding.use_library(libs[name])
+            call(name, 0)  # outside the capture first
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(calls):
+                    call(name, i)
+            graphs[name] = g
+        torch.cuda.synchronize()
 
     def unit(name) -> float:
         _binding.use_library(libs[name])
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         ev[0].record(stream)
-        for _ in range(calls):
-            call(name, counter[0])
-            counter[0] += 1
+        if args.graph:
+            graphs[name].replay()
+        else:
+            for _ in range(calls):
+                call(name, counter[0])
+                counter[0] += 1
         ev[1].record(stream)
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / calls
@@ -157,7 +180,7 @@ def main() -> int:
     diff_out = float(np.max(np.abs(outs["baseline"][1].astype(np.float64) -
                                    outs["candidate"][1].astype(np.float64))))
     res = {"workload": w.name, "rows": w.rows, "op": args.op, "calls_per_unit": calls,
-           "warmup_units": args.warmup_units, "pairs": args.pairs,
+           "warmup_units": args.warmup_units, "pairs": args.pairs, "graph": args.graph,
            "baseline": {"lib": libs["baseline"], "mean_ms": round(float(np.mean(base)), 5),
                         "median_ms": round(float(np.median(base)), 5)},
            "candidate": {"lib": libs["candidate"], "mean_ms": round(float(np.mean(cand)), 5),

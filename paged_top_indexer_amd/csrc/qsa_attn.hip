@@ -53,6 +53,7 @@ struct AttnParams {
   float scale_log2;
   int splits;
   int split_positions;
+  Placement place;  // of the attention (rows x splits) and combine (rows x heads) grids
   FusedSelect sel;  // the fused path's selection inputs
 };
 
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64 * kWaves) void qsa_attn_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const RowCol id = row_col_of_block(blockIdx.x, p.splits, p.rows, 1);  // XCD-aware placement
+  const RowCol id = row_col_of_block(blockIdx.x, p.splits, p.place);
   const int64_t r = id.row;
   const int split = (int)id.col;
   if (r >= p.rows) return;
@@ -366,7 +367,7 @@ constexpr int kMaxSplits = kCombineMaxSplits;  // >= every plan's splits (qsa_la
 __global__ __launch_bounds__(kThreads) void qsa_attn_combine_kernel(AttnParams p) {
   __shared__ float weight[kMaxSplits];
   __shared__ float total;
-  const RowCol id = row_col_of_block(blockIdx.x, kAttHeads, p.rows, 1);
+  const RowCol id = row_col_of_block(blockIdx.x, kAttHeads, p.place);
   const int64_t r = id.row;
   const int h = (int)id.col;
   const int tid = threadIdx.x;
@@ -429,23 +430,23 @@ int launch_attn(const AttnArgs& a, const AttnPlan& plan, void* stream) {
   p.scale_log2 = a.scale_log2;
   p.splits = plan.splits;
   p.split_positions = plan.split_positions;
+  p.place = attn_placement(a.rows);
+  const dim3 grid((unsigned)grid_blocks(a.rows, plan.splits, p.place));
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (plan.waves == kAttnRowWaves && a.fused) {
-    hipLaunchKernelGGL((qsa_attn_kernel<kAttnRowWaves, true>),
-                       dim3((unsigned)grid_blocks(a.rows, plan.splits, 1)),
-                       dim3(64 * kAttnRowWaves), 0, s, p);
+    hipLaunchKernelGGL((qsa_attn_kernel<kAttnRowWaves, true>), grid, dim3(64 * kAttnRowWaves), 0,
+                       s, p);
   } else if (plan.waves == kAttnRowWaves) {
-    hipLaunchKernelGGL((qsa_attn_kernel<kAttnRowWaves, false>),
-                       dim3((unsigned)grid_blocks(a.rows, plan.splits, 1)),
-                       dim3(64 * kAttnRowWaves), 0, s, p);
+    hipLaunchKernelGGL((qsa_attn_kernel<kAttnRowWaves, false>), grid, dim3(64 * kAttnRowWaves), 0,
+                       s, p);
   } else {
-    hipLaunchKernelGGL((qsa_attn_kernel<kAttnThreads / 64, false>),
-                       dim3((unsigned)grid_blocks(a.rows, plan.splits, 1)), dim3(kAttnThreads),
-                       0, s, p);
+    hipLaunchKernelGGL((qsa_attn_kernel<kAttnThreads / 64, false>), grid, dim3(kAttnThreads), 0,
+                       s, p);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.splits == 1) return (int)err;
-  hipLaunchKernelGGL(qsa_attn_combine_kernel, dim3((unsigned)grid_blocks(a.rows, kAttHeads, 1)),
+  hipLaunchKernelGGL(qsa_attn_combine_kernel,
+                     dim3((unsigned)grid_blocks(a.rows, kAttHeads, p.place)),
                      dim3(kThreads), 0, s, p);
   return (int)hipGetLastError();
 }

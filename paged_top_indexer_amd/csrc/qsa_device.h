@@ -25,41 +25,35 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 
 // Workgroups are dealt to the XCDs round-robin by id (each XCD has its own
 // L2).  A row-indexed grid of `cols` columns (a row's chunks, attention
-// splits or heads) places its work in one of two ways, decided by
-// deal_cells (qsa_launch.h) the same way in every kernel that sees the same
-// rows:
-//  - Cells dealt over the XCDs (any batch of more than one row; fewer than 32
-//    runs of rows): kRowGroup consecutive rows x one column form a cell, cell
-//    c (row-major) goes to XCD c % 8, and its rows take consecutive slots
-//    there.  A row's columns spread over all XCDs, so every XCD gets an
-//    equal share of the work whatever the rows' lengths and however few the
-//    rows, while the same column of neighbouring rows (a request's
-//    speculative-decode rows, which read the same keys) meets in one L2.
-//  - XCD groups (a single row; 32 or more runs of a request's rows): groups
-//    of kRowGroup consecutive rows, group g on XCD g % 8 with all its
-//    columns.  The kernels that work on one row then meet on one XCD and
-//    hand their data over through its L2 (the merge places its rows this
-//    way), and the runs of one request read their keys through one L2.
+// splits or heads) places its work in one of two ways (Placement,
+// qsa_launch.h):
+//  - Cells dealt over the XCDs: cell_rows consecutive rows x one column form
+//    a cell, cell c (row-major) goes to XCD c % 8, and its rows take
+//    consecutive slots there.  A row's columns spread over the XCDs, so
+//    every XCD gets an equal share of the work whatever the rows' lengths
+//    and however few the rows; cells of several rows keep the same column of
+//    neighbouring rows (a request's speculative-decode rows, which read the
+//    same keys) in one L2.
+//  - XCD groups: groups of kRowGroup consecutive rows, group g on XCD g % 8
+//    with all its columns, so the kernels that work on one row meet on one
+//    XCD and hand their data over through its L2.
 // Workgroups mapped past the last row exit.
-// (kXcds, kRowGroup, deal_cells and grid_blocks are in qsa_launch.h, shared
-// with the host code that sizes the grids.)
 __device__ __forceinline__ int64_t row_on_xcd(int64_t xcd, int64_t s) {
   return kRowGroup * (kXcds * (s / kRowGroup) + xcd) + s % kRowGroup;
 }
 
-// (row, column) of workgroup b of a grid of grid_blocks(units, cols, group)
-// workgroups: `cols` per row over `units` rows (or runs of `group` rows).
+// (row, column) of workgroup b of a grid of grid_blocks(units, cols, pl)
+// workgroups, `cols` per row.
 struct RowCol {
   int64_t row, col;
 };
 
-__device__ __forceinline__ RowCol row_col_of_block(int64_t b, int64_t cols, int64_t units,
-                                                   int group) {
+__device__ __forceinline__ RowCol row_col_of_block(int64_t b, int64_t cols, Placement pl) {
   const int64_t xcd = b % kXcds;
   const int64_t slot = b / kXcds;
-  if (deal_cells(units, group)) {
-    const int64_t cell = slot / kRowGroup * kXcds + xcd;
-    return {cell / cols * kRowGroup + slot % kRowGroup, cell % cols};
+  if (pl.deal) {
+    const int64_t cell = slot / pl.cell_rows * kXcds + xcd;
+    return {cell / cols * pl.cell_rows + slot % pl.cell_rows, cell % cols};
   }
   return {row_on_xcd(xcd, slot / cols), slot % cols};
 }

@@ -57,12 +57,13 @@ SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
   return p;
 }
 
-// Splits: up to 256 rows, whole-CU workgroups (below); above, 4-wave
-// workgroups, enough splits for about one resident round of them over the
-// batch (3 per CU on 256 CUs) in multiples of 64 index positions (each wave
-// loads its indices 64 at a time) -- a batch of 768 rows or more gets one
-// split per row.
-AttnPlan plan_attn(int64_t rows) {
+// Splits: whole-CU workgroups (below) for 8 to 256 rows, and for fewer rows
+// when asked (whole_cu: a decode step that selects inside the attention
+// launch); otherwise 4-wave workgroups, enough splits for about one
+// resident round of them over the batch (3 per CU on 256 CUs) in multiples
+// of 64 index positions (each wave loads its indices 64 at a time) -- 33
+// splits of 64 for a single row, one split per row from 768 rows up.
+AttnPlan plan_attn(int64_t rows, bool whole_cu) {
   AttnPlan p;
   constexpr int64_t kResident = 768;
   const int64_t want =
@@ -71,12 +72,13 @@ AttnPlan plan_attn(int64_t rows) {
                : 1;
   p.split_positions = 64 * (int)((kOutWidth + 64 * want - 1) / (64 * want));
   p.splits = (kOutWidth + p.split_positions - 1) / p.split_positions;
-  // Up to 256 rows: about one workgroup of kAttnRowWaves waves per CU
-  // (splits = 256 / rows, at most 11 of 192 positions), each wave a whole
-  // number of 16-position tiles; 256 rows take one workgroup per row and
-  // need no combine.
+  // About one workgroup of kAttnRowWaves waves per CU (splits = 256 / rows,
+  // at most 11 of 192 positions), each wave a whole number of 16-position
+  // tiles; 256 rows take one workgroup per row and need no combine.  Below
+  // 8 rows, 11 such workgroups per row (one tile per wave, 12 waves'
+  // partials merged in LDS) are slower than 33 of 4 waves.
   constexpr int kUnit = 16 * kAttnRowWaves;
-  if (rows > 0 && rows <= 256) {
+  if (rows > 0 && rows <= 256 && (whole_cu || rows >= 8)) {
     const int splits = (int)std::max<int64_t>(1, 256 / rows);
     p.waves = kAttnRowWaves;
     p.split_positions = kUnit * ((kOutWidth + splits * kUnit - 1) / (splits * kUnit));
@@ -99,10 +101,10 @@ AttnPlan plan_attn(int64_t rows) {
 DecodePlan plan_decode(int64_t rows, int64_t table_width, int group) {
   DecodePlan d;
   d.select = plan_select(rows, table_width, group);
-  d.attn = plan_attn(rows);
-  d.fused = d.select.chunks_per_row > 1 &&
-            d.select.chunks_per_row * d.select.cand_cap <= kFusedCands &&
-            d.attn.waves == kAttnRowWaves;
+  const bool fusable = d.select.chunks_per_row > 1 &&
+                       d.select.chunks_per_row * d.select.cand_cap <= kFusedCands;
+  d.attn = plan_attn(rows, fusable);
+  d.fused = fusable && d.attn.waves == kAttnRowWaves;
   d.attn_off = align256(d.select.bytes);
   d.bytes = d.attn_off + d.attn.bytes;
   return d;

@@ -100,6 +100,7 @@ struct SelectParams {
   int chunk_blocks;
   int cand_cap;
   int group;  // consecutive query rows per chunk workgroup (1..4)
+  Placement place;  // of the chunk grid (row groups x chunks)
 };
 
 // The visible blocks V, tail T and chunks of query row r
@@ -664,8 +665,7 @@ qsa_select_chunk_kernel(SelectParams p) {
   __shared__ ChunkSmem sm;
   const int tid = threadIdx.x;
   const int group = kGroup == 1 ? 1 : p.group;
-  const RowCol id =
-      row_col_of_block(blockIdx.x, p.chunks_per_row, (p.rows + group - 1) / group, group);
+  const RowCol id = row_col_of_block(blockIdx.x, p.chunks_per_row, p.place);
   const int64_t r0 = id.row * group;
   const int64_t chunk = id.col;
   if (r0 >= p.rows) return;
@@ -1087,13 +1087,14 @@ SelectParams make_params(const SelectArgs& a, const SelectPlan& plan) {
   p.chunk_blocks = plan.chunk_pages * kPageSlots;
   p.cand_cap = (int)plan.cand_cap;
   p.group = plan.group;
+  p.place = chunk_placement((a.rows + plan.group - 1) / plan.group, plan.group);
   return p;
 }
 
 template <int kSrc, bool kLogitsOut>
 void launch_chunks(const SelectParams& p, hipStream_t s) {
   const int64_t groups = (p.rows + p.group - 1) / p.group;
-  const dim3 grid((unsigned)grid_blocks(groups, p.chunks_per_row, p.group));
+  const dim3 grid((unsigned)grid_blocks(groups, p.chunks_per_row, p.place));
   if constexpr (kSrc != kSrcLogits) {  // (logits rows are never grouped)
     if (p.group > 1) {
       hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, kMaxGroup>), grid,

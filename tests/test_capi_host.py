@@ -58,12 +58,16 @@ def test_workspace_sizes():
     assert B.select_workspace_bytes(4, 256) == 2 * (4 * 32 * 512 * 4)
     # a row that fits one batch already keeps its 1024-workgroup chunks
     assert B.select_workspace_bytes(4, 64) == 2 * (4 * 64 * 128 * 4)
-    # 2 rows: whole-CU attention workgroups, 11 splits of 192 positions --
-    # partials, then (max, sum) rounded up to 256 bytes; the decode step of a
-    # 40-page table adds 40 one-page chunks of 128 candidates per row
-    attn = 2 * 11 * 3 * 256 * 4 + 768
-    assert B.sparse_attn_workspace_bytes(2) == attn
-    assert B.decode_step_workspace_bytes(2, 40) == 2 * (2 * 40 * 128 * 4) + attn
+    # 2 rows: 4-wave attention workgroups, 33 splits of 64 positions --
+    # partials, then (max, sum) rounded up to 256 bytes
+    assert B.sparse_attn_workspace_bytes(2) == 2 * 33 * 3 * 256 * 4 + 1792
+    # the decode step of a 40-page table: 40 one-page chunks of 128
+    # candidates per row (5120 <= 8192), selected inside whole-CU attention
+    # workgroups, 11 splits of 192 positions
+    assert B.decode_step_workspace_bytes(2, 40) == 2 * (2 * 40 * 128 * 4) + (
+        2 * 11 * 3 * 256 * 4 + 768)
+    # 8 rows: whole-CU attention workgroups, 11 splits
+    assert B.sparse_attn_workspace_bytes(8) == 8 * 11 * 3 * 256 * 4 + 2304
     # 300 rows: 4-wave workgroups, 3 splits of 704 positions
     assert B.sparse_attn_workspace_bytes(300) == 300 * 3 * 3 * 256 * 4 + 21760
 

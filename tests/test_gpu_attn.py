@@ -133,13 +133,13 @@ def test_inputs_unchanged_and_fail_closed():
     assert torch.all(out == 7.0)
 
 
-# Batch sizes across the split plans and workgroup placements: 12-wave
-# workgroups up to 256 rows (11 splits of 192 positions up to 23 rows, 6 of
-# 384 at 24 rows, 4 at 64, one per row at 256), one row on one XCD and
-# larger batches dealt over the XCDs in cells of 4 rows; 4-wave workgroups
-# from 257 rows up (fewer, longer splits as rows grow; one split per row,
-# no combine, from 768 rows).
-SPLIT_BATCHES = [1, 2, 3, 5, 16, 23, 24, 33, 64, 100, 256, 300, 767, 768, 900]
+# Batch sizes across the split plans and workgroup placements: 4-wave
+# workgroups below 8 rows (33 splits of 64 positions, fewer and longer as
+# rows grow) and from 257 rows up (one split per row, no combine, from 768
+# rows); 12-wave workgroups from 8 to 256 rows (11 splits of 192 positions
+# up to 23 rows, 6 of 384 at 24 rows, 4 at 64, one per row at 256).  One row
+# sits on one XCD; larger batches are dealt over the XCDs row by row.
+SPLIT_BATCHES = [1, 2, 3, 5, 7, 8, 16, 23, 24, 33, 64, 100, 256, 300, 767, 768, 900]
 
 
 @pytest.mark.parametrize("rows", SPLIT_BATCHES)
