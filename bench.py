@@ -42,9 +42,13 @@ both ends.  The
 steps rotate over distinct KV caches and over block tables that map the
 rows through distinct page permutations of the key cache, as consecutive
 layers would read distinct caches (no step finds its data in the last-level
-cache because an earlier step read it).  A second
-pass runs the two stages through qsa_select and qsa_sparse_attn with events
-between them for the per-stage times and the roofline.  Prints one JSON line.
+cache because an earlier step read it).  The same K steps replayed from a
+HIP graph give the device's time per step without the host's launches
+(stages.ms_per_step_graph: a small batch's calls from Python are bound by
+their argument marshalling).  A second pass runs the two stages through
+qsa_select and qsa_sparse_attn with events between them for the per-stage
+times; each stage's K calls back to back, replayed from a HIP graph, give
+the roofline.  Prints one JSON line.
 The oracle then checks every row of the timed configuration's output (the
 band rule on N(0,1) inputs, bit-exact selection on integer inputs, attention
 within 2e-3 and one fp16 ulp); the exit status is 1 when any row fails.
@@ -668,6 +672,24 @@ def main() -> int:
             k, v = kv_views[i % len(kv_views)]
             decode_fn(*sel_at(i), q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
 
+    def graph_ms(fn) -> float:
+        """ms per call of fn(0..K-1) captured once in a HIP graph and replayed
+        between two events on the launch stream (fn(0) runs once outside the
+        capture first)."""
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        g.replay()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / args.steps
+
     def timed_steps(lead_in: bool) -> float:
         """ms per step over exactly K decode steps between two events, after a
         synchronisation.  lead_in: a ~0.2 ms device sleep is queued between
@@ -694,6 +716,10 @@ def main() -> int:
     wall = time.perf_counter() - t_start
     # the same K steps with the region opening on an idle GPU, for reference
     ms_per_step_cold = timed_steps(lead_in=False)
+    # and captured once in a HIP graph, replayed between two events: the
+    # device's time per step without the host's launches (a small batch's
+    # steps from Python are bound by their ~12 us of argument marshalling)
+    ms_per_step_graph = graph_ms(step)
     clocks = None if args.no_context else gpu_clocks()
 
     # Per-stage times: the same two stages through their own entry points,
@@ -746,8 +772,8 @@ def main() -> int:
         torch.cuda.synchronize()
         extra["select_row_by_row_ms"] = round(flat_ev[0].elapsed_time(flat_ev[1]) / args.steps, 4)
         log(f"selection row by row {extra['select_row_by_row_ms']:.4f} ms")
-    log(f"step {ms_per_step:.4f} ms (cold start {ms_per_step_cold:.4f} ms; wall "
-        f"{wall * 1e3 / args.steps:.4f} ms); stages: select "
+    log(f"step {ms_per_step:.4f} ms (cold start {ms_per_step_cold:.4f} ms, graph-replayed "
+        f"{ms_per_step_graph:.4f} ms; wall {wall * 1e3 / args.steps:.4f} ms); stages: select "
         f"{np.mean(sel_ms):.4f} ms (min {np.min(sel_ms):.4f}), attention {np.mean(att_ms):.4f} ms")
 
     # one more step on the first KV cache (the oracle's) for the parity check
@@ -785,15 +811,10 @@ def main() -> int:
 
     def back_to_back_ms(fn) -> float:
         """Average duration of fn's launches: K calls back to back on the
-        launch stream between two events (no events between the kernels)."""
-        fn(0)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for i in range(args.steps):
-            fn(i)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        return ev[0].elapsed_time(ev[1]) / args.steps
+        launch stream between two events (no events between the kernels),
+        replayed from a HIP graph so that no host launch gap sits between
+        them."""
+        return graph_ms(fn)
 
     # Roofline of each stage: algorithmic bytes per launch / the launch's
     # average duration back to back; the stage that takes longer is the
@@ -885,6 +906,7 @@ def main() -> int:
                    "step_frac_of_peak": round(step_gbs / HBM_PEAK_GBS, 4),
                    "step_frac_of_ceiling": round(step_gbs / ceiling, 4) if ceiling else None,
                    "ms_per_step_cold_start": round(ms_per_step_cold, 4),
+                   "ms_per_step_graph": round(ms_per_step_graph, 4),
                    "timed_entry_point": ("qsa_paged_logits + qsa_topk_per_row + qsa_sparse_attn"
                                          if two_pass else
                                          "qsa_build_metadata + qsa_decode_step" if meta else
@@ -894,7 +916,9 @@ def main() -> int:
                                    "qsa_select and qsa_sparse_attn with events between them "
                                    "(the records add a few us per stage); roofline "
                                    "avg_launch_ms: each stage's call K times back to back "
-                                   "between two events (attention rotating the KV caches)"},
+                                   "between two events (attention rotating the KV caches), "
+                                   "replayed from a HIP graph; ms_per_step_graph: the K "
+                                   "decode steps likewise"},
     }
     if context is not None:
         result["single_row_latency"] = context
