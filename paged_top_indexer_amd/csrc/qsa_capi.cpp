@@ -308,8 +308,9 @@ int check_workspace(void* ws, size_t have, size_t need, Span guarded[], int ngua
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // A launch of `cols` workgroups of `threads` threads per row over `rows`
-// rows (padded to whole XCD groups) must stay under 2^32 work-items, the
-// limit of one dispatch.
+// rows must stay under 2^32 work-items, the limit of one dispatch; checked
+// for rows padded to whole XCD groups, which no placement's grid exceeds
+// (grid_blocks).
 int check_grid(const char* what, int64_t rows, int64_t cols, int threads) {
   const int64_t per_row = (cols > 0 ? cols : 1) * (int64_t)threads;
   if (qsa::padded_rows(rows) > qsa::kMaxWorkItems / per_row) {
@@ -326,9 +327,10 @@ int check_select_grid(const char* what, const qsa::SelectPlan& plan, int64_t gro
   return check_grid(what, qsa::padded_rows(groups) * plan.group, 1, qsa::kMergeThreads);
 }
 
-// Both kernels of the attention (splits; combine, one workgroup per head).
+// Both kernels of the attention (splits of plan.waves waves; combine, one
+// workgroup per head).
 int check_attn_grid(int64_t rows, const qsa::AttnPlan& plan) {
-  QSA_TRY(check_grid("attention", rows, plan.splits, qsa::kAttnThreads));
+  QSA_TRY(check_grid("attention", rows, plan.splits, 64 * plan.waves));
   return check_grid("attention", rows, qsa::kAttHeads, qsa::kCombineThreads);
 }
 
