@@ -323,7 +323,8 @@ int check_grid(const char* what, int64_t rows, int64_t cols, int threads) {
 // Both kernels of the selection (chunks over the row groups; the merge,
 // one workgroup per row of the padded groups).
 int check_select_grid(const char* what, const qsa::SelectPlan& plan, int64_t groups) {
-  QSA_TRY(check_grid(what, groups, plan.chunks_per_row, qsa::kChunkThreads));
+  QSA_TRY(check_grid(what, groups, plan.chunks_per_row,
+                     plan.big ? qsa::kChunkBigThreads : qsa::kChunkThreads));
   return check_grid(what, qsa::padded_rows(groups) * plan.group, 1, qsa::kMergeThreads);
 }
 
@@ -381,7 +382,7 @@ int select_impl(const qsa_tensor* q, const qsa_tensor* weights, const qsa_tensor
   QSA_TRY(check_select_output("out", out, q, weights, kcache, kscale, e4m3, block_table,
                               token_to_req, seq_lens, query_pos));
   if (v.rows == 0) return QSA_OK;
-  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width, v.group);
+  const qsa::SelectPlan plan = qsa::plan_select(v.rows, v.width, v.group, true);
   QSA_TRY(check_select_grid("selection", plan, plan_groups(plan, v.rows)));
   Span guarded[9] = {span_of(q),        span_of(kcache),   span_of(block_table),
                      span_of(token_to_req), span_of(seq_lens), span_of(query_pos),
@@ -528,7 +529,7 @@ QSA_API size_t qsa_select_workspace_bytes(int64_t rows, int64_t table_width) {
   // enough for every row grouping (q as [R, 4, 128] or [B, n, 4, 128])
   size_t bytes = 0;
   for (int group = 1; group <= qsa::kMaxGroup; ++group) {
-    bytes = std::max(bytes, qsa::plan_select(rows, table_width, group).bytes);
+    bytes = std::max(bytes, qsa::plan_select(rows, table_width, group, true).bytes);
   }
   return bytes;
 }

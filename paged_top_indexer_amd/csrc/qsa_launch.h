@@ -30,6 +30,7 @@ constexpr int64_t kMaxWorkItems = 0xFFFFFFFFll;
 // Threads per workgroup of each kernel (the host checks grid sizes with
 // them).
 constexpr int kChunkThreads = 256;
+constexpr int kChunkBigThreads = 512;  // 64-page chunks (SelectPlan::big)
 constexpr int kMergeThreads = 768;
 constexpr int kAttnThreads = 256;
 constexpr int kCombineThreads = 256;
@@ -90,9 +91,12 @@ constexpr int64_t grid_blocks(int64_t units, int64_t cols, Placement pl) {
 constexpr int kMaxGroup = 4;
 
 // Largest chunk (in cache pages) for groups of `group` rows: the chunk
-// kernel keeps group * chunk_pages * 128 scores in LDS (at most 4096), and a
-// group's rows are selected one per wave from at most 1024 scores each.
-constexpr int max_chunk_pages(int group) { return group <= 1 ? 32 : 8; }
+// kernel keeps group * chunk_pages * 128 scores in LDS (at most 4096 with 4
+// waves, 8192 with the 8 of a big plan), and a group's rows are selected
+// one per wave from at most 1024 scores each.
+constexpr int max_chunk_pages(int group, bool big = false) {
+  return group <= 1 ? (big ? 64 : 32) : 8;
+}
 
 // Launch plan of the selection.  A row's visible blocks are cut into chunks
 // of `chunk_pages` cache pages; one workgroup of the chunk kernel scores one
@@ -106,12 +110,15 @@ struct SelectPlan {
                                // whole table when it has at most 4 pages)
   int64_t chunks_per_row = 1;  // grid columns per row (ceil(W / chunk_pages))
   int64_t cand_cap = 0;        // candidate slots per chunk: min(512, 128*chunk_pages)
+  bool big = false;            // 64-page chunks of kChunkBigThreads threads
   size_t keys_off = 0;         // byte offsets inside the workspace
   size_t blocks_off = 0;
   size_t bytes = 0;            // total workspace bytes (0 = none needed)
 };
 
-SelectPlan plan_select(int64_t rows, int64_t table_width, int group = 1);
+// big_ok: a selection from keys (not paged logits, not a logits matrix),
+// which may take 64-page chunks of 8-wave workgroups.
+SelectPlan plan_select(int64_t rows, int64_t table_width, int group = 1, bool big_ok = false);
 
 // Launch plan of the attention kernel: `splits` workgroups per row, each
 // covering `split_positions` index positions with `waves` waves (tiles of

@@ -25,13 +25,23 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // the chunk kernel.  A table of at most 4 pages (512 blocks: every visible
 // block is selected, no top-k) is one chunk per row whatever the batch, so
 // short rows finish in the chunk kernel without a merge launch.
-SelectPlan plan_select(int64_t rows, int64_t table_width, int group) {
+SelectPlan plan_select(int64_t rows, int64_t table_width, int group, bool big_ok) {
   SelectPlan p;
   p.group = std::max(1, std::min(group, kMaxGroup));
   const int64_t groups = (rows + p.group - 1) / p.group;
   const int64_t w = table_width > 0 ? table_width : 1;
   int pages = max_chunk_pages(p.group);
-  if (w * kPageSlots <= kTopKBlocks) {
+  // Long rows (4 or more 64-page chunks) of a batch that fills the chip with
+  // them (512 workgroups, two per CU): 64-page chunks of 8-wave workgroups,
+  // half the candidates of 32-page chunks for the kernel that finishes each
+  // row.  (Rows of two such chunks lose more parallelism than they save.)
+  const int big = max_chunk_pages(p.group, true);
+  const int64_t big_chunks = (w + big - 1) / big;
+  if (big_ok && p.group == 1 && big_chunks >= 4 && groups * big_chunks >= 512 &&
+      big_chunks * kTopKBlocks <= kFusedCands) {
+    p.big = true;
+    pages = big;
+  } else if (w * kPageSlots <= kTopKBlocks) {
     pages = (int)w;
   } else {
     while (pages > 1 && groups * ((w + pages - 1) / pages) < 1024) pages >>= 1;
@@ -100,7 +110,7 @@ AttnPlan plan_attn(int64_t rows, bool whole_cu) {
 // and the attention takes whole-CU workgroups (up to 256 rows).
 DecodePlan plan_decode(int64_t rows, int64_t table_width, int group) {
   DecodePlan d;
-  d.select = plan_select(rows, table_width, group);
+  d.select = plan_select(rows, table_width, group, true);
   const bool fusable = d.select.chunks_per_row > 1 &&
                        d.select.chunks_per_row * d.select.cand_cap <= kFusedCands;
   d.attn = plan_attn(rows, fusable);

@@ -66,10 +66,11 @@
 namespace qsa {
 namespace {
 
-// (kChunkThreads = 256; kMergeThreads = 768: 3 waves per SIMD hide part of
-// the merge's LDS latency -- both in qsa_launch.h)
-constexpr int kMaxChunkPages = 32;
-constexpr int kMaxChunkBlocks = kMaxChunkPages * kPageSlots;  // 4096
+// (kChunkThreads = 256, kChunkBigThreads = 512 for 64-page chunks;
+// kMergeThreads = 768: 3 waves per SIMD hide part of the merge's LDS
+// latency -- all in qsa_launch.h)
+constexpr int kMaxChunkPages = 64;  // one page per lane
+constexpr int kMaxChunkBlocks = 32 * kPageSlots;  // 4096: 4-wave workgroups
 // LDS list of the merge: the running best plus a batch of kFusedCands
 // candidates (the plans keep a row within one batch where they can)
 constexpr int kMergeList = kFusedCands + kTopKBlocks;
@@ -238,17 +239,21 @@ __device__ void wave_topk(const uint32_t* keys, int n, int k, uint32_t* hist, Em
   }
 }
 
-// 40 KiB: four workgroups per CU.
+// LDS of a chunk workgroup of kWaves waves over chunks of up to kBlocks
+// blocks: 40 KiB for 4 waves and 4096 blocks (four workgroups per CU),
+// 72 KiB for 8 waves and 8192 blocks (two).
+template <int kWaves, int kBlocks>
 struct ChunkSmem {
-  uint32_t keys[kMaxChunkBlocks];
+  static constexpr int kNumWaves = kWaves;
+  uint32_t keys[kBlocks];
   alignas(16) uint32_t hist0[kBins];  // counted while scoring
   union {
     // scoring: one 16-key tile per wave, 16-byte chunk j of key n stored at
     // [n][j ^ n] (fp16: 16 chunks per key) or [n][j ^ (n & 7)] (e4m3: 8
     // chunks per key), so that both the coalesced write and the
     // MFMA-layout read touch distinct bank groups
-    u32x4 stage[kChunkWaves][16][16];
-    u32x4 stage8[kChunkWaves][16][8];
+    u32x4 stage[kWaves][16][16];
+    u32x4 stage8[kWaves][16][8];
     // selection (after scoring)
     struct {
       alignas(16) uint32_t hist1[kBins];
@@ -256,7 +261,7 @@ struct ChunkSmem {
       Scratch s;
     } sel;
     // one wave per row (groups of several rows): a radix histogram per wave
-    alignas(16) uint32_t wave_hist[kChunkWaves][kWaveBins];
+    alignas(16) uint32_t wave_hist[kWaves][kWaveBins];
   } u;
 };
 
@@ -265,13 +270,14 @@ struct ChunkSmem {
 // first radix histogram when a single-row group's chunk needs a select
 // (groups of several rows count it row by row after scoring).
 struct LdsSink {
-  ChunkSmem* sm;
+  uint32_t* keys;
+  uint32_t* hist0;
   int stride;
   bool count;
   __device__ __forceinline__ void operator()(int j, int i, float sc) const {
     const uint32_t key = score_key(sc);
-    sm->keys[j * stride + i] = key;
-    if (count) atomicAdd(&sm->hist0[digit0(key)], 1u);
+    keys[j * stride + i] = key;
+    if (count) atomicAdd(&hist0[digit0(key)], 1u);
   }
 };
 
@@ -279,10 +285,10 @@ struct LdsSink {
 // go out in one coalesced pass once the chunk is scored (small scattered
 // stores in the middle of the key stream slow the stream down).
 struct LogitsSink {
-  ChunkSmem* sm;
+  uint32_t* keys;
   int stride;
   __device__ __forceinline__ void operator()(int j, int i, float sc) const {
-    sm->keys[j * stride + i] = __float_as_uint(sc);
+    keys[j * stride + i] = __float_as_uint(sc);
   }
 };
 
@@ -332,15 +338,16 @@ __device__ __forceinline__ float head_sum(const floatx4& acc, const HeadWeights&
 }
 
 // Lane i: the block table's entry for the chunk's i-th logical page of
-// request req (at most 32 pages), or -1 past the table's width or the
-// lanes, or for an invalid request.  It needs only the request id, so it
+// request req (at most 64 pages, one per lane), or -1 past the table's
+// width, or for an invalid request.  It needs only the request id, so it
 // is loaded while the row's sequence length is still in flight (and
 // checked only where it is used, so that nothing waits for it early).
 __device__ __forceinline__ int32_t page_row(const SelectParams& p, int64_t req, int64_t chunk_base,
                                             int lane) {
   const int64_t col = chunk_base / kPageSlots + lane;
   int32_t entry = -1;
-  if (req >= 0 && req < p.num_reqs && lane < kMaxChunkPages && col < p.table_width) {
+  if (req >= 0 && req < p.num_reqs && lane < p.chunk_blocks / kPageSlots &&
+      col < p.table_width) {
     entry = p.block_table[req * p.bt_stride + col];
   }
   return entry;
@@ -385,10 +392,11 @@ __device__ __forceinline__ int tile_keys(int t, int tt, int ntiles, int nblk, ui
 // holds dims [32c + 8g, +8) of key n (B) or of A row n = head n % 4 of the
 // pass's row n / 4.  The result of key n for row j (its 4 heads) lands in
 // lane n + 16j.
-template <typename Sink>
-__device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem& sm,
+template <typename Smem, typename Sink>
+__device__ __forceinline__ void score_chunk_f16(const SelectParams& p, Smem& sm,
                                                 const PassRows& pr, int32_t row_pages,
                                                 const Sink& sink) {
+  constexpr int kWaves = Smem::kNumWaves;
   constexpr int kUnroll = 4;  // tiles in flight per wave (4 KiB each)
   constexpr int kPageBytes = kPageSlots * kSelDim * 2;
   const int lane = threadIdx.x & 63;
@@ -447,21 +455,21 @@ __device__ __forceinline__ void score_chunk_f16(const SelectParams& p, ChunkSmem
   // per-tile waits rely on)
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    issue(u, wave + u * kChunkWaves);
+    issue(u, wave + u * kWaves);
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll 1
-  for (int t0 = wave; t0 < ntiles; t0 += kChunkWaves * kUnroll) {
+  for (int t0 = wave; t0 < ntiles; t0 += kWaves * kUnroll) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * kChunkWaves;
+      const int t = t0 + u * kWaves;
       // transpose through the wave's LDS tile
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int key = 4 * c + g;
         stage[key][s16 ^ key] = raw[u][c];
       }
-      issue(u, t + kChunkWaves * kUnroll);
+      issue(u, t + kWaves * kUnroll);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_wave_barrier();
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -499,14 +507,15 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(uint32_t w0, uint32_t w1) {
 // visit the 128 dims, so each lane takes 32 contiguous bytes of its key:
 // MFMA k step c gives lane (n + 16g) dims [32g + 8c, +8) of key n (B) or of
 // A row n (head n % 4 of the pass's row n / 4); results as for fp16 keys.
-// Each wave walks whole pages (pages wave, wave + 4, ... of the chunk; eight
+// Each wave walks whole pages (pages wave, wave + kWaves, ... of the chunk; eight
 // 16-key tiles each), so a page's 128 scales are read once per wave as two
 // coalesced 256-byte loads (slots l and 64 + l in lane l), one page ahead,
 // and a tile takes its keys' scales from them with a lane permute.
-template <typename Sink>
-__device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSmem& sm,
+template <typename Smem, typename Sink>
+__device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, Smem& sm,
                                                  const PassRows& pr, int32_t row_pages,
                                                  const Sink& sink) {
+  constexpr int kWaves = Smem::kNumWaves;
   constexpr int kUnroll = 8;  // tiles in flight per wave (2 KiB each): one page
   constexpr int kPageBytes = kPageSlots * kSelDim;
   constexpr int kScaleBytes = kPageSlots * 4;
@@ -534,9 +543,9 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
   const int ntiles = (nblk + 15) >> 4;
   const int npages = (nblk + kPageSlots - 1) / kPageSlots;
   // the wave's tiles: k-th = tile k % 8 of the wave's (k / 8)-th page
-  const int nk = npages > wave ? kUnroll * ((npages - wave + kChunkWaves - 1) / kChunkWaves) : 0;
+  const int nk = npages > wave ? kUnroll * ((npages - wave + kWaves - 1) / kWaves) : 0;
   if (nk == 0) return;
-  auto tile_of = [&](int k) { return kUnroll * (wave + kChunkWaves * (k / kUnroll)) + k % kUnroll; };
+  auto tile_of = [&](int k) { return kUnroll * (wave + kWaves * (k / kUnroll)) + k % kUnroll; };
   u32x4(*stage)[8] = sm.u.stage8[wave];
   const int s8 = lane & 7;     // 16-byte chunk of a key this lane loads
   const int k8 = lane >> 3;    // key of the 8-key half tile this lane loads
@@ -623,22 +632,22 @@ __device__ __forceinline__ void score_chunk_e4m3(const SelectParams& p, ChunkSme
 }
 
 // Scores given as a logits matrix: the chunk's nblk columns of row r.
-template <typename Sink>
+template <int kThreads, typename Sink>
 __device__ __forceinline__ void score_chunk_logits(const SelectParams& p, int64_t r,
                                                    int64_t chunk_base, int nblk, const Sink& sink) {
   constexpr int kUnroll = 8;
   const float* src = p.logits_in + r * p.logits_stride + chunk_base;
 #pragma unroll 1
-  for (int i0 = threadIdx.x; i0 < nblk; i0 += kChunkThreads * kUnroll) {
+  for (int i0 = threadIdx.x; i0 < nblk; i0 += kThreads * kUnroll) {
     float v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int i = i0 + u * kChunkThreads;
+      const int i = i0 + u * kThreads;
       v[u] = i < nblk ? __builtin_nontemporal_load(src + i) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int i = i0 + u * kChunkThreads;
+      const int i = i0 + u * kThreads;
       if (i < nblk) sink(0, i, v[u]);
     }
   }
@@ -659,10 +668,12 @@ enum : int { kSrcF16 = 0, kSrcE4M3 = 1, kSrcLogits = 2 };
 // workgroups per CU), except the e4m3 scorer over groups of rows: 4 rows x
 // 4 heads of queries plus a page of codes in flight need ~148 VGPRs, so it
 // runs at 3 waves per SIMD rather than spill to scratch.
-template <int kSrc, bool kLogitsOut, int kGroup>
-__global__ __launch_bounds__(kChunkThreads, (kSrc == kSrcE4M3 && kGroup > 1) ? 3 : 4) void
+template <int kSrc, bool kLogitsOut, int kGroup, int kThreads>
+__global__ __launch_bounds__(kThreads, (kSrc == kSrcE4M3 && kGroup > 1) ? 3 : 4) void
 qsa_select_chunk_kernel(SelectParams p) {
-  __shared__ ChunkSmem sm;
+  static_assert(kThreads == kChunkThreads || kThreads == kChunkBigThreads, "chunk workgroups");
+  __shared__ ChunkSmem<kThreads / 64, kThreads == kChunkBigThreads ? 2 * kMaxChunkBlocks
+                                                                      : kMaxChunkBlocks> sm;
   const int tid = threadIdx.x;
   const int group = kGroup == 1 ? 1 : p.group;
   const RowCol id = row_col_of_block(blockIdx.x, p.chunks_per_row, p.place);
@@ -728,12 +739,12 @@ qsa_select_chunk_kernel(SelectParams p) {
 
   const bool count_hist = !kLogitsOut && kGroup == 1 && nblk[0] > kTopKBlocks;
   if (count_hist) {
-    for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
+    for (int i = tid; i < kBins; i += kThreads) sm.hist0[i] = 0;
     __syncthreads();
   }
   auto score_all = [&](const auto& sink) {
     if constexpr (kSrc == kSrcLogits) {
-      score_chunk_logits(p, r0, chunk_base, nblk[0], sink);  // one row per group
+      score_chunk_logits<kThreads>(p, r0, chunk_base, nblk[0], sink);  // one row per group
       return;
     }
     uint32_t todo = 0;
@@ -767,9 +778,9 @@ qsa_select_chunk_kernel(SelectParams p) {
     }
   };
   if constexpr (kLogitsOut) {
-    score_all(LogitsSink{&sm, p.chunk_blocks});
+    score_all(LogitsSink{sm.keys, p.chunk_blocks});
   } else {
-    score_all(LdsSink{&sm, p.chunk_blocks, count_hist});
+    score_all(LdsSink{sm.keys, sm.hist0, p.chunk_blocks, count_hist});
   }
   __syncthreads();
 
@@ -781,7 +792,7 @@ qsa_select_chunk_kernel(SelectParams p) {
       const int nb = (int)max((int64_t)0, min((int64_t)p.chunk_blocks, row.visible - chunk_base));
       float* out_row = p.logits_out + r * p.logits_stride;
       const uint32_t* keys = sm.keys + j * p.chunk_blocks;
-      for (int i = tid; i < nb; i += kChunkThreads) {
+      for (int i = tid; i < nb; i += kThreads) {
         __builtin_nontemporal_store(__uint_as_float(keys[i]), out_row + chunk_base + i);
       }
       // -inf from the row's end (or the chunk's start) to the chunk's end;
@@ -790,7 +801,7 @@ qsa_select_chunk_kernel(SelectParams p) {
       const int64_t hi = chunk == p.chunks_per_row - 1
                              ? p.logits_width
                              : min(chunk_base + (int64_t)p.chunk_blocks, p.logits_width);
-      for (int64_t b = lo + tid; b < hi; b += kChunkThreads) out_row[b] = -__builtin_inff();
+      for (int64_t b = lo + tid; b < hi; b += kThreads) out_row[b] = -__builtin_inff();
     }
     return;
   }
@@ -802,9 +813,9 @@ qsa_select_chunk_kernel(SelectParams p) {
     const bool select = nb > kTopKBlocks;
     const uint32_t* keys = sm.keys + j * p.chunk_blocks;
     if (select && !count_hist) {
-      for (int i = tid; i < kBins; i += kChunkThreads) sm.hist0[i] = 0;
+      for (int i = tid; i < kBins; i += kThreads) sm.hist0[i] = 0;
       __syncthreads();
-      for (int i = tid; i < nb; i += kChunkThreads) atomicAdd(&sm.hist0[digit0(keys[i])], 1u);
+      for (int i = tid; i < nb; i += kThreads) atomicAdd(&sm.hist0[digit0(keys[i])], 1u);
       __syncthreads();
     }
     const int k_local = min(kTopKBlocks, nb);
@@ -813,12 +824,12 @@ qsa_select_chunk_kernel(SelectParams p) {
     auto block_of = [&](int i) { return (uint32_t)(chunk_base + i); };
     Scratch& s = sm.u.sel.s;
     if (select) {
-      topk_threshold<kChunkThreads>(lds_key, block_of, nb, k_local, s, sm.hist0, sm.u.sel.hist1,
+      topk_threshold<kThreads>(lds_key, block_of, nb, k_local, s, sm.hist0, sm.u.sel.hist1,
                                     T, bcut);
     }
     if (row.nchunks == 1) {
       uint64_t* sorted = sm.u.sel.sorted;
-      compact_topk<kChunkThreads>(
+      compact_topk<kThreads>(
           lds_key, block_of, nb, T, bcut,
           [&](uint32_t slot, int i, uint32_t x) { sorted[slot] = pack(x, block_of(i)); }, s);
       if constexpr (kGroup == 1) {
@@ -831,7 +842,7 @@ qsa_select_chunk_kernel(SelectParams p) {
       const int64_t cbase = (r * p.chunks_per_row + chunk) * p.cand_cap;
       uint32_t* ckeys = p.cand_keys + cbase;
       uint32_t* cblocks = p.cand_blocks + cbase;
-      compact_topk<kChunkThreads>(
+      compact_topk<kThreads>(
           lds_key, block_of, nb, T, bcut,
           [&](uint32_t slot, int i, uint32_t x) {
             ckeys[slot] = x;
@@ -1091,19 +1102,28 @@ SelectParams make_params(const SelectArgs& a, const SelectPlan& plan) {
   return p;
 }
 
+// big: the plan's 64-page chunks of 8-wave workgroups (a selection from
+// keys, one row per workgroup); otherwise 4 waves.
 template <int kSrc, bool kLogitsOut>
-void launch_chunks(const SelectParams& p, hipStream_t s) {
+void launch_chunks(const SelectParams& p, bool big, hipStream_t s) {
   const int64_t groups = (p.rows + p.group - 1) / p.group;
   const dim3 grid((unsigned)grid_blocks(groups, p.chunks_per_row, p.place));
   if constexpr (kSrc != kSrcLogits) {  // (logits rows are never grouped)
     if (p.group > 1) {
-      hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, kMaxGroup>), grid,
-                         dim3(kChunkThreads), 0, s, p);
+      hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, kMaxGroup, kChunkThreads>),
+                         grid, dim3(kChunkThreads), 0, s, p);
       return;
     }
+    if constexpr (!kLogitsOut) {
+      if (big) {
+        hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, false, 1, kChunkBigThreads>), grid,
+                           dim3(kChunkBigThreads), 0, s, p);
+        return;
+      }
+    }
   }
-  hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, 1>), grid, dim3(kChunkThreads), 0,
-                     s, p);
+  hipLaunchKernelGGL((qsa_select_chunk_kernel<kSrc, kLogitsOut, 1, kChunkThreads>), grid,
+                     dim3(kChunkThreads), 0, s, p);
 }
 
 }  // namespace
@@ -1113,11 +1133,11 @@ int launch_select(const SelectArgs& a, const SelectPlan& plan, void* stream, boo
   const SelectParams p = make_params(a, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.logits_in) {
-    launch_chunks<kSrcLogits, false>(p, s);
+    launch_chunks<kSrcLogits, false>(p, false, s);
   } else if (a.kscale) {
-    launch_chunks<kSrcE4M3, false>(p, s);
+    launch_chunks<kSrcE4M3, false>(p, plan.big, s);
   } else {
-    launch_chunks<kSrcF16, false>(p, s);
+    launch_chunks<kSrcF16, false>(p, plan.big, s);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || plan.chunks_per_row == 1 || !merge) return (int)err;
@@ -1140,9 +1160,9 @@ int launch_paged_logits(const SelectArgs& a, const SelectPlan& plan, void* strea
   const SelectParams p = make_params(a, plan);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a.kscale) {
-    launch_chunks<kSrcE4M3, true>(p, s);
+    launch_chunks<kSrcE4M3, true>(p, false, s);
   } else {
-    launch_chunks<kSrcF16, true>(p, s);
+    launch_chunks<kSrcF16, true>(p, false, s);
   }
   return (int)hipGetLastError();
 }
