@@ -37,8 +37,10 @@ Workloads (``--workload``), one per configuration of the decode batch:
 Inputs are seeded synthetic data, resident in HBM before timing starts.
 
 One step = one qsa_decode_step call (selection then attention on one
-stream, no host sync); K steps (200 by default) are timed with HIP events at
-both ends.  The
+stream, no host sync); after ~25 ms of plain HBM reads (the device's ramp-up
+under load) and W warm-up steps, K steps (200 by default) are timed with HIP
+events at both ends, the last warm-up step queued right before the start
+event (so the region opens on a busy GPU, one step behind another).  The
 steps rotate over distinct KV caches and over block tables that map the
 rows through distinct page permutations of the key cache, as consecutive
 layers would read distinct caches (no step finds its data in the last-level
@@ -173,11 +175,11 @@ def stored_counters(workload: str):
     return rec
 
 
-def read_ceiling(torch, qsa, dev, gib: int = 2, reps: int = 5) -> float:
-    """The box's practical HBM read ceiling (GB/s): qsa_read_probe of
-    libqsa_probe.so (include/qsa_probe.h, a measurement aid built apart from
-    the method's library) streaming `gib` GiB with nontemporal loads, `reps`
-    times between HIP events."""
+def read_probe(torch, dev, gib: int = 2):
+    """A callable that streams a `gib` GiB device buffer once with
+    nontemporal loads: qsa_read_probe of libqsa_probe.so (include/qsa_probe.h,
+    a measurement aid built apart from the method's library), on the current
+    stream.  Returns (probe, buffer bytes)."""
     import ctypes
 
     from paged_top_indexer_amd import build
@@ -196,6 +198,13 @@ def read_ceiling(torch, qsa, dev, gib: int = 2, reps: int = 5) -> float:
         if rc != 0:
             raise RuntimeError(f"qsa_read_probe failed with status {rc}")
 
+    return probe, buf.numel()
+
+
+def read_ceiling(torch, probe, nbytes: int, reps: int = 5) -> float:
+    """The box's practical HBM read ceiling (GB/s): the read probe over its
+    `nbytes` buffer, `reps` times between HIP events."""
+    stream = torch.cuda.current_stream()
     probe()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record(stream)
@@ -203,9 +212,7 @@ def read_ceiling(torch, qsa, dev, gib: int = 2, reps: int = 5) -> float:
         probe()
     ev[1].record(stream)
     torch.cuda.synchronize()
-    gbs = (gib << 30) * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9
-    del buf
-    return gbs
+    return nbytes * reps / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9
 
 
 def r1_latencies(torch, qsa, wl, dev, calls: int = 64) -> dict:
@@ -509,9 +516,9 @@ def workload_config(w, kv_copies: int, key_tables: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # 200 by default: a timed region carries a fixed ~0.14 ms start cost
-    # (measured: 0.2382 / 0.2340 / 0.2321 ms per step at K = 20 / 64 / 200),
-    # which a short region would spread over its few steps
+    # 200 by default: a region opened on an idle GPU carries a fixed ~0.14 ms
+    # start cost (measured: 0.2382 / 0.2340 / 0.2321 ms per step at K = 20 /
+    # 64 / 200), which the lead-in below takes out of the timed region
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -672,10 +679,30 @@ def main() -> int:
             k, v = kv_views[i % len(kv_views)]
             decode_fn(*sel_at(i), q_attn, k, v, scale, indices=idx, out=out, workspace=ws_all)
 
+    # The device runs the first ~10 ms of memory load after an idle spell
+    # slower while it ramps up (measured at the long-context shape:
+    # consecutive regions of 20 decode steps from the process's start read
+    # 0.2305, 0.2258, then 0.2230-0.2239 ms per step; after ~10-25 ms of
+    # plain HBM reads the first region already reads 0.2235-0.2240 ms, while
+    # a 25 ms device sleep does not help; in one process, K = 20 selections
+    # timed after a graph capture read 4% slower than the same a pass
+    # later).  device_warmup queues
+    # `reps` streams of the read probe's 2 GiB buffer (none of the
+    # workload's; ~0.3 ms each) before a timed measurement, so that a short
+    # timed region does not measure that ramp.
+    probe, probe_bytes = read_probe(torch, dev)
+
+    def device_warmup(reps: int) -> None:
+        for _ in range(reps):
+            probe()
+
     def graph_ms(fn) -> float:
         """ms per call of fn(0..K-1) captured once in a HIP graph and replayed
         between two events on the launch stream (fn(0) runs once outside the
-        capture first)."""
+        capture first).  After the capture ~10 ms of plain reads and an
+        eager fn(4) (another cache and table than the graph's first call)
+        are queued before the start event: the device is up to speed and
+        busy while the host launches the graph."""
         fn(0)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
@@ -684,23 +711,26 @@ def main() -> int:
                 fn(i)
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        device_warmup(32)
+        fn(4)
         ev[0].record(stream)
         g.replay()
         ev[1].record(stream)
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / args.steps
 
-    def timed_steps(lead_in: bool) -> float:
+    def timed_steps(lead_in) -> float:
         """ms per step over exactly K decode steps between two events, after a
-        synchronisation.  lead_in: a ~0.2 ms device sleep is queued between
-        the synchronisation and the start event, so the timed region opens
-        with the first step already queued -- otherwise it also holds the
-        host's first launch (marshalling, the launch path) on an idle GPU, a
-        fixed ~0.1 ms that a short region spreads over its few steps."""
+        synchronisation.  lead_in: work queued between the synchronisation
+        and the start event, so that the timed region opens with the GPU
+        busy and the first timed step already queued -- otherwise it also
+        holds the host's first launch (marshalling, the launch path) on an
+        idle GPU, a fixed cost that a short region spreads over its few
+        steps.  None opens the region on an idle GPU."""
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        if lead_in:
-            torch.cuda._sleep(500_000)  # GPU clock cycles (~0.2 ms)
+        if lead_in is not None:
+            lead_in()
         ev[0].record(stream)
         for i in range(args.steps):
             step(i)
@@ -708,14 +738,25 @@ def main() -> int:
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / args.steps
 
-    # warm-up, then exactly K timed decode steps (events only at the ends)
-    for i in range(args.warmup):
+    # ~25 ms of plain HBM reads (device_warmup), W untimed warm-up steps,
+    # then exactly K timed decode steps (events only at the ends).  The last warm-up step is the lead-in: it is queued after
+    # the synchronisation, right before the start event, so the region opens
+    # as a serving loop runs, one step behind another (a ~0.2 ms device sleep
+    # there instead, on an idle-but-for-one-wave GPU, read ~1 us per step more
+    # at K = 20 on one box).  Without warm-up the sleep is the lead-in.
+    device_warmup(80)
+    torch.cuda.synchronize()
+    for i in range(args.warmup - 1):
         step(i)
+    if args.warmup > 0:
+        lead = lambda: step(args.warmup - 1)  # noqa: E731
+    else:
+        lead = lambda: torch.cuda._sleep(500_000)  # noqa: E731  (GPU clock cycles, ~0.2 ms)
     t_start = time.perf_counter()
-    ms_per_step = timed_steps(lead_in=True)
+    ms_per_step = timed_steps(lead)
     wall = time.perf_counter() - t_start
     # the same K steps with the region opening on an idle GPU, for reference
-    ms_per_step_cold = timed_steps(lead_in=False)
+    ms_per_step_cold = timed_steps(None)
     # and captured once in a HIP graph, replayed between two events: the
     # device's time per step without the host's launches (a small batch's
     # steps from Python are bound by their ~12 us of argument marshalling)
@@ -773,7 +814,8 @@ def main() -> int:
         extra["select_row_by_row_ms"] = round(flat_ev[0].elapsed_time(flat_ev[1]) / args.steps, 4)
         log(f"selection row by row {extra['select_row_by_row_ms']:.4f} ms")
     log(f"step {ms_per_step:.4f} ms (cold start {ms_per_step_cold:.4f} ms, graph-replayed "
-        f"{ms_per_step_graph:.4f} ms; wall {wall * 1e3 / args.steps:.4f} ms); stages: select "
+        f"{ms_per_step_graph:.4f} ms; wall {wall * 1e3 / args.steps:.4f} ms with the lead-in); "
+        f"stages: select "
         f"{np.mean(sel_ms):.4f} ms (min {np.min(sel_ms):.4f}), attention {np.mean(att_ms):.4f} ms")
 
     # one more step on the first KV cache (the oracle's) for the parity check
@@ -838,7 +880,7 @@ def main() -> int:
         " + qsa_attn_combine_kernel)" if qsa.sparse_attn_workspace_bytes(R) > 0 else ")")
     log(f"back to back: selection {sel_roof_ms:.4f} ms, attention {att_roof_ms:.4f} ms per launch")
     counters = stored_counters(w.name)
-    ceiling = None if args.no_context else read_ceiling(torch, qsa, dev)
+    ceiling = None if args.no_context else read_ceiling(torch, probe, probe_bytes)
 
     def roof(nbytes, ms, kernel, traffic):
         gbs = nbytes / (ms / 1e3) / 1e9
