@@ -80,7 +80,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # used only while their hash matches the one it was taken on)
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_top_indexer_amd", "csrc", f)
                   for f in ("qsa_select.hip", "qsa_attn.hip", "qsa_device.h", "qsa_launch.h",
-                            "qsa_plan.cpp")]
+                            "qsa_topk.h", "qsa_plan.cpp")]
 
 # --workload name -> (builder, integer inputs: the selection is checked
 # bit-exact; else by the band rule)

@@ -244,7 +244,15 @@ __device__ void topk_threshold(KeyAt key_at, BlockAt block_at, int n, int k, Scr
     auto tie_key = [&](int i) { return key_at(i) == t ? 0x7FFFFFFFu - block_at(i) : 0u; };
     for (int i = threadIdx.x; i < kBins; i += NT) hist0[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += NT) atomicAdd(&hist0[digit0(tie_key(i))], 1u);
+    // Only the entries equal to T are counted: every other entry's tie key
+    // is 0, below all of theirs (block ids are below 2^31), and need_eq <
+    // eq_total of them are taken, so the boundary never falls among the
+    // zeros and bin 0 need not hold them (counting them would put nearly
+    // every entry's LDS atomic on that one bin).
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint32_t tk = tie_key(i);
+      if (tk != 0) atomicAdd(&hist0[digit0(tk)], 1u);
+    }
     __syncthreads();
     uint32_t t2 = 0;
     int ne2 = 0, et2 = 0;
