@@ -155,7 +155,8 @@ __device__ void select_row(const FusedSelect& f, int64_t r, const Row& row, SelP
   if (m > k) {
     for (int i = tid; i < m; i += NT) atomicAdd(&sm.hist0[digit0(lds_key(i))], 1u);
     __syncthreads();
-    topk_threshold<NT>(lds_key, block_of, m, k, sm.s, sm.hist0, sm.hist1, T, bcut);
+    topk_threshold<NT>(lds_key, block_of, m, k, (uint32_t)row.visible, sm.s, sm.hist0, sm.hist1, T,
+                       bcut);
   }
   compact_topk<NT>(
       lds_key, block_of, m, T, bcut,

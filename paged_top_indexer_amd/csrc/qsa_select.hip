@@ -824,8 +824,8 @@ qsa_select_chunk_kernel(SelectParams p) {
     auto block_of = [&](int i) { return (uint32_t)(chunk_base + i); };
     Scratch& s = sm.u.sel.s;
     if (select) {
-      topk_threshold<kThreads>(lds_key, block_of, nb, k_local, s, sm.hist0, sm.u.sel.hist1,
-                                    T, bcut);
+      topk_threshold<kThreads>(lds_key, block_of, nb, k_local, (uint32_t)(chunk_base + nb), s,
+                               sm.hist0, sm.u.sel.hist1, T, bcut);
     }
     if (row.nchunks == 1) {
       uint64_t* sorted = sm.u.sel.sorted;
@@ -984,8 +984,8 @@ __global__ __launch_bounds__(kMergeThreads) void qsa_select_merge_kernel(SelectP
     }
     uint32_t T = 0, bcut = 0xFFFFFFFFu;
     if (n_list > kk) {
-      topk_threshold<kMergeThreads>(lds_key, block_of, n_list, kk, sm.s, sm.hist0, sm.hist1, T,
-                                    bcut);
+      topk_threshold<kMergeThreads>(lds_key, block_of, n_list, kk, (uint32_t)row.visible, sm.s,
+                                    sm.hist0, sm.hist1, T, bcut);
     }
     compact_topk<kMergeThreads>(
         lds_key, block_of, n_list, T, bcut,
@@ -1056,7 +1056,8 @@ __global__ __launch_bounds__(kRowTopkThreads) void qsa_topk_row_kernel(SelectPar
   if (n > k) {
     for (int i = tid; i < n; i += kRowTopkThreads) atomicAdd(&sm.hist0[digit0(lds_key(i))], 1u);
     __syncthreads();
-    topk_threshold<kRowTopkThreads>(lds_key, block_of, n, k, sm.s, sm.hist0, sm.hist1, T, bcut);
+    topk_threshold<kRowTopkThreads>(lds_key, block_of, n, k, (uint32_t)n, sm.s, sm.hist0, sm.hist1,
+                                    T, bcut);
   }
   compact_topk<kRowTopkThreads>(
       lds_key, block_of, n, T, bcut,

@@ -226,13 +226,15 @@ __device__ void radix_select(KeyAt key_at, int n, int k, Scratch& s, uint32_t* h
 
 // Threshold of the top-k (1 <= k <= n) under the total order (key
 // descending, block ascending): the top-k are the entries with key > T and
-// the entries with key == T and block < bcut.  Preconditions as for
-// radix_select.  When the keys equal to T are only partly in, a second
-// radix select over 0x7FFFFFFF - block of those entries (block ids are
-// distinct) finds the last block that is in.
+// the entries with key == T and block < bcut.  Every block id is below
+// block_end (at most 2^31).  Preconditions as for radix_select.  When the
+// keys equal to T are only partly in, a second radix select over tie keys
+// of those entries (block ids are distinct) finds the last block that is
+// in.
 template <int NT, typename KeyAt, typename BlockAt>
-__device__ void topk_threshold(KeyAt key_at, BlockAt block_at, int n, int k, Scratch& s,
-                               uint32_t* hist0, uint32_t* hist1, uint32_t& T, uint32_t& bcut) {
+__device__ void topk_threshold(KeyAt key_at, BlockAt block_at, int n, int k, uint32_t block_end,
+                               Scratch& s, uint32_t* hist0, uint32_t* hist1, uint32_t& T,
+                               uint32_t& bcut) {
   int need_eq = 0, eq_total = 0;
   radix_select<NT>(key_at, n, k, s, hist0, hist1, T, need_eq, eq_total);
   if (need_eq == 0) {
@@ -240,15 +242,24 @@ __device__ void topk_threshold(KeyAt key_at, BlockAt block_at, int n, int k, Scr
   } else if (need_eq == eq_total) {
     bcut = 0xFFFFFFFFu;
   } else {
+    // Tie key of an entry equal to T: (M - block) << sh with M = 2^B the
+    // smallest power of two above every block id -- nonzero, larger for a
+    // smaller block, and with the block's significant bits at the top of
+    // the word, so that the radix digits resolve them in one pass (B <= 10)
+    // or two (B <= 21) rather than spending the first on bits every block
+    // shares.  Every other entry's tie key is 0.
+    const int B = block_end > 1 ? 32 - __builtin_clz(block_end - 1) : 0;
+    const uint32_t M = 1u << B;
+    const int sh = 31 - B;
     const uint32_t t = T;
-    auto tie_key = [&](int i) { return key_at(i) == t ? 0x7FFFFFFFu - block_at(i) : 0u; };
+    auto tie_key = [&](int i) { return key_at(i) == t ? (M - block_at(i)) << sh : 0u; };
     for (int i = threadIdx.x; i < kBins; i += NT) hist0[i] = 0;
     __syncthreads();
-    // Only the entries equal to T are counted: every other entry's tie key
-    // is 0, below all of theirs (block ids are below 2^31), and need_eq <
-    // eq_total of them are taken, so the boundary never falls among the
-    // zeros and bin 0 need not hold them (counting them would put nearly
-    // every entry's LDS atomic on that one bin).
+    // Only the entries equal to T are counted: the others' tie key 0 lies
+    // below all of theirs, and need_eq < eq_total of them are taken, so the
+    // boundary never falls among the zeros and bin 0 need not hold them
+    // (counting them would put nearly every entry's LDS atomic on that one
+    // bin).
     for (int i = threadIdx.x; i < n; i += NT) {
       const uint32_t tk = tie_key(i);
       if (tk != 0) atomicAdd(&hist0[digit0(tk)], 1u);
@@ -257,9 +268,11 @@ __device__ void topk_threshold(KeyAt key_at, BlockAt block_at, int n, int k, Scr
     uint32_t t2 = 0;
     int ne2 = 0, et2 = 0;
     radix_select<NT>(tie_key, n, need_eq, s, hist0, hist1, t2, ne2, et2);
-    // the tie keys taken are those > t2, plus t2 itself when ne2 > 0 (tie
-    // keys of the entries equal to T are distinct, so ne2 is 0 or 1)
-    bcut = (0x7FFFFFFFu - t2) + (ne2 > 0 ? 1u : 0u);
+    // The tie keys taken are those > t2, plus t2 itself when ne2 > 0 (tie
+    // keys are distinct, so ne2 is 0 or 1; t2 is then an entry's own tie
+    // key).  (M - b) << sh > t2 exactly when M - b > t2 >> sh, that is when
+    // b < M - (t2 >> sh).
+    bcut = (M - (t2 >> sh)) + (ne2 > 0 ? 1u : 0u);
   }
 }
 
